@@ -1,0 +1,84 @@
+"""Plant plausible mistakes in the oracle (CPU only) and check that at least
+one pin in test_oracle_pins.py catches each one. This guards the pins
+themselves: a pin that still passes on a broken oracle pins nothing."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.gmla_oracle as G
+from tests import test_oracle_pins as P
+
+
+def _rope_wrong_sign(u, pos, base):
+    u = np.asarray(u, dtype=np.float64)
+    d = u.shape[-1]
+    theta = np.power(float(base), -2.0 * np.arange(d // 2) / d)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * theta
+    out = np.empty_like(u)
+    out[..., 0::2] = u[..., 0::2] * np.cos(ang) + u[..., 1::2] * np.sin(ang)
+    out[..., 1::2] = -u[..., 0::2] * np.sin(ang) + u[..., 1::2] * np.cos(ang)
+    return out
+
+
+def _rope_half_split(u, pos, base):
+    # pairs (i, i + d/2) instead of (2i, 2i+1)
+    u = np.asarray(u, dtype=np.float64)
+    d = u.shape[-1]
+    theta = np.power(float(base), -2.0 * np.arange(d // 2) / d)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * theta
+    a, b = u[..., : d // 2], u[..., d // 2:]
+    return np.concatenate([a * np.cos(ang) - b * np.sin(ang), a * np.sin(ang) + b * np.cos(ang)], -1)
+
+
+def _attend_strict(q_rows, k, v, t_rows, scale):
+    # causal boundary s < t instead of s <= t (position 0 keeps itself)
+    return _orig_attend(q_rows, k, v, [max(int(t) - 1, 0) for t in t_rows], scale)
+
+
+def _attend_no_max(q_rows, k, v, t_rows, scale):
+    o, lse = _orig_attend(q_rows, k, v, t_rows, scale)
+    return o, lse - 1.0  # lse off by a constant
+
+
+def _sigmoid_wrong(z):
+    return 1.0 / (1.0 + np.exp(np.asarray(z, dtype=np.float64)))
+
+
+def _value_up_transposed_heads(o_lat, W_uv):
+    o = np.einsum("thc,hdc->thd", np.asarray(o_lat, float), np.asarray(W_uv, float)[::-1])
+    return o.reshape(o.shape[0], -1)
+
+
+def _reconstruct_swapped(c, W_uk, W_uv):
+    k, v = _orig_reconstruct(c, W_uk, W_uv)
+    return k, np.einsum("...c,hdc->...hd", np.asarray(c, float), np.asarray(W_uv, float)[:, :, ::-1])
+
+
+_orig_attend = G.attend_rows
+_orig_reconstruct = G.reconstruct_kv
+
+MUTATIONS = [
+    ("rope_rotate", _rope_wrong_sign, [P.test_rope_matches_complex_rotation_and_is_relative,
+                                       lambda: P.test_decode_matches_mqa_sdpa(8)]),
+    ("rope_rotate", _rope_half_split, [P.test_rope_matches_complex_rotation_and_is_relative,
+                                       lambda: P.test_decode_matches_mqa_sdpa(8)]),
+    ("attend_rows", _attend_strict, [lambda: P.test_causal_attention_matches_torch_sdpa(7, 3, 5, 6),
+                                     P.test_whole_layer_matches_scalar_brute_force]),
+    ("attend_rows", _attend_no_max, [P.test_zero_query_gives_uniform_mean_and_log_count,
+                                     P.test_decode_single_token_and_lse_closed_form]),
+    ("sigmoid", _sigmoid_wrong, [P.test_sigmoid_matches_scipy_and_range, P.test_gate_special_cases,
+                                 P.test_whole_layer_matches_scalar_brute_force]),
+    ("value_up_projection", _value_up_transposed_heads,
+     [P.test_decode_equals_last_prefill_row, P.test_value_up_projection_moves_wuv_past_the_weighted_sum]),
+    ("reconstruct_kv", _reconstruct_swapped, [P.test_prefill_explicit_equals_absorbed_route,
+                                              P.test_whole_layer_matches_scalar_brute_force]),
+]
+
+
+@pytest.mark.parametrize("name,bad,pins", MUTATIONS, ids=[f"{m[0]}:{m[1].__name__}" for m in MUTATIONS])
+def test_every_planted_mistake_is_caught(monkeypatch, name, bad, pins):
+    monkeypatch.setattr(G, name, bad)
+    monkeypatch.setattr(oracle, name, bad)
+    for pin in pins:
+        with pytest.raises(AssertionError):
+            pin()

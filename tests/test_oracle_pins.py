@@ -1,0 +1,367 @@
+"""Pins for the fp64 oracle: each test checks it against something other than
+itself -- a library routine, a closed form, an invariant, a special case, a
+scalar brute force, or the numbers the pages print. CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle as O
+from gated_mla_latent_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+rng = np.random.default_rng(1234)
+
+
+def _sdpa(q, k, v, scale, causal):
+    """torch's own scaled_dot_product_attention in fp64 on the CPU.
+    q,k,v: [L, H, d] numpy -> [L, H, dv]."""
+    qt = torch.from_numpy(np.ascontiguousarray(q.transpose(1, 0, 2)))
+    kt = torch.from_numpy(np.ascontiguousarray(k.transpose(1, 0, 2)))
+    vt = torch.from_numpy(np.ascontiguousarray(v.transpose(1, 0, 2)))
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=causal, scale=scale)
+    return o.numpy().transpose(1, 0, 2)
+
+
+# ---------------------------------------------------------------- attention
+@pytest.mark.parametrize("L,H,dk,dv", [(1, 1, 4, 4), (7, 3, 5, 6), (33, 2, 16, 8)])
+def test_causal_attention_matches_torch_sdpa(L, H, dk, dv):
+    q = rng.standard_normal((L, H, dk))
+    k = rng.standard_normal((L, H, dk))
+    v = rng.standard_normal((L, H, dv))
+    scale = 0.37
+    o, _ = O.causal_attention(q, k, v, scale)
+    ref = _sdpa(q, k, v, scale, causal=True)
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+
+
+def test_softmax_rows_sum_to_one_and_are_nonnegative():
+    L, H = 9, 3
+    q = rng.standard_normal((L, H, 4)) * 3
+    k = rng.standard_normal((L, H, 4))
+    # v = 1 everywhere: o_t = sum_s a_ts, which must be exactly one.
+    o, _ = O.causal_attention(q, k, np.ones((L, H, 1)), 1.0)
+    np.testing.assert_allclose(o, 1.0, atol=1e-12)
+    # v_s = e_s (one-hot on the key index): o_t is the weight row itself.
+    eye = np.broadcast_to(np.eye(L)[:, None, :], (L, H, L))
+    a, _ = O.causal_attention(q, k, eye, 1.0)
+    assert (a >= 0).all()
+    # weights beyond t are exactly zero (causal, inclusive boundary)
+    for t in range(L):
+        assert np.all(a[t, :, t + 1:] == 0)
+        assert np.all(a[t, :, t] > 0)
+
+
+def test_first_position_returns_its_own_value_and_lse():
+    L, H = 5, 2
+    q = rng.standard_normal((L, H, 3))
+    k = rng.standard_normal((L, H, 3))
+    v = rng.standard_normal((L, H, 4))
+    o, lse = O.causal_attention(q, k, v, 0.5)
+    np.testing.assert_array_equal(o[0], v[0])
+    np.testing.assert_allclose(lse[0], 0.5 * np.einsum("hd,hd->h", q[0], k[0]), atol=1e-12)
+
+
+def test_zero_query_gives_uniform_mean_and_log_count():
+    L, H = 6, 2
+    q = np.zeros((L, H, 3))
+    k = rng.standard_normal((L, H, 3))
+    v = rng.standard_normal((L, H, 2))
+    o, lse = O.causal_attention(q, k, v, 1.0)
+    for t in range(L):
+        np.testing.assert_allclose(o[t], v[: t + 1].mean(axis=0), atol=1e-12)
+        np.testing.assert_allclose(lse[t], math.log(t + 1), atol=1e-12)
+
+
+def test_dominant_key_selects_its_value():
+    L, H, d = 4, 1, 2
+    k = np.zeros((L, H, d))
+    k[2, 0] = [50.0, 0.0]
+    q = np.tile(np.array([50.0, 0.0]), (L, H, 1))
+    v = rng.standard_normal((L, H, 3))
+    o, _ = O.causal_attention(q, k, v, 1.0)
+    np.testing.assert_allclose(o[3, 0], v[2, 0], atol=1e-12)
+
+
+# ---------------------------------------------------------------- RoPE
+def _rope_complex(u, pos, base):
+    """RoPE as complex multiplication of interleaved pairs by e^{i pos theta}."""
+    d = u.shape[-1]
+    z = u[..., 0::2] + 1j * u[..., 1::2]
+    theta = base ** (-np.arange(0, d, 2) / d)
+    z = z * np.exp(1j * np.asarray(pos)[..., None] * theta)
+    out = np.empty_like(u)
+    out[..., 0::2] = z.real
+    out[..., 1::2] = z.imag
+    return out
+
+
+def test_rope_matches_complex_rotation_and_is_relative():
+    d = 64
+    q = rng.standard_normal((3, d))
+    k = rng.standard_normal((3, d))
+    for pos in [0, 1, 17, 1000, 131071]:
+        np.testing.assert_allclose(O.rope_rotate(q, pos, 10000.0), _rope_complex(q, pos, 10000.0),
+                                   rtol=0, atol=1e-10)
+    np.testing.assert_array_equal(O.rope_rotate(q, 0, 10000.0), q)
+    r = O.rope_rotate(q, 77, 10000.0)
+    np.testing.assert_allclose(np.linalg.norm(r, axis=-1), np.linalg.norm(q, axis=-1), rtol=1e-13)
+    # <R_t q, R_s k> depends only on t - s
+    a = np.einsum("nd,nd->n", O.rope_rotate(q, 50, 10000.0), O.rope_rotate(k, 20, 10000.0))
+    b = np.einsum("nd,nd->n", O.rope_rotate(q, 30, 10000.0), k)
+    np.testing.assert_allclose(a, b, atol=1e-10)
+    # d_r = 2 closed form: theta_0 = 1
+    u = np.array([[1.0, 0.0]])
+    np.testing.assert_allclose(O.rope_rotate(u, 0.5, 10000.0), [[math.cos(0.5), math.sin(0.5)]], atol=1e-15)
+
+
+# ---------------------------------------------------------------- gate
+def test_sigmoid_matches_scipy_and_range():
+    z = np.linspace(-30, 30, 1001)
+    np.testing.assert_allclose(O.sigmoid(z), scipy.special.expit(z), rtol=1e-14, atol=0)
+    z = rng.standard_normal(1000) * 5
+    s = O.sigmoid(z)
+    assert ((s > 0) & (s < 1)).all()
+
+
+def test_gate_special_cases():
+    T, D, Hdv = 5, 8, 6
+    x = rng.standard_normal((T, D))
+    ot = rng.standard_normal((T, Hdv))
+    W_o = rng.standard_normal((D, Hdv))
+    # W_g = 0 -> every gate is exactly 1/2
+    y = O.gate_out_reference(x, ot, np.zeros((Hdv, D)), W_o)
+    np.testing.assert_allclose(y, 0.5 * ot @ W_o.T, atol=1e-12)
+    # a gate driven to +inf lets o~ through unchanged (ungated MLA)
+    W_g = np.zeros((Hdv, D)); W_g[:, 0] = 1.0
+    x2 = x.copy(); x2[:, 0] = 80.0
+    y = O.gate_out_reference(x2, ot, W_g, W_o)
+    np.testing.assert_allclose(y, ot @ W_o.T, atol=1e-12)
+    # driven to -inf, the layer output vanishes
+    x2[:, 0] = -800.0
+    y = O.gate_out_reference(x2, ot, W_g, W_o)
+    np.testing.assert_allclose(y, 0.0, atol=1e-300)
+    # the gate is per channel: channel j is scaled by sigmoid((W_g x)_j) alone
+    W_g = rng.standard_normal((Hdv, D))
+    _, gated = O.gate_out_reference(x, ot, W_g, W_o, return_gated=True)
+    np.testing.assert_allclose(gated, scipy.special.expit(x @ W_g.T) * ot, atol=1e-14)
+
+
+# ---------------------------------------------------------------- absorption
+def test_prefill_explicit_equals_absorbed_route():
+    """q.(W_UK c) = (W_UK^T q).c and sum_s a_s W_UV c_s = W_UV sum_s a_s c_s
+    ([GF] §一, [N03] §5.1 / exercise 4): compute the layer through the
+    absorbed route here and compare with the oracle's explicit route."""
+    B, L, D, H, dc, dk, dv = 2, 11, 16, 3, 8, 5, 7
+    x = rng.standard_normal((B, L, D))
+    W_c = rng.standard_normal((dc, D))
+    W_q = rng.standard_normal((H * dk, D))
+    W_uk = rng.standard_normal((H, dk, dc))
+    W_uv = rng.standard_normal((H, dv, dc))
+    scale = 0.21
+    c, ot, lse = O.prefill_reference(x, W_c, W_q, W_uk, W_uv, scale)
+    for b in range(B):
+        cb = x[b] @ W_c.T
+        q = (x[b] @ W_q.T).reshape(L, H, dk)
+        for h in range(H):
+            qa = q[:, h] @ W_uk[h]  # [L, dc] absorbed query
+            z = (qa @ cb.T) * scale
+            z[np.triu_indices(L, 1)] = -np.inf
+            a = scipy.special.softmax(z, axis=1)
+            o_lat = a @ cb
+            np.testing.assert_allclose(ot[b, :, h * dv:(h + 1) * dv], o_lat @ W_uv[h].T, atol=1e-11)
+            np.testing.assert_allclose(lse[b, :, h], scipy.special.logsumexp(z, axis=1), atol=1e-11)
+
+
+def test_prefill_matches_torch_sdpa_per_head():
+    B, L, D, H, dc, dk, dv = 1, 20, 12, 2, 6, 4, 4
+    x = rng.standard_normal((B, L, D))
+    W_c = rng.standard_normal((dc, D)); W_q = rng.standard_normal((H * dk, D))
+    W_uk = rng.standard_normal((H, dk, dc)); W_uv = rng.standard_normal((H, dv, dc))
+    _, ot, _ = O.prefill_reference(x, W_c, W_q, W_uk, W_uv, 0.3)
+    c = torch.nn.functional.linear(torch.from_numpy(x[0]), torch.from_numpy(W_c)).numpy()
+    q = torch.nn.functional.linear(torch.from_numpy(x[0]), torch.from_numpy(W_q)).numpy().reshape(L, H, dk)
+    k = np.stack([c @ W_uk[h].T for h in range(H)], axis=1)
+    v = np.stack([c @ W_uv[h].T for h in range(H)], axis=1)
+    ref = _sdpa(q, k, v, 0.3, causal=True).reshape(L, H * dv)
+    np.testing.assert_allclose(ot[0], ref, atol=1e-12)
+
+
+def test_prefill_rows_subset_equals_full():
+    B, L, D, H, dc, dk, dv = 1, 13, 8, 2, 4, 3, 3
+    x = rng.standard_normal((B, L, D))
+    ws = [rng.standard_normal(s) for s in [(dc, D), (H * dk, D), (H, dk, dc), (H, dv, dc)]]
+    _, full, lf = O.prefill_reference(x, *ws, 0.5)
+    rows = [0, 4, 12]
+    _, part, lp = O.prefill_reference(x, *ws, 0.5, rows=rows)
+    np.testing.assert_allclose(part, full[:, rows], atol=1e-13)
+    np.testing.assert_allclose(lp, lf[:, rows], atol=1e-13)
+
+
+# ---------------------------------------------------------------- decode
+def _decode_via_mqa_sdpa(inp):
+    """Absorbed decode is MQA with one shared key [c; R k^R] and value c
+    ([N03] §3.1): one torch SDPA call per sequence, RoPE via complex numbers."""
+    q_abs = inp.q_abs.double().numpy()
+    cache = inp.cache.double().numpy()
+    outs = []
+    for b in range(inp.B):
+        L = int(inp.seq_len[b]); s0 = int(inp.seq_start[b])
+        rows = cache[s0:s0 + L]
+        q = q_abs[b].copy()
+        if inp.d_r:
+            q[:, inp.d_c:] = _rope_complex(q[:, inp.d_c:], L - 1, inp.rope_base)
+        qt = torch.from_numpy(q)[:, None, :]  # [H, 1, W]
+        kt = torch.from_numpy(rows)[None].expand(inp.H, L, rows.shape[1])
+        vt = torch.from_numpy(rows[:, :inp.d_c])[None].expand(inp.H, L, inp.d_c)
+        o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=inp.sm_scale)
+        outs.append(o[:, 0].numpy())
+    return np.stack(outs)
+
+
+@pytest.mark.parametrize("d_r", [0, 8])
+def test_decode_matches_mqa_sdpa(d_r):
+    inp = W.make_decode(4, 5, 16, d_r, 1, 40, dtype=torch.float32, seed=3)
+    o, lse = O.decode_reference(inp.q_abs.numpy(), inp.cache.numpy(), inp.seq_start.numpy(),
+                                inp.seq_len.numpy(), inp.d_c, inp.d_r, inp.rope_base, inp.sm_scale)
+    np.testing.assert_allclose(o, _decode_via_mqa_sdpa(inp), atol=1e-12)
+    assert np.isfinite(lse).all()
+
+
+def test_decode_ignores_rows_outside_its_sequence():
+    a = W.make_decode(3, 4, 16, 8, 5, 30, dtype=torch.float32, seed=5, gap_rows=0)
+    b = W.make_decode(3, 4, 16, 8, 5, 30, dtype=torch.float32, seed=5, gap_rows=7)
+    args = lambda i: (i.q_abs.numpy(), i.cache.numpy(), i.seq_start.numpy(), i.seq_len.numpy(),
+                      i.d_c, i.d_r, i.rope_base, i.sm_scale)
+    oa, la = O.decode_reference(*args(a))
+    ob, lb = O.decode_reference(*args(b))
+    np.testing.assert_array_equal(oa, ob)
+    np.testing.assert_array_equal(la, lb)
+
+
+def test_decode_single_token_and_lse_closed_form():
+    inp = W.make_decode(2, 3, 8, 4, 1, 1, dtype=torch.float32, seed=9)
+    q = inp.q_abs.double().numpy(); cache = inp.cache.double().numpy()
+    o, lse = O.decode_reference(q, cache, inp.seq_start.numpy(), inp.seq_len.numpy(),
+                                8, 4, inp.rope_base, inp.sm_scale)
+    for b in range(2):
+        row = cache[int(inp.seq_start[b])]
+        np.testing.assert_array_equal(o[b], np.broadcast_to(row[:8], (3, 8)))
+        # position 0: the rotation is the identity
+        np.testing.assert_allclose(lse[b], inp.sm_scale * q[b] @ row, atol=1e-12)
+
+
+def test_decode_equals_last_prefill_row():
+    """Prefill's last row and a decode step over prefill's own latent agree
+    once the query is absorbed (q~_h = W_UK^(h)T q_h) and W_UV is applied on
+    the output side."""
+    B, L, D, H, dc, dk, dv = 2, 9, 10, 3, 8, 4, 5
+    x = rng.standard_normal((B, L, D))
+    W_c = rng.standard_normal((dc, D)); W_q = rng.standard_normal((H * dk, D))
+    W_uk = rng.standard_normal((H, dk, dc)); W_uv = rng.standard_normal((H, dv, dc))
+    scale = 0.4
+    c, ot, lse = O.prefill_reference(x, W_c, W_q, W_uk, W_uv, scale)
+    q = (x[:, -1] @ W_q.T).reshape(B, H, dk)
+    q_abs = np.einsum("bhk,hkc->bhc", q, W_uk)
+    cache = c.reshape(B * L, dc)
+    o_lat, lse_d = O.decode_reference(q_abs, cache, np.arange(B) * L, np.full(B, L), dc, 0, 0.0, scale)
+    np.testing.assert_allclose(O.value_up_projection(o_lat, W_uv), ot[:, -1], atol=1e-11)
+    np.testing.assert_allclose(lse_d, lse[:, -1], atol=1e-11)
+
+
+def test_lse_merge_of_disjoint_key_sets_equals_whole():
+    L, H, d = 37, 4, 6
+    q = rng.standard_normal((1, H, d)); k = rng.standard_normal((L, H, d)); v = rng.standard_normal((L, H, 5))
+    full_o, full_l = O.attend_rows(q, k, v, [L - 1], 0.7)
+    parts = []
+    for lo, hi in [(0, 10), (10, 11), (11, 37)]:
+        # keys lo..hi-1 only: treat them as a sequence and attend from its end
+        o, l = O.attend_rows(q, k[lo:hi], v[lo:hi], [hi - lo - 1], 0.7)
+        parts.append((o, l))
+    parts.append((np.zeros_like(full_o), np.full_like(full_l, -np.inf)))  # an empty split
+    o, l = O.lse_merge(parts)
+    np.testing.assert_allclose(o, full_o, atol=1e-12)
+    np.testing.assert_allclose(l, full_l, atol=1e-12)
+
+
+def test_value_up_projection_moves_wuv_past_the_weighted_sum():
+    T, H, dc, dv, S = 3, 2, 5, 4, 7
+    a = scipy.special.softmax(rng.standard_normal((T, H, S)), axis=-1)
+    c = rng.standard_normal((S, dc))
+    W_uv = rng.standard_normal((H, dv, dc))
+    o_lat = np.einsum("ths,sc->thc", a, c)
+    explicit = np.einsum("ths,shd->thd", a, np.einsum("sc,hdc->shd", c, W_uv)).reshape(T, H * dv)
+    np.testing.assert_allclose(O.value_up_projection(o_lat, W_uv), explicit, atol=1e-12)
+
+
+# ---------------------------------------------------------------- brute force
+def _brute_layer(x, W_c, W_q, W_uk, W_uv, W_g, W_o, scale):
+    """Scalar loops over every index, math.exp only: one sequence."""
+    L, D = len(x), len(x[0])
+    H, dk, dc = len(W_uk), len(W_uk[0]), len(W_uk[0][0])
+    dv = len(W_uv[0])
+    c = [[sum(W_c[i][j] * x[s][j] for j in range(D)) for i in range(dc)] for s in range(L)]
+    y = []
+    for t in range(L):
+        ot = []
+        for h in range(H):
+            q = [sum(W_q[h * dk + i][j] * x[t][j] for j in range(D)) for i in range(dk)]
+            z = []
+            for s in range(t + 1):
+                k = [sum(W_uk[h][i][m] * c[s][m] for m in range(dc)) for i in range(dk)]
+                z.append(scale * sum(q[i] * k[i] for i in range(dk)))
+            mx = max(z)
+            e = [math.exp(v - mx) for v in z]
+            den = sum(e)
+            for i in range(dv):
+                acc = 0.0
+                for s in range(t + 1):
+                    v = sum(W_uv[h][i][m] * c[s][m] for m in range(dc))
+                    acc += e[s] / den * v
+                ot.append(acc)
+        g = [1.0 / (1.0 + math.exp(-sum(W_g[n][j] * x[t][j] for j in range(D)))) for n in range(H * dv)]
+        y.append([sum(W_o[i][n] * g[n] * ot[n] for n in range(H * dv)) for i in range(len(W_o))])
+    return c, y
+
+
+def test_whole_layer_matches_scalar_brute_force():
+    L, D, H, dc, dk, dv = 6, 5, 2, 4, 3, 3
+    x = rng.standard_normal((1, L, D))
+    ws = dict(W_c=rng.standard_normal((dc, D)), W_q=rng.standard_normal((H * dk, D)),
+              W_uk=rng.standard_normal((H, dk, dc)), W_uv=rng.standard_normal((H, dv, dc)),
+              W_g=rng.standard_normal((H * dv, D)), W_o=rng.standard_normal((D, H * dv)))
+    c, _, y = O.gated_mla_layer(x, *ws.values(), 0.45)
+    cb, yb = _brute_layer(x[0].tolist(), *[w.tolist() for w in ws.values()], 0.45)
+    np.testing.assert_allclose(c[0], cb, atol=1e-12)
+    np.testing.assert_allclose(y[0], yb, atol=1e-11)
+
+
+# ---------------------------------------------------------------- bytes
+def _bytes(case):
+    kw = {k: case[k] for k in ("h", "g", "d_h", "d_c", "d_r") if k in case}
+    n = O.kv_bytes_per_token(case["mechanism"], layers=case["layers"],
+                             bytes_per_elem=case["bytes_per_elem"], **kw)
+    return n * case.get("context", 1)
+
+
+def test_kv_bytes_reproduce_printed_worked_examples():
+    with open(os.path.join(GOLDEN, "kv_bytes_worked_examples.json")) as f:
+        g = json.load(f)
+    unit = {"elements": 1, "B": 1, "KiB": 1024, "MiB": 2 ** 20, "GiB": 2 ** 30}
+    for case in g["cases"]:
+        val = _bytes(case) / unit[case["unit"]]
+        tol = case.get("rounded_to", 0) / 2 + 1e-12
+        assert abs(val - case["printed"]) <= tol, (case["cite"], val)
+    mha = O.kv_bytes_per_token("MHA", h=128, d_h=128, layers=60)
+    mla = O.kv_bytes_per_token("MLA", d_c=512, d_r=64, layers=60)
+    assert abs(mha / mla - g["ratios"][0]["printed"]) <= g["ratios"][0]["tolerance"]
+    gqa = O.kv_bytes_per_token("GQA", h=64, g=8, d_h=128)
+    assert gqa / O.kv_bytes_per_token("MHA", h=64, d_h=128) == g["ratios"][1]["printed"]
+    # GQA end points: g = 1 is MQA, g = h is MHA
+    assert O.kv_bytes_per_token("GQA", h=8, g=1, d_h=64) == O.kv_bytes_per_token("MQA", d_h=64)
+    assert O.kv_bytes_per_token("GQA", h=8, g=8, d_h=64) == O.kv_bytes_per_token("MHA", h=8, d_h=64)
+    assert O.decode_step_cache_bytes([3, 4], 512, 64) == 7 * 1152
