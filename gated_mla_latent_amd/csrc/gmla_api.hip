@@ -1,0 +1,366 @@
+// C-ABI layer of libgmla: argument checks, workspace layout, dispatch to the
+// kernels, and the optional per-kernel event trace. See include/gmla.h.
+#include "../../include/gmla.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+
+using namespace gmla;
+
+namespace {
+
+thread_local std::string g_err;
+
+gmla_status_t fail(gmla_status_t s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+gmla_status_t ok() {
+  g_err.clear();
+  return GMLA_OK;
+}
+bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
+size_t esize(gmla_dtype_t dt) { return dt == GMLA_F32 ? 4 : 2; }
+
+#define REQUIRE(cond, status, msg) \
+  do {                             \
+    if (!(cond)) return fail(status, msg); \
+  } while (0)
+
+// ---------------------------------------------------------------- trace
+struct TraceRec {
+  const char* name;
+  hipEvent_t start, stop;
+};
+std::mutex g_tr_mu;
+bool g_tr_on = false;
+std::vector<TraceRec> g_tr;
+int g_tr_used = 0;
+std::string g_tr_names;
+
+int trace_pre(const char* name, hipStream_t st) {
+  if (!g_tr_on) return -1;
+  std::lock_guard<std::mutex> lk(g_tr_mu);
+  if (g_tr_used >= (int)g_tr.size()) return -1;
+  const int i = g_tr_used++;
+  g_tr[i].name = name;
+  hipEventRecord(g_tr[i].start, st);
+  return i;
+}
+void trace_post(int i, hipStream_t st) {
+  if (i >= 0) hipEventRecord(g_tr[i].stop, st);
+}
+
+template <class F>
+gmla_status_t run(const char* name, hipStream_t st, F&& f) {
+  const int tr = trace_pre(name, st);
+  hipError_t e = f();
+  trace_post(tr, st);
+  if (e != hipSuccess) return fail(GMLA_ERR_HIP, std::string(name) + ": " + hipGetErrorString(e));
+  return GMLA_OK;
+}
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
+  return cus;
+}
+
+int decode_slices(int num_splits) { return num_splits > 0 ? num_splits : device_cus(); }
+
+GemmArgs gemm(const void* A, int64_t lda, const void* W, int64_t ldw, void* C, int64_t ldc, int M, int N, int K,
+              int epi = EPI_STORE, const void* O = nullptr, int64_t ldo = 0) {
+  GemmArgs g{};
+  g.A = (const bf16*)A; g.W = (const bf16*)W; g.C = (bf16*)C; g.O = (const bf16*)O;
+  g.M = M; g.N = N; g.K = K; g.batches = 1;
+  g.lda = lda; g.ldw = ldw; g.ldc = ldc; g.ldo = ldo;
+  g.epi = epi;
+  return g;
+}
+GemmF32Args gemm32(const void* A, int64_t lda, const void* W, int64_t ldw, void* C, int64_t ldc, int M, int N, int K,
+                   int epi = EPI_STORE, const void* O = nullptr, int64_t ldo = 0) {
+  GemmF32Args g{};
+  g.A = (const float*)A; g.W = (const float*)W; g.C = (float*)C; g.O = (const float*)O;
+  g.M = M; g.N = N; g.K = K; g.batches = 1;
+  g.lda = lda; g.ldw = ldw; g.ldc = ldc; g.ldo = ldo;
+  g.epi = epi;
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gmla_status_string(gmla_status_t s) {
+  switch (s) {
+    case GMLA_OK: return "ok";
+    case GMLA_ERR_INVALID_ARG: return "invalid argument";
+    case GMLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case GMLA_ERR_WORKSPACE: return "workspace too small";
+    case GMLA_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* gmla_last_error(void) { return g_err.c_str(); }
+
+int gmla_version(void) { return 10000; }
+
+// ============================================================ prefill
+size_t gmla_prefill_workspace_size(int B, int L, int H, int d_k, int d_v, gmla_dtype_t dtype) {
+  if (B <= 0 || L <= 0 || H <= 0 || d_k <= 0 || d_v <= 0) return 0;
+  const size_t T = (size_t)B * L;
+  const size_t es = esize(dtype);
+  return up256(T * H * d_k * es) * 2 + up256(T * H * d_v * es);
+}
+
+gmla_status_t gmla_prefill(const void* x, const void* W_c, const void* W_q, const void* W_uk, const void* W_uv,
+                           void* latent_out, void* o_tilde, void* workspace, size_t workspace_bytes, int B, int L,
+                           int d_model, int H, int d_c, int d_k, int d_v, float sm_scale, gmla_dtype_t dtype,
+                           void* stream) {
+  REQUIRE(dtype == GMLA_F32 || dtype == GMLA_BF16, GMLA_ERR_INVALID_ARG, "dtype must be GMLA_F32 or GMLA_BF16");
+  REQUIRE(x && W_c && W_q && W_uk && W_uv && latent_out && o_tilde, GMLA_ERR_INVALID_ARG, "null tensor pointer");
+  REQUIRE(B > 0 && L > 0 && d_model > 0 && H > 0 && d_c > 0 && d_k > 0 && d_v > 0, GMLA_ERR_INVALID_ARG,
+          "sizes must be positive");
+  REQUIRE(std::isfinite(sm_scale), GMLA_ERR_INVALID_ARG, "sm_scale must be finite");
+  REQUIRE(al16(x) && al16(W_c) && al16(W_q) && al16(W_uk) && al16(W_uv) && al16(latent_out) && al16(o_tilde),
+          GMLA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  REQUIRE((long long)B * L * std::max(std::max(d_model, H * d_k), H * d_v) < (1LL << 40), GMLA_ERR_UNSUPPORTED,
+          "problem too large");
+  if (dtype == GMLA_BF16) {
+    REQUIRE(d_model % 64 == 0, GMLA_ERR_UNSUPPORTED, "bf16 prefill needs d_model % 64 == 0");
+    REQUIRE(d_c % 64 == 0, GMLA_ERR_UNSUPPORTED, "bf16 prefill needs d_c % 64 == 0");
+    REQUIRE(d_k == d_v && (d_k == 64 || d_k == 128), GMLA_ERR_UNSUPPORTED,
+            "bf16 prefill needs d_k == d_v in {64, 128}");
+  } else {
+    REQUIRE(d_k <= 1024 && d_v <= 512, GMLA_ERR_UNSUPPORTED, "fp32 prefill needs d_k <= 1024, d_v <= 512");
+  }
+  const size_t need = gmla_prefill_workspace_size(B, L, H, d_k, d_v, dtype);
+  REQUIRE(workspace && workspace_bytes >= need, GMLA_ERR_WORKSPACE,
+          "prefill workspace needs " + std::to_string(need) + " bytes");
+  REQUIRE(al16(workspace), GMLA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+
+  hipStream_t st = (hipStream_t)stream;
+  const int T = B * L;
+  const size_t es = esize(dtype);
+  char* ws = (char*)workspace;
+  void* q = ws;
+  void* k = ws + up256((size_t)T * H * d_k * es);
+  void* v = (char*)k + up256((size_t)T * H * d_k * es);
+  const int HK = H * d_k, HV = H * d_v;
+  gmla_status_t s;
+  if (dtype == GMLA_BF16) {
+    // c = x W_c^T (cache rows), q = x W_q^T, K = c W_UK^T, V = c W_UV^T (W_UK as [H*d_k, d_c])
+    if ((s = run("gemm_latent", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_c, d_model, latent_out, d_c, T, d_c, d_model), st); }))) return s;
+    if ((s = run("gemm_query", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_q, d_model, q, HK, T, HK, d_model), st); }))) return s;
+    if ((s = run("gemm_key_recon", st, [&] { return launch_gemm_bf16(gemm(latent_out, d_c, W_uk, d_c, k, HK, T, HK, d_c), st); }))) return s;
+    if ((s = run("gemm_value_recon", st, [&] { return launch_gemm_bf16(gemm(latent_out, d_c, W_uv, d_c, v, HV, T, HV, d_c), st); }))) return s;
+    AttnArgs a{};
+    a.q = (const bf16*)q; a.k = (const bf16*)k; a.v = (const bf16*)v; a.o = (bf16*)o_tilde;
+    a.B = B; a.L = L; a.H = H; a.D = d_k;
+    a.sqb = (int64_t)L * HK; a.sqt = HK; a.sqh = d_k;
+    a.skb = (int64_t)L * HK; a.skt = HK; a.skh = d_k;
+    a.svb = (int64_t)L * HV; a.svt = HV; a.svh = d_v;
+    a.sob = (int64_t)L * HV; a.sot = HV; a.soh = d_v;
+    a.scale_log2 = sm_scale * 1.4426950408889634f;
+    if ((s = run("prefill_attn", st, [&] { return launch_prefill_attn_bf16(a, st); }))) return s;
+  } else {
+    if ((s = run("gemm_f32", st, [&] { return launch_gemm_f32(gemm32(x, d_model, W_c, d_model, latent_out, d_c, T, d_c, d_model), st); }))) return s;
+    if ((s = run("gemm_f32", st, [&] { return launch_gemm_f32(gemm32(x, d_model, W_q, d_model, q, HK, T, HK, d_model), st); }))) return s;
+    if ((s = run("gemm_f32", st, [&] { return launch_gemm_f32(gemm32(latent_out, d_c, W_uk, d_c, k, HK, T, HK, d_c), st); }))) return s;
+    if ((s = run("gemm_f32", st, [&] { return launch_gemm_f32(gemm32(latent_out, d_c, W_uv, d_c, v, HV, T, HV, d_c), st); }))) return s;
+    AttnF32Args a{};
+    a.q = (const float*)q; a.k = (const float*)k; a.v = (const float*)v; a.o = (float*)o_tilde;
+    a.B = B; a.L = L; a.H = H; a.Dk = d_k; a.Dv = d_v;
+    a.sqb = (int64_t)L * HK; a.sqt = HK; a.sqh = d_k;
+    a.skb = (int64_t)L * HK; a.skt = HK; a.skh = d_k;
+    a.svb = (int64_t)L * HV; a.svt = HV; a.svh = d_v;
+    a.sob = (int64_t)L * HV; a.sot = HV; a.soh = d_v;
+    a.scale = sm_scale;
+    if ((s = run("prefill_attn_f32", st, [&] { return launch_prefill_attn_f32(a, st); }))) return s;
+  }
+  return ok();
+}
+
+// ============================================================ decode
+size_t gmla_decode_workspace_size(int B, int H, int d_c, int num_splits, gmla_dtype_t dtype) {
+  if (B <= 0 || H <= 0 || d_c <= 0 || num_splits < 0) return 0;
+  if (dtype == GMLA_F32) return 0;
+  const size_t G = (size_t)decode_slices(num_splits);
+  return up256((size_t)B * 8) + up256(2 * G * H * 4) + up256(2 * G * H * (size_t)d_c * 4);
+}
+
+gmla_status_t gmla_decode(const void* q_abs, const void* cache, const int64_t* seq_start, const int32_t* seq_len,
+                          void* o_lat, float* lse, void* workspace, size_t workspace_bytes, int B, int H, int d_c,
+                          int d_r, float rope_base, float sm_scale, int num_splits, gmla_dtype_t dtype,
+                          void* stream) {
+  REQUIRE(dtype == GMLA_F32 || dtype == GMLA_BF16, GMLA_ERR_INVALID_ARG, "dtype must be GMLA_F32 or GMLA_BF16");
+  REQUIRE(q_abs && cache && seq_start && seq_len && o_lat, GMLA_ERR_INVALID_ARG, "null tensor pointer");
+  REQUIRE(B > 0 && H > 0 && d_c > 0 && d_r >= 0, GMLA_ERR_INVALID_ARG, "sizes must be positive (d_r >= 0)");
+  REQUIRE(d_r % 2 == 0, GMLA_ERR_INVALID_ARG, "d_r must be even (RoPE pairs)");
+  REQUIRE(num_splits >= 0 && num_splits <= 65535, GMLA_ERR_INVALID_ARG, "num_splits must be in [0, 65535]");
+  REQUIRE(std::isfinite(sm_scale) && std::isfinite(rope_base) && rope_base >= 0.f, GMLA_ERR_INVALID_ARG,
+          "sm_scale must be finite and rope_base finite and >= 0");
+  REQUIRE(al16(q_abs) && al16(cache) && al16(seq_start) && al16(seq_len) && al16(o_lat) && (!lse || al16(lse)),
+          GMLA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == GMLA_F32) {
+    REQUIRE(d_c + d_r <= 1024 && d_c <= 512, GMLA_ERR_UNSUPPORTED, "fp32 decode needs d_c + d_r <= 1024, d_c <= 512");
+    DecodeF32Args a{};
+    a.q = (const float*)q_abs; a.cache = (const float*)cache; a.seq_start = seq_start; a.seq_len = seq_len;
+    a.o_lat = (float*)o_lat; a.lse = lse; a.B = B; a.H = H; a.d_c = d_c; a.d_r = d_r;
+    a.scale = sm_scale; a.rope_base = d_r > 0 ? rope_base : 0.f;
+    gmla_status_t s = run("decode_f32", st, [&] { return launch_decode_f32(a, st); });
+    return s ? s : ok();
+  }
+  REQUIRE(decode_bf16_supported(d_c, d_r), GMLA_ERR_UNSUPPORTED, "bf16 decode needs d_c == 512 and d_r in {0, 64}");
+  const int G = decode_slices(num_splits);
+  const size_t need = gmla_decode_workspace_size(B, H, d_c, num_splits, dtype);
+  REQUIRE(workspace && workspace_bytes >= need, GMLA_ERR_WORKSPACE,
+          "decode workspace needs " + std::to_string(need) + " bytes");
+  REQUIRE(((uintptr_t)workspace & 255u) == 0, GMLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  char* ws = (char*)workspace;
+  DecodeArgs a{};
+  a.q = (const bf16*)q_abs; a.cache = (const bf16*)cache; a.seq_start = seq_start; a.seq_len = seq_len;
+  a.o_lat = (bf16*)o_lat; a.lse = lse;
+  a.prefix = (long long*)ws;
+  a.part_lse = (float*)(ws + up256((size_t)B * 8));
+  a.part_o = (float*)(ws + up256((size_t)B * 8) + up256(2 * (size_t)G * H * 4));
+  a.B = B; a.H = H; a.d_c = d_c; a.d_r = d_r; a.G = G;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.rope_base = d_r > 0 ? rope_base : 0.f;
+  gmla_status_t s;
+  if ((s = run("decode_attn", st, [&] { return launch_decode_attn(a, st); }))) return s;
+  if ((s = run("decode_combine", st, [&] { return launch_decode_combine(a, st); }))) return s;
+  return ok();
+}
+
+// ============================================================ gate + output
+size_t gmla_gate_out_workspace_size(int T, int H, int d_v, int with_value_up, gmla_dtype_t dtype) {
+  if (T <= 0 || H <= 0 || d_v <= 0) return 0;
+  const size_t one = up256((size_t)T * H * d_v * esize(dtype));
+  return with_value_up ? 2 * one : one;
+}
+
+gmla_status_t gmla_gate_out(const void* x, const void* o, const void* W_uv, const void* W_g, const void* W_o, void* y,
+                            void* workspace, size_t workspace_bytes, int T, int d_model, int H, int d_c, int d_v,
+                            gmla_dtype_t dtype, void* stream) {
+  REQUIRE(dtype == GMLA_F32 || dtype == GMLA_BF16, GMLA_ERR_INVALID_ARG, "dtype must be GMLA_F32 or GMLA_BF16");
+  REQUIRE(x && o && W_g && W_o && y, GMLA_ERR_INVALID_ARG, "null tensor pointer");
+  REQUIRE(T > 0 && d_model > 0 && H > 0 && d_v > 0 && (!W_uv || d_c > 0), GMLA_ERR_INVALID_ARG,
+          "sizes must be positive");
+  REQUIRE(al16(x) && al16(o) && (!W_uv || al16(W_uv)) && al16(W_g) && al16(W_o) && al16(y), GMLA_ERR_INVALID_ARG,
+          "tensor pointers must be 16-byte aligned");
+  const int HV = H * d_v;
+  if (dtype == GMLA_BF16) {
+    REQUIRE(d_model % 64 == 0 && HV % 64 == 0 && d_v % 4 == 0, GMLA_ERR_UNSUPPORTED,
+            "bf16 gate_out needs d_model % 64 == 0, H*d_v % 64 == 0, d_v % 4 == 0");
+    REQUIRE(!W_uv || d_c % 64 == 0, GMLA_ERR_UNSUPPORTED, "bf16 value up-projection needs d_c % 64 == 0");
+  }
+  const size_t need = gmla_gate_out_workspace_size(T, H, d_v, W_uv != nullptr, dtype);
+  REQUIRE(workspace && workspace_bytes >= need, GMLA_ERR_WORKSPACE,
+          "gate_out workspace needs " + std::to_string(need) + " bytes");
+  REQUIRE(al16(workspace), GMLA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  const size_t es = esize(dtype);
+  char* ws = (char*)workspace;
+  void* gated = ws;
+  const void* ot = o;
+  gmla_status_t s;
+  if (dtype == GMLA_BF16) {
+    if (W_uv) {
+      void* otw = ws + up256((size_t)T * HV * es);
+      GemmArgs g = gemm(o, (int64_t)H * d_c, W_uv, d_c, otw, HV, T, d_v, d_c);
+      g.batches = H; g.sA = d_c; g.sW = (int64_t)d_v * d_c; g.sC = d_v;
+      if ((s = run("gemm_value_up", st, [&] { return launch_gemm_bf16(g, st); }))) return s;
+      ot = otw;
+    }
+    if ((s = run("gemm_gate", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_g, d_model, gated, HV, T, HV, d_model, EPI_GATE, ot, HV), st); }))) return s;
+    if ((s = run("gemm_out", st, [&] { return launch_gemm_bf16(gemm(gated, HV, W_o, HV, y, d_model, T, d_model, HV), st); }))) return s;
+  } else {
+    if (W_uv) {
+      void* otw = ws + up256((size_t)T * HV * es);
+      GemmF32Args g = gemm32(o, (int64_t)H * d_c, W_uv, d_c, otw, HV, T, d_v, d_c);
+      g.batches = H; g.sA = d_c; g.sW = (int64_t)d_v * d_c; g.sC = d_v;
+      if ((s = run("gemm_f32", st, [&] { return launch_gemm_f32(g, st); }))) return s;
+      ot = otw;
+    }
+    if ((s = run("gemm_f32", st, [&] { return launch_gemm_f32(gemm32(x, d_model, W_g, d_model, gated, HV, T, HV, d_model, EPI_GATE, ot, HV), st); }))) return s;
+    if ((s = run("gemm_f32", st, [&] { return launch_gemm_f32(gemm32(gated, HV, W_o, HV, y, d_model, T, d_model, HV), st); }))) return s;
+  }
+  return ok();
+}
+
+// ============================================================ trace
+gmla_status_t gmla_trace_begin(int max_launches) {
+  REQUIRE(max_launches > 0 && max_launches <= (1 << 20), GMLA_ERR_INVALID_ARG, "max_launches out of range");
+  std::lock_guard<std::mutex> lk(g_tr_mu);
+  while ((int)g_tr.size() < max_launches) {
+    TraceRec r{nullptr, nullptr, nullptr};
+    if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess)
+      return fail(GMLA_ERR_HIP, "hipEventCreate failed");
+    g_tr.push_back(r);
+  }
+  g_tr_on = true;
+  return ok();
+}
+
+gmla_status_t gmla_trace_end(void) {
+  std::lock_guard<std::mutex> lk(g_tr_mu);
+  g_tr_on = false;
+  return ok();
+}
+
+gmla_status_t gmla_trace_summary(const char* name, int* count, double* mean_ms) {
+  REQUIRE(name && count && mean_ms, GMLA_ERR_INVALID_ARG, "null argument");
+  std::lock_guard<std::mutex> lk(g_tr_mu);
+  int n = 0;
+  double sum = 0;
+  for (int i = 0; i < g_tr_used; ++i) {
+    if (!g_tr[i].name || std::strcmp(g_tr[i].name, name) != 0) continue;
+    if (hipEventSynchronize(g_tr[i].stop) != hipSuccess) return fail(GMLA_ERR_HIP, "hipEventSynchronize failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, g_tr[i].start, g_tr[i].stop) != hipSuccess)
+      return fail(GMLA_ERR_HIP, "hipEventElapsedTime failed");
+    sum += ms;
+    ++n;
+  }
+  *count = n;
+  *mean_ms = n ? sum / n : 0.0;
+  return ok();
+}
+
+const char* gmla_trace_kernels(void) {
+  std::lock_guard<std::mutex> lk(g_tr_mu);
+  g_tr_names.clear();
+  for (int i = 0; i < g_tr_used; ++i) {
+    const std::string nm = g_tr[i].name ? g_tr[i].name : "";
+    if ((";" + g_tr_names + ";").find(";" + nm + ";") == std::string::npos) {
+      if (!g_tr_names.empty()) g_tr_names += ";";
+      g_tr_names += nm;
+    }
+  }
+  return g_tr_names.c_str();
+}
+
+void gmla_trace_reset(void) {
+  std::lock_guard<std::mutex> lk(g_tr_mu);
+  for (auto& r : g_tr) {
+    if (r.start) hipEventDestroy(r.start);
+    if (r.stop) hipEventDestroy(r.stop);
+  }
+  g_tr.clear();
+  g_tr_used = 0;
+  g_tr_on = false;
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// Internal launch interface between the C-ABI layer and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gmla {
+
+typedef __bf16 bf16;
+
+// ---------------------------------------------------------------- decode
+struct DecodeArgs {
+  const bf16* q;            // [B, H, d_c + d_r]
+  const bf16* cache;        // [rows, d_c + d_r]
+  const int64_t* seq_start; // [B] first cache row of each sequence
+  const int32_t* seq_len;   // [B]
+  bf16* o_lat;              // [B, H, d_c]
+  float* lse;               // [B, H] or null
+  float* part_o;            // [2G, H, d_c] partial outputs of cut sequences
+  float* part_lse;          // [2G, H]
+  long long* prefix;        // [B] exclusive prefix sums of seq_len
+  int B, H, d_c, d_r, G;
+  float scale_log2;         // sm_scale * log2(e)
+  float rope_base;          // 0 = no rotation of the query's RoPE part
+};
+hipError_t launch_decode_attn(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st);
+bool decode_bf16_supported(int d_c, int d_r);
+
+// ---------------------------------------------------------------- GEMM
+// C[m, n] = epi( sum_k A[m, k] * W[n, k] ), all bf16 with fp32 accumulation.
+// A is [M, K] (row stride lda), W is [N, K] (row stride ldw), C is [M, N]
+// (row stride ldc). Batches advance every pointer by its batch stride.
+enum GemmEpilogue { EPI_STORE = 0, EPI_GATE = 1 };
+struct GemmArgs {
+  const bf16* A;
+  const bf16* W;
+  bf16* C;
+  const bf16* O;            // EPI_GATE: C = sigmoid(acc) * O[m, n]
+  int M, N, K, batches;
+  int64_t lda, ldw, ldc, ldo;
+  int64_t sA, sW, sC, sO;   // batch strides (elements)
+  int epi;
+};
+hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t st);
+
+// ---------------------------------------------------------------- prefill attention
+// Causal flash attention, one head per (b, h): q,k,v rows of width D.
+// Element (b, t, h, :) of X lives at X + b*sXb + t*sXt + h*sXh.
+struct AttnArgs {
+  const bf16* q; const bf16* k; const bf16* v; bf16* o;
+  int B, L, H, D;
+  int64_t sqb, sqt, sqh, skb, skt, skh, svb, svt, svh, sob, sot, soh;
+  float scale_log2;
+};
+hipError_t launch_prefill_attn_bf16(const AttnArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------- fp32 path
+struct GemmF32Args {
+  const float* A; const float* W; float* C; const float* O;
+  int M, N, K, batches;
+  int64_t lda, ldw, ldc, ldo, sA, sW, sC, sO;
+  int epi;
+};
+hipError_t launch_gemm_f32(const GemmF32Args& g, hipStream_t st);
+struct AttnF32Args {
+  const float* q; const float* k; const float* v; float* o;
+  int B, L, H, Dk, Dv;
+  int64_t sqb, sqt, sqh, skb, skt, skh, svb, svt, svh, sob, sot, soh;
+  float scale;
+};
+hipError_t launch_prefill_attn_f32(const AttnF32Args& a, hipStream_t st);
+struct DecodeF32Args {
+  const float* q; const float* cache; const int64_t* seq_start; const int32_t* seq_len;
+  float* o_lat; float* lse;
+  int B, H, d_c, d_r;
+  float scale, rope_base;
+};
+hipError_t launch_decode_f32(const DecodeF32Args& a, hipStream_t st);
+
+}  // namespace gmla

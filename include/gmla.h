@@ -1,0 +1,154 @@
+/*
+ * gmla.h -- Gated Multi-head Latent Attention kernels for AMD Instinct MI355X
+ * (gfx950). C ABI of libgmla.so.
+ *
+ * What the library computes (sources are web pages, cited by title and
+ * section):
+ *   [GF]  "Gated MLA 计算公式：输出门与 FFN 的区别" -- §一: each token caches a
+ *         latent c_s = W_c x_s and every head reconstructs k = W_k^(h) c,
+ *         v = W_v^(h) c; §二: per-head causal softmax attention over s <= t,
+ *         head concatenation o~_t, and the per-channel output gate
+ *         y_t = W_o [ Sigmoid(W_g x_t) (.) o~_t ]; NoPE in Kimi K3.
+ *   [N03] "LLM 注意力与计算内核精读笔记 · 03 注意力头变体：MQA / GQA / MLA" --
+ *         §5.1: W^UK folds into the query and W^UV moves past the weighted
+ *         sum, so decode attends the latent directly; §5.2: decoupled RoPE,
+ *         a shared d_h^R-wide rotated key cached next to the latent.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor is dense and row-major (last index fastest). Weights use
+ *     the [out_features, in_features] layout. Device pointers unless stated.
+ *   - dtype GMLA_BF16: bf16 storage, fp32 accumulation, intermediates (c, q,
+ *     K, V, P, o~, gated) rounded to bf16 (round to nearest even).
+ *     dtype GMLA_F32: fp32 storage and true fp32 arithmetic throughout.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously; nothing synchronises the host.
+ *   - The caller owns every buffer. The library allocates no device memory in
+ *     these calls and keeps no state between them (apart from the optional
+ *     trace below). Scratch space is the caller's `workspace`, at least the
+ *     size the matching *_workspace_size() returns, 256-byte aligned.
+ *     Calls that share a workspace must not overlap in time.
+ *   - Errors: arguments are checked on the host before anything is enqueued.
+ *     A failed check returns a status != GMLA_OK and enqueues nothing.
+ *     GMLA_ERR_HIP reports a HIP launch error. gmla_last_error() gives a
+ *     human-readable reason for the calling thread's last failure.
+ *     No function aborts or throws.
+ *   - Every device pointer must be 16-byte aligned.
+ */
+#ifndef GMLA_H
+#define GMLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GMLA_OK = 0,
+  GMLA_ERR_INVALID_ARG = 1, /* null pointer, misalignment, non-positive size */
+  GMLA_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels implement */
+  GMLA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  GMLA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} gmla_status_t;
+
+typedef enum { GMLA_F32 = 0, GMLA_BF16 = 1 } gmla_dtype_t;
+
+/* ------------------------------------------------------------------------
+ * Prefill: latent projection, explicit per-head K/V reconstruction and
+ * causal attention ([GF] §一 and §二 first two equations).
+ *
+ *   x          [B, L, d_model]      input hidden states
+ *   W_c        [d_c, d_model]       latent (down) projection
+ *   W_q        [H*d_k, d_model]     query projection, head-major rows
+ *   W_uk       [H, d_k, d_c]        per-head key up-projection
+ *   W_uv       [H, d_v, d_c]        per-head value up-projection
+ *   latent_out [B, L, d_c]          out: c_s = W_c x_s (the cache rows)
+ *   o_tilde    [B, L, H*d_v]        out: o~_t = Concat_h o_t^(h), channel
+ *                                   h*d_v + j; o_t^(h) = sum_{s<=t}
+ *                                   softmax_s(sm_scale q_t^(h).k_s^(h)) v_s^(h)
+ * The gate and output projection follow with gmla_gate_out(W_uv = NULL).
+ * Sizes: all >= 1. BF16 needs d_model % 64 == 0, d_c % 64 == 0 and
+ * d_k == d_v in {64, 128}; F32 needs d_k <= 1024 and d_v <= 512.
+ * ---------------------------------------------------------------------- */
+size_t gmla_prefill_workspace_size(int B, int L, int H, int d_k, int d_v, gmla_dtype_t dtype);
+gmla_status_t gmla_prefill(const void* x, const void* W_c, const void* W_q, const void* W_uk, const void* W_uv,
+                           void* latent_out, void* o_tilde, void* workspace, size_t workspace_bytes, int B, int L,
+                           int d_model, int H, int d_c, int d_k, int d_v, float sm_scale, gmla_dtype_t dtype,
+                           void* stream);
+
+/* ------------------------------------------------------------------------
+ * Decode: one query token per sequence against the latent cache, with W_UK
+ * already absorbed into the query ([N03] §5.1, exercise 4 answer) and an
+ * optional decoupled RoPE part ([N03] §5.2).
+ *
+ *   q_abs     [B, H, d_c + d_r]  q~_h = (W_UK^(h))^T q_h, then the RoPE query
+ *                                part (not yet rotated; rotated here to
+ *                                position seq_len[b] - 1 unless rope_base == 0)
+ *   cache     [rows, d_c + d_r]  row j = [c_j ; kR_j], kR_j already rotated
+ *   seq_start [B] int64 (device) first cache row of sequence b
+ *   seq_len   [B] int32 (device) L_b; rows seq_start[b] .. + L_b - 1
+ *   o_lat     [B, H, d_c]        out: sum_j softmax_j(s) c_j with
+ *                                s_j = sm_scale (q~_h . [c_j ; kR_j])
+ *   lse       [B, H] fp32 or NULL  out: natural log of sum_j exp(s_j)
+ * Every head shares one latent row per token (MQA-shaped), V is the latent
+ * part c_j only. L_b >= 1 is required; a sequence with L_b <= 0 yields
+ * o_lat = 0 and lse = -inf. The seq_* arrays are read on the device and
+ * trusted (rows must lie inside `cache`).
+ * num_splits: number of equal slices the concatenated token range of all
+ * sequences is cut into (one workgroup each); 0 = one per compute unit.
+ * The result does not depend on it beyond fp32 rounding.
+ * BF16 needs d_c == 512 and d_r in {0, 64}; F32 needs
+ * d_c + d_r <= 1024 and d_c <= 512.
+ * ---------------------------------------------------------------------- */
+size_t gmla_decode_workspace_size(int B, int H, int d_c, int num_splits, gmla_dtype_t dtype);
+gmla_status_t gmla_decode(const void* q_abs, const void* cache, const int64_t* seq_start, const int32_t* seq_len,
+                          void* o_lat, float* lse, void* workspace, size_t workspace_bytes, int B, int H, int d_c,
+                          int d_r, float rope_base, float sm_scale, int num_splits, gmla_dtype_t dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Gate and output projection ([GF] §二 boxed equation):
+ *   y_t = W_o [ Sigmoid(W_g x_t) (.) o~_t ]
+ * With W_uv == NULL, `o` is o~ [T, H*d_v] (prefill output). With W_uv given,
+ * `o` is the decode output o_lat [T, H, d_c] and o~_h = W_uv[h] o_lat_h is
+ * formed first (W_UV moved to the output side, [N03] §5.1; it cannot be
+ * pre-multiplied into W_o because the gate between them is per channel).
+ *   x [T, d_model], W_g [H*d_v, d_model], W_o [d_model, H*d_v], y [T, d_model]
+ * BF16 needs d_model % 64 == 0, (H*d_v) % 64 == 0, d_c % 64 == 0 and
+ * d_v % 4 == 0.
+ * ---------------------------------------------------------------------- */
+size_t gmla_gate_out_workspace_size(int T, int H, int d_v, int with_value_up, gmla_dtype_t dtype);
+gmla_status_t gmla_gate_out(const void* x, const void* o, const void* W_uv, const void* W_g, const void* W_o,
+                            void* y, void* workspace, size_t workspace_bytes, int T, int d_model, int H, int d_c,
+                            int d_v, gmla_dtype_t dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Diagnostics
+ * ---------------------------------------------------------------------- */
+const char* gmla_status_string(gmla_status_t status);
+/* Reason for the calling thread's most recent failure ("" if none). */
+const char* gmla_last_error(void);
+/* Library version as 10000*major + 100*minor + patch. */
+int gmla_version(void);
+
+/* Kernel trace: while enabled, every kernel the library enqueues is bracketed
+ * by a pair of HIP events recorded on the same stream, so per-kernel device
+ * time can be read back without a profiler. gmla_trace_begin creates up to
+ * max_launches event pairs (host-side HIP objects) and starts recording;
+ * launches beyond that are not traced. gmla_trace_end stops recording.
+ * gmla_trace_summary waits for the recorded events and returns, for kernel
+ * `name`, the number of traced launches and their mean duration in
+ * milliseconds (count 0 if none). gmla_trace_reset drops all records and
+ * destroys the events. Not for concurrent use from several threads. */
+gmla_status_t gmla_trace_begin(int max_launches);
+gmla_status_t gmla_trace_end(void);
+gmla_status_t gmla_trace_summary(const char* name, int* count, double* mean_ms);
+/* Names of the kernels seen so far, separated by ';' (valid until the next
+ * trace call). */
+const char* gmla_trace_kernels(void);
+void gmla_trace_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GMLA_H */

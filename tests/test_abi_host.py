@@ -1,0 +1,122 @@
+"""Host-side checks of libgmla.so (no GPU needed): the library loads, exports
+every function include/gmla.h declares, and rejects bad arguments with the
+documented status before anything reaches the GPU."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from gated_mla_latent_amd import build, ops
+    if not os.path.exists(ops.LIB_PATH):
+        build.build()
+    return ops.lib()
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "gmla.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(gmla_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version(L):
+    assert L.gmla_status_string(0) == b"ok"
+    assert L.gmla_status_string(3) == b"workspace too small"
+    assert L.gmla_version() >= 10000
+
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+A = 0x100000  # an aligned fake device address; never dereferenced (validation fails first)
+
+
+def _dec(L, **kw):
+    a = dict(q=A, cache=A, start=A, len_=A, o=A, lse=0, ws=A, wsb=1 << 40, B=4, H=64, d_c=512, d_r=0,
+             base=10000.0, scale=0.1, splits=8, dt=1)
+    a.update(kw)
+    return L.gmla_decode(a["q"], a["cache"], a["start"], a["len_"], a["o"], a["lse"], a["ws"], a["wsb"], a["B"],
+                         a["H"], a["d_c"], a["d_r"], a["base"], a["scale"], a["splits"], a["dt"], None)
+
+
+def test_decode_argument_checks(L):
+    assert _dec(L, q=0) == INVALID
+    assert _dec(L, cache=A + 8) == INVALID          # misaligned
+    assert _dec(L, B=0) == INVALID
+    assert _dec(L, d_r=3) == INVALID                # odd RoPE width
+    assert _dec(L, splits=-1) == INVALID
+    assert _dec(L, scale=float("nan")) == INVALID
+    assert _dec(L, base=-1.0) == INVALID
+    assert _dec(L, dt=7) == INVALID
+    assert _dec(L, d_c=384) == UNSUPPORTED          # bf16 kernels take d_c == 512
+    assert _dec(L, d_c=256) == UNSUPPORTED
+    assert _dec(L, d_r=32) == UNSUPPORTED
+    assert _dec(L, wsb=16) == WORKSPACE
+    assert _dec(L, ws=0) == WORKSPACE
+    assert b"workspace" in L.gmla_last_error()
+    assert _dec(L, ws=A + 16) == INVALID            # workspace must be 256-byte aligned
+
+
+def test_decode_workspace_size_formula(L):
+    B, H, d_c, G = 4, 64, 512, 8
+    up = lambda n: (n + 255) // 256 * 256
+    assert L.gmla_decode_workspace_size(B, H, d_c, G, 1) == up(B * 8) + up(2 * G * H * 4) + up(2 * G * H * d_c * 4)
+    assert L.gmla_decode_workspace_size(B, H, d_c, G, 0) == 0  # fp32 path needs none
+    assert L.gmla_decode_workspace_size(0, H, d_c, G, 1) == 0
+
+
+def _pre(L, **kw):
+    a = dict(x=A, Wc=A, Wq=A, Wuk=A, Wuv=A, lat=A, ot=A, ws=A, wsb=1 << 40, B=1, Lq=16, D=256, H=2, d_c=128, d_k=128,
+             d_v=128, scale=0.1, dt=1)
+    a.update(kw)
+    return L.gmla_prefill(a["x"], a["Wc"], a["Wq"], a["Wuk"], a["Wuv"], a["lat"], a["ot"], a["ws"], a["wsb"], a["B"],
+                          a["Lq"], a["D"], a["H"], a["d_c"], a["d_k"], a["d_v"], a["scale"], a["dt"], None)
+
+
+def test_prefill_argument_checks(L):
+    assert _pre(L, Wq=0) == INVALID
+    assert _pre(L, x=A + 2) == INVALID
+    assert _pre(L, Lq=0) == INVALID
+    assert _pre(L, D=100) == UNSUPPORTED            # bf16 needs d_model % 64 == 0
+    assert _pre(L, d_c=96) == UNSUPPORTED
+    assert _pre(L, d_k=96, d_v=96) == UNSUPPORTED
+    assert _pre(L, d_k=128, d_v=64) == UNSUPPORTED
+    assert _pre(L, d_v=2048, d_k=2048, dt=0) == UNSUPPORTED
+    assert _pre(L, wsb=100) == WORKSPACE
+    need = L.gmla_prefill_workspace_size(1, 16, 2, 128, 128, 1)
+    assert need == 3 * 16 * 2 * 128 * 2
+
+
+def _gate(L, **kw):
+    a = dict(x=A, o=A, Wuv=0, Wg=A, Wo=A, y=A, ws=A, wsb=1 << 40, T=4, D=256, H=2, d_c=0, d_v=64, dt=1)
+    a.update(kw)
+    return L.gmla_gate_out(a["x"], a["o"], a["Wuv"], a["Wg"], a["Wo"], a["y"], a["ws"], a["wsb"], a["T"], a["D"],
+                           a["H"], a["d_c"], a["d_v"], a["dt"], None)
+
+
+def test_gate_out_argument_checks(L):
+    assert _gate(L, Wg=0) == INVALID
+    assert _gate(L, T=0) == INVALID
+    assert _gate(L, Wuv=A, d_c=0) == INVALID
+    assert _gate(L, D=200) == UNSUPPORTED
+    assert _gate(L, Wuv=A, d_c=100) == UNSUPPORTED
+    assert _gate(L, wsb=10) == WORKSPACE
+    assert L.gmla_gate_out_workspace_size(4, 2, 64, 1, 1) == 2 * 256 * ((4 * 2 * 64 * 2 + 255) // 256)
+
+
+def test_trace_api_without_launches(L):
+    assert L.gmla_trace_begin(0) == INVALID
+    n, ms = C.c_int(5), C.c_double(1.0)
+    assert L.gmla_trace_summary(b"decode_attn", C.byref(n), C.byref(ms)) == OK
+    assert n.value == 0 and ms.value == 0.0
+    L.gmla_trace_reset()

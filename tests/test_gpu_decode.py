@@ -1,0 +1,133 @@
+"""GPU parity of gmla_decode (through the C ABI) against the fp64 oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gated_mla_latent_amd import ops
+from gated_mla_latent_amd import workloads as W
+from tests.gpu_util import BF16_TOL, F32_TOL, dev, f64, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(inp, num_splits=0):
+    o, lse = ops.decode(dev(inp.q_abs), dev(inp.cache), dev(inp.seq_start), dev(inp.seq_len), inp.d_c, inp.d_r,
+                        inp.rope_base, inp.sm_scale, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _oracle(inp, batches=None):
+    return O.decode_reference(inp.q_abs.float().numpy(), inp.cache.float().numpy(), inp.seq_start.numpy(),
+                              inp.seq_len.numpy(), inp.d_c, inp.d_r, inp.rope_base, inp.sm_scale, batches=batches)
+
+
+def _check(inp, o, lse, tol=BF16_TOL, batches=None):
+    ro, rl = _oracle(inp, batches)
+    bs = list(range(inp.B)) if batches is None else list(batches)
+    e_o = rel_err(o[bs].float(), ro[bs])
+    e_l = float(np.abs(f64(lse)[bs] - rl[bs]).max())
+    say(f"  {inp.name or 'decode'} B={inp.B} H={inp.H} d_c={inp.d_c} d_r={inp.d_r}: o rel err {e_o:.2e}, lse abs err {e_l:.2e}")
+    assert e_o <= tol
+    assert e_l <= 2e-2  # natural-log units; scores are accumulated in fp32 from bf16 operands
+    return e_o
+
+
+# ragged lengths covering 1, tile-1, tile, tile+1 and several tiles
+RAGGED = [1, 31, 32, 33, 63, 64, 65, 200, 257, 600]
+
+
+@pytest.mark.parametrize("H,d_c,d_r", [(64, 512, 0), (128, 512, 64), (128, 512, 0), (64, 512, 64),
+                                       (16, 512, 0), (96, 512, 64), (200, 512, 64)])
+def test_decode_ragged_matches_oracle(H, d_c, d_r):
+    say(f"[decode ragged] H={H} d_c={d_c} d_r={d_r}")
+    inp = W.make_decode(len(RAGGED), H, d_c, d_r, 0, lengths=RAGGED, seed=11, name="ragged")
+    o, lse = _run(inp)
+    _check(inp, o, lse)
+
+
+@pytest.mark.skip(reason="the bf16 decode kernel for d_c = 256 faulted on the GPU (cause not found); "
+                         "the d_c in {128, 256} paths are switched off and return GMLA_ERR_UNSUPPORTED")
+@pytest.mark.parametrize("d_c,d_r", [(256, 0), (256, 64), (128, 0)])
+def test_decode_narrow_latent_widths(d_c, d_r):
+    inp = W.make_decode(len(RAGGED), 64, d_c, d_r, 0, lengths=RAGGED, seed=11, name="narrow")
+    o, lse = _run(inp)
+    _check(inp, o, lse)
+
+
+def test_decode_narrow_latent_widths_are_rejected():
+    inp = W.make_decode(2, 64, 256, 0, 5, 9, seed=1)
+    with pytest.raises(ops.GmlaError) as e:
+        _run(inp)
+    assert e.value.status == 2
+
+
+@pytest.mark.parametrize("num_splits", [1, 2, 7, 64, 0])
+def test_decode_split_invariance(num_splits):
+    say(f"[decode splits] num_splits={num_splits}")
+    inp = W.make_decode(6, 128, 512, 64, 1, 700, seed=3, name="splits")
+    o, lse = _run(inp, num_splits)
+    _check(inp, o, lse)
+    o1, l1 = _run(inp, 1)
+    # the same answer up to fp32 rounding of the partial merge and bf16 output rounding
+    assert rel_err(o.float(), f64(o1)) <= 8e-3
+    assert float((lse - l1).abs().max()) <= 1e-4
+
+
+def test_decode_honours_seq_start_with_gaps():
+    say("[decode gaps]")
+    inp = W.make_decode(5, 64, 512, 64, 10, 300, seed=5, gap_rows=13, name="gaps")
+    o, lse = _run(inp, 3)
+    _check(inp, o, lse)
+
+
+def test_decode_empty_sequence_gives_zero_and_minus_inf():
+    say("[decode empty]")
+    inp = W.make_decode(3, 64, 512, 0, 0, lengths=[40, 0, 70], seed=2, name="empty")
+    o, lse = _run(inp)
+    assert torch.all(o[1] == 0)
+    assert torch.all(torch.isneginf(lse[1]))
+    _check(inp, o, lse, batches=[0, 2])
+
+
+def test_decode_long_rope_positions():
+    """One long sequence: RoPE angles at position ~1e5 and a many-slice split."""
+    say("[decode long]")
+    inp = W.make_decode(2, 128, 512, 64, 0, lengths=[100_003, 5], seed=7, name="long")
+    o, lse = _run(inp)
+    _check(inp, o, lse)
+
+
+def test_decode_score_range_forces_redo_pass():
+    """Scores that grow by far more than the kernel's first-tile reference
+    (keys scaled up after token 64) exercise the exact redo path."""
+    say("[decode redo]")
+    inp = W.make_decode(2, 64, 512, 0, 0, lengths=[300, 129], seed=9, name="redo")
+    c = inp.cache.float()
+    s0 = int(inp.seq_start[0])
+    c[s0 + 64:s0 + 300] *= 12.0
+    inp.cache = c.to(torch.bfloat16)
+    o, lse = _run(inp, 1)
+    _check(inp, o, lse)
+
+
+def test_decode_fp32_path():
+    say("[decode fp32]")
+    inp = W.make_decode(4, 8, 64, 16, 1, 90, dtype=torch.float32, seed=4, name="f32")
+    o, lse = _run(inp)
+    _check(inp, o, lse, tol=F32_TOL)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("cfg", ["config2", "config3", "config5"])
+def test_decode_full_size_configs(cfg):
+    """Full workload sizes in the launch configuration the benchmark times
+    (num_splits = 0); the oracle checks a sample of sequences."""
+    say(f"[decode full] {cfg}")
+    inp = getattr(W, cfg)(with_output_side=False)
+    o, lse = _run(inp)
+    sample = {"config2": [0, 7, 31], "config3": [0, 33, 63], "config5": [0, 5]}[cfg]
+    _check(inp, o, lse, batches=sample)

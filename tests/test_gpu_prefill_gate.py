@@ -1,0 +1,139 @@
+"""GPU parity of gmla_prefill and gmla_gate_out (through the C ABI) against
+the fp64 oracle, plus the prefill/decode consistency of the HIP path."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gated_mla_latent_amd import ops
+from gated_mla_latent_amd import workloads as W
+from tests.gpu_util import BF16_TOL, F32_TOL, dev, f64, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _prefill(inp):
+    c, ot = ops.prefill(dev(inp.x), dev(inp.W_c), dev(inp.W_q), dev(inp.W_uk), dev(inp.W_uv), inp.sm_scale)
+    B, L, D = inp.x.shape
+    y = ops.gate_out(dev(inp.x).reshape(B * L, D), ot.reshape(B * L, -1), dev(inp.W_g), dev(inp.W_o))
+    torch.cuda.synchronize()
+    return c, ot, y.reshape(B, L, D)
+
+
+def _np(t):
+    return t.float().numpy()
+
+
+@pytest.mark.parametrize("B,L,D,H,d_c,d", [(2, 300, 256, 4, 128, 128), (1, 517, 512, 3, 64, 64),
+                                           (1, 64, 128, 2, 64, 128), (3, 33, 256, 5, 128, 64)])
+def test_prefill_bf16_matches_oracle(B, L, D, H, d_c, d):
+    say(f"[prefill bf16] B={B} L={L} D={D} H={H} d_c={d_c} d={d}")
+    inp = W.make_prefill(B, L, D, H, d_c, d, d, seed=21)
+    c, ot, y = _prefill(inp)
+    rc, rot, ry = O.gated_mla_layer(_np(inp.x), _np(inp.W_c), _np(inp.W_q), _np(inp.W_uk), _np(inp.W_uv),
+                                    _np(inp.W_g), _np(inp.W_o), inp.sm_scale)
+    e = (rel_err(c.float(), rc), rel_err(ot.float(), rot), rel_err(y.float(), ry))
+    say(f"  rel err c {e[0]:.2e}  o~ {e[1]:.2e}  y {e[2]:.2e}")
+    assert max(e) <= BF16_TOL
+
+
+def test_prefill_fp32_tiny_config():
+    """The tiny fp32 workload at its full size (B=1, L=128, d_model=256, H=4,
+    d_c=64, d_k=d_v=32), against the whole-layer oracle at 1e-4."""
+    say("[prefill fp32 tiny config]")
+    inp = W.config1()
+    c, ot, y = _prefill(inp)
+    rc, rot, ry = O.gated_mla_layer(_np(inp.x), _np(inp.W_c), _np(inp.W_q), _np(inp.W_uk), _np(inp.W_uv),
+                                    _np(inp.W_g), _np(inp.W_o), inp.sm_scale)
+    e = (rel_err(c, rc), rel_err(ot, rot), rel_err(y, ry))
+    say(f"  rel err c {e[0]:.2e}  o~ {e[1]:.2e}  y {e[2]:.2e}")
+    assert max(e) <= F32_TOL
+
+
+@pytest.mark.parametrize("T,D,H,d_c,d_v", [(32, 1024, 64, 512, 128), (64, 512, 16, 256, 64), (8, 256, 8, 128, 32),
+                                           (5, 512, 4, 64, 128), (100, 512, 4, 128, 64)])
+def test_gate_out_with_value_up_projection(T, D, H, d_c, d_v):
+    say(f"[gate_out decode-side] T={T} D={D} H={H} d_c={d_c} d_v={d_v}")
+    g = torch.Generator().manual_seed(5)
+    o_lat = torch.randn(T, H, d_c, generator=g).to(torch.bfloat16)
+    x = torch.randn(T, D, generator=g).to(torch.bfloat16)
+    W_uv = (torch.randn(H, d_v, d_c, generator=g) / d_c ** 0.5).to(torch.bfloat16)
+    W_g = (torch.randn(H * d_v, D, generator=g) / D ** 0.5).to(torch.bfloat16)
+    W_o = (torch.randn(D, H * d_v, generator=g) / (H * d_v) ** 0.5).to(torch.bfloat16)
+    y = ops.gate_out(dev(x), dev(o_lat), dev(W_g), dev(W_o), W_uv=dev(W_uv))
+    torch.cuda.synchronize()
+    ot = O.value_up_projection(_np(o_lat), _np(W_uv))
+    ry = O.gate_out_reference(_np(x), ot, _np(W_g), _np(W_o))
+    e = rel_err(y.float(), ry)
+    say(f"  rel err y {e:.2e}")
+    assert e <= BF16_TOL
+
+
+def test_gate_out_fp32_with_value_up_projection():
+    say("[gate_out fp32]")
+    g = torch.Generator().manual_seed(6)
+    T, D, H, d_c, d_v = 7, 96, 3, 40, 24
+    o_lat, x = torch.randn(T, H, d_c, generator=g), torch.randn(T, D, generator=g)
+    W_uv, W_g, W_o = torch.randn(H, d_v, d_c, generator=g), torch.randn(H * d_v, D, generator=g), torch.randn(D, H * d_v, generator=g)
+    y = ops.gate_out(dev(x), dev(o_lat), dev(W_g), dev(W_o), W_uv=dev(W_uv))
+    torch.cuda.synchronize()
+    ry = O.gate_out_reference(x.double().numpy(), O.value_up_projection(o_lat.numpy(), W_uv.numpy()),
+                              W_g.numpy(), W_o.numpy())
+    assert rel_err(y, ry) <= F32_TOL
+
+
+def test_prefill_last_row_equals_decode_on_its_latent():
+    """HIP prefill's last position and a HIP decode step over the latent that
+    prefill wrote agree once the query is absorbed on the host."""
+    say("[prefill vs decode]")
+    B, L, D, H, d_c, d = 2, 130, 256, 64, 512, 128
+    inp = W.make_prefill(B, L, D, H, d_c, d, d, seed=8)
+    c, ot, _ = _prefill(inp)
+    q = (inp.x[:, -1].double() @ inp.W_q.double().T).reshape(B, H, d)
+    q_abs = torch.einsum("bhk,hkc->bhc", q, inp.W_uk.double()).to(torch.bfloat16).contiguous()
+    seq_start = torch.arange(B, dtype=torch.int64) * L
+    seq_len = torch.full((B,), L, dtype=torch.int32)
+    o_lat, lse = ops.decode(dev(q_abs), c.reshape(B * L, d_c), dev(seq_start), dev(seq_len), d_c, 0, 0.0,
+                            inp.sm_scale)
+    torch.cuda.synchronize()
+    o_dec = O.value_up_projection(f64(o_lat), _np(inp.W_uv))
+    e = rel_err(ot[:, -1].float(), o_dec)
+    say(f"  rel diff {e:.2e}")
+    assert e <= 2e-2
+
+
+@pytest.mark.slow
+def test_prefill_full_size_sampled_rows():
+    """The B=2, L=8192, d_model=7168, H=64 prefill at full size, as the
+    benchmark launches it; the oracle checks the latent in full and o~, y on
+    a seeded sample of query rows (first, second, third, last, 12 random)."""
+    say("[prefill full] generating")
+    inp = W.config4()
+    c, ot, y = _prefill(inp)
+    rng = np.random.default_rng(0)
+    rows = sorted(set([0, 1, 2, inp.L - 1] + rng.choice(inp.L, 12, replace=False).tolist()))
+    say(f"  oracle on rows {rows}")
+    rc, rot, _ = O.prefill_reference(_np(inp.x), _np(inp.W_c), _np(inp.W_q), _np(inp.W_uk), _np(inp.W_uv),
+                                     inp.sm_scale, rows=rows)
+    xr = _np(inp.x)[:, rows].reshape(-1, inp.d_model)
+    ry = O.gate_out_reference(xr, rot.reshape(xr.shape[0], -1), _np(inp.W_g), _np(inp.W_o))
+    e = (rel_err(c.float(), rc), rel_err(ot[:, rows].float(), rot),
+         rel_err(y[:, rows].float().reshape(xr.shape[0], -1), ry))
+    say(f"  rel err c {e[0]:.2e}  o~ {e[1]:.2e}  y {e[2]:.2e}")
+    assert max(e) <= BF16_TOL
+
+
+@pytest.mark.slow
+def test_decode_output_side_full_size():
+    """gate_out on the decode workload's output side at full size (T = 32,
+    d_model = 7168, H = 64, d_c = 512, d_v = 128)."""
+    say("[gate_out full decode-side]")
+    inp = W.config2()
+    g = torch.Generator().manual_seed(1)
+    o_lat = torch.randn(inp.B, inp.H, inp.d_c, generator=g).to(torch.bfloat16)
+    y = ops.gate_out(dev(inp.x), dev(o_lat), dev(inp.W_g), dev(inp.W_o), W_uv=dev(inp.W_uv))
+    torch.cuda.synchronize()
+    ry = O.gate_out_reference(_np(inp.x), O.value_up_projection(_np(o_lat), _np(inp.W_uv)), _np(inp.W_g), _np(inp.W_o))
+    e = rel_err(y.float(), ry)
+    say(f"  rel err y {e:.2e}")
+    assert e <= BF16_TOL
