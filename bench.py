@@ -1,0 +1,371 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gated-MLA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload decode_nope]
+
+A step is one pass of the hot path over one batch of synthetic input:
+  decode_*  : gmla_decode (attention over the latent cache + split combine)
+              followed by gmla_gate_out (value up-projection, sigmoid gate,
+              W_o) for the B query tokens;
+  prefill   : gmla_prefill (latent, query, K/V reconstruction, causal
+              attention) followed by gmla_gate_out over all B*L tokens;
+  tiny_fp32 : the same as prefill for the tiny fp32 workload.
+Inputs are resident in HBM before timing starts; several copies of every
+input that is read in the step rotate so that the 256 MB Infinity Cache
+cannot serve a step from the previous one. The library is called through
+its C ABI (argument tuples marshalled once). Per-kernel device times come
+from the library's event trace, recorded on the launch stream around every
+kernel during the timed steps.
+
+Prints one JSON line (rank 0). The fp64 CPU oracle is timed on a bounded
+sample of the same workload on the host cores (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tokens/s + HBM GB/s (or MFMA %) of roofline; prefill TFLOP/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+F32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector, published
+
+WORKLOADS = {
+    "decode_nope": ("config2", "decode NoPE, B=32, H=64, d_c=512, L_b~U[1024,8192], bf16 + gate/W_o (d_model 7168, d_v 128)"),
+    "decode_rope": ("config3", "decode RoPE, B=64, H=128, d_c=512+d_r=64, L_b~U[1024,16384], bf16 + gate/W_o (d_model 7168, d_v 128)"),
+    "decode_long": ("config5", "decode RoPE, B=8, H=128, d_c=512+64, L=131072 each, bf16 + gate/W_o (d_model 7168, d_v 128)"),
+    "prefill": ("config4", "causal prefill B=2, L=8192, d_model=7168, H=64, d_c=512, d_k=d_v=128, bf16 + gate/W_o"),
+    "tiny_fp32": ("config1", "causal prefill B=1, L=128, d_model=256, H=4, d_c=64, d_k=d_v=32, fp32 + gate/W_o"),
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_nope", choices=sorted(WORKLOADS))
+    ap.add_argument("--copies", type=int, default=3, help="rotating input copies (cache-defeating)")
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-trace", action="store_true")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------- accounting
+def decode_bytes(inp):
+    W = inp.d_c + inp.d_r
+    tokens = int(inp.seq_len.clamp(min=0).sum())
+    cache = tokens * W * 2
+    q = inp.B * inp.H * W * 2
+    out = inp.B * inp.H * inp.d_c * 2 + inp.B * inp.H * 4
+    return {"cache": cache, "q": q, "out": out, "tokens": tokens}
+
+
+def decode_attn_flops(inp):
+    tokens = int(inp.seq_len.clamp(min=0).sum())
+    return tokens * inp.H * (2 * (inp.d_c + inp.d_r) + 2 * inp.d_c)
+
+
+def gate_out_bytes(inp):
+    T, D, H, dv, dc = inp.B, inp.d_model, inp.H, inp.d_v, inp.d_c
+    HV = H * dv
+    return {
+        "gemm_value_up": H * dv * dc * 2 + T * H * dc * 2 + T * HV * 2,
+        "gemm_gate": HV * D * 2 + T * D * 2 + 2 * T * HV * 2,
+        "gemm_out": D * HV * 2 + T * HV * 2 + T * D * 2,
+    }
+
+
+def gate_out_flops(inp):
+    T, D, H, dv, dc = inp.B, inp.d_model, inp.H, inp.d_v, inp.d_c
+    return {"gemm_value_up": 2 * T * H * dv * dc, "gemm_gate": 2 * T * D * H * dv, "gemm_out": 2 * T * D * H * dv}
+
+
+def prefill_flops(p):
+    T = p.B * p.L
+    pairs = p.B * p.L * (p.L + 1) // 2  # unmasked (t, s <= t) pairs per head
+    f = {
+        "gemm_latent": 2 * T * p.d_model * p.d_c,
+        "gemm_query": 2 * T * p.d_model * p.H * p.d_k,
+        "gemm_key_recon": 2 * T * p.d_c * p.H * p.d_k,
+        "gemm_value_recon": 2 * T * p.d_c * p.H * p.d_v,
+        "prefill_attn": 2 * pairs * p.H * (p.d_k + p.d_v),
+        "gemm_gate": 2 * T * p.d_model * p.H * p.d_v,
+        "gemm_out": 2 * T * p.H * p.d_v * p.d_model,
+    }
+    return f
+
+
+# ----------------------------------------------------------------------------- runners
+def _vp(t):
+    return C.c_void_p(t.data_ptr()) if t is not None else C.c_void_p(0)
+
+
+def build_decode(args, inp, torch, ops):
+    dev = "cuda"
+    L = ops.lib()
+    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    q = inp.q_abs.to(dev)
+    seq_start, seq_len = inp.seq_start.to(dev), inp.seq_len.to(dev)
+    x = inp.x.to(dev)
+    copies = []
+    for i in range(args.copies):
+        copies.append(dict(cache=inp.cache.to(dev), W_uv=inp.W_uv.to(dev), W_g=inp.W_g.to(dev), W_o=inp.W_o.to(dev)))
+        log(f"  copy {i} resident")
+    o_lat = torch.empty((inp.B, inp.H, inp.d_c), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((inp.B, inp.H), dtype=torch.float32, device=dev)
+    y = torch.empty((inp.B, inp.d_model), dtype=torch.bfloat16, device=dev)
+    wsd_n = L.gmla_decode_workspace_size(inp.B, inp.H, inp.d_c, args.num_splits, 1)
+    wsg_n = L.gmla_gate_out_workspace_size(inp.B, inp.H, inp.d_v, 1, 1)
+    wsd = torch.empty(wsd_n, dtype=torch.uint8, device=dev)
+    wsg = torch.empty(wsg_n, dtype=torch.uint8, device=dev)
+    calls = []
+    for c in copies:
+        dec = (_vp(q), _vp(c["cache"]), _vp(seq_start), _vp(seq_len), _vp(o_lat), _vp(lse), _vp(wsd), C.c_size_t(wsd_n),
+               inp.B, inp.H, inp.d_c, inp.d_r, C.c_float(inp.rope_base), C.c_float(inp.sm_scale), args.num_splits, 1,
+               stream)
+        go = (_vp(x), _vp(o_lat), _vp(c["W_uv"]), _vp(c["W_g"]), _vp(c["W_o"]), _vp(y), _vp(wsg), C.c_size_t(wsg_n),
+              inp.B, inp.d_model, inp.H, inp.d_c, inp.d_v, 1, stream)
+        calls.append((dec, go))
+    keep = (q, seq_start, seq_len, x, copies, o_lat, lse, y, wsd, wsg)
+
+    def step(i):
+        dec, go = calls[i % len(calls)]
+        s = L.gmla_decode(*dec)
+        if s:
+            raise RuntimeError(L.gmla_last_error().decode())
+        s = L.gmla_gate_out(*go)
+        if s:
+            raise RuntimeError(L.gmla_last_error().decode())
+
+    return step, keep
+
+
+def build_prefill(args, p, torch, ops):
+    dev = "cuda"
+    L = ops.lib()
+    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    dt = 1 if p.dtype == torch.bfloat16 else 0
+    T = p.B * p.L
+    copies = []
+    for i in range(args.copies):
+        copies.append({k: getattr(p, k).to(dev) for k in ("x", "W_c", "W_q", "W_uk", "W_uv", "W_g", "W_o")})
+        log(f"  copy {i} resident")
+    lat = torch.empty((p.B, p.L, p.d_c), dtype=p.dtype, device=dev)
+    ot = torch.empty((p.B, p.L, p.H * p.d_v), dtype=p.dtype, device=dev)
+    y = torch.empty((T, p.d_model), dtype=p.dtype, device=dev)
+    wsp_n = L.gmla_prefill_workspace_size(p.B, p.L, p.H, p.d_k, p.d_v, dt)
+    wsg_n = L.gmla_gate_out_workspace_size(T, 1, p.H * p.d_v, 0, dt)
+    wsp = torch.empty(wsp_n, dtype=torch.uint8, device=dev)
+    wsg = torch.empty(wsg_n, dtype=torch.uint8, device=dev)
+    calls = []
+    for c in copies:
+        pre = (_vp(c["x"]), _vp(c["W_c"]), _vp(c["W_q"]), _vp(c["W_uk"]), _vp(c["W_uv"]), _vp(lat), _vp(ot), _vp(wsp),
+               C.c_size_t(wsp_n), p.B, p.L, p.d_model, p.H, p.d_c, p.d_k, p.d_v, C.c_float(p.sm_scale), dt, stream)
+        go = (_vp(c["x"]), _vp(ot), C.c_void_p(0), _vp(c["W_g"]), _vp(c["W_o"]), _vp(y), _vp(wsg), C.c_size_t(wsg_n),
+              T, p.d_model, 1, 0, p.H * p.d_v, dt, stream)
+        calls.append((pre, go))
+    keep = (copies, lat, ot, y, wsp, wsg)
+
+    def step(i):
+        pre, go = calls[i % len(calls)]
+        s = L.gmla_prefill(*pre)
+        if s:
+            raise RuntimeError(L.gmla_last_error().decode())
+        s = L.gmla_gate_out(*go)
+        if s:
+            raise RuntimeError(L.gmla_last_error().decode())
+
+    return step, keep
+
+
+# ----------------------------------------------------------------------------- cpu baseline
+def cpu_baseline_decode(inp, budget_s):
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    q = inp.q_abs.float().numpy()
+    cache = inp.cache  # bf16 torch; rows are upcast per sequence inside the oracle
+    # time one sequence, then size the sample to the budget
+    order = list(range(inp.B))
+    done, tokens, t0 = [], 0, time.perf_counter()
+    for b in order:
+        s0, Lb = int(inp.seq_start[b]), int(inp.seq_len[b])
+        rows = cache[s0:s0 + Lb].float().numpy()
+        O.decode_reference(q[b:b + 1], rows, np.array([0]), np.array([Lb]), inp.d_c, inp.d_r, inp.rope_base,
+                           inp.sm_scale)
+        done.append(b)
+        tokens += Lb
+        if time.perf_counter() - t0 > budget_s:
+            break
+    t_dec = time.perf_counter() - t0
+    # output side for the sampled query tokens
+    t1 = time.perf_counter()
+    o_lat = np.random.default_rng(0).standard_normal((len(done), inp.H, inp.d_c))
+    ot = O.value_up_projection(o_lat, inp.W_uv.float().numpy())
+    O.gate_out_reference(inp.x[done].float().numpy(), ot, inp.W_g.float().numpy(), inp.W_o.float().numpy())
+    t_go = time.perf_counter() - t1
+    secs = t_dec + t_go
+    return {"value": len(done) / secs, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 oracle: decode of {len(done)} of {inp.B} sequences ({tokens} cached tokens) plus "
+                      f"gate/W_o for those {len(done)} query tokens; {secs:.1f} s on the host"}
+
+
+def cpu_baseline_prefill(p, budget_s):
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    # sample: the first Ls positions of sequence 0; Ls doubles until the
+    # oracle run takes about a third of the budget (or covers the sequence)
+    Ls = min(p.L, 64)
+    W = [getattr(p, k).float().numpy() for k in ("W_c", "W_q", "W_uk", "W_uv", "W_g", "W_o")]
+    while True:
+        x = p.x[:1, :Ls].float().numpy()
+        t0 = time.perf_counter()
+        O.gated_mla_layer(x, *W, p.sm_scale)
+        secs = time.perf_counter() - t0
+        if secs >= budget_s / 3 or Ls >= p.L:
+            break
+        Ls = min(p.L, Ls * 2)
+    fl = prefill_flops(p.__class__(**{**p.__dict__, "B": 1, "L": Ls}))
+    return {"value": sum(fl.values()) / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 oracle: whole layer on the first {Ls} positions of one sequence "
+                      f"({sum(fl.values()) / 1e9:.1f} GFLOP); {secs:.1f} s on the host"}
+
+
+# ----------------------------------------------------------------------------- main
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU layout is described in the design notes, not benchmarked.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np  # noqa: F401
+    import torch
+    from gated_mla_latent_amd import ops, workloads as W
+    from gated_mla_latent_amd.build import LIB_PATH, build
+    if not os.path.exists(LIB_PATH):
+        build()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    cfg_name, desc = WORKLOADS[args.workload]
+    log(f"[bench] generating {args.workload} ({desc})")
+    gen = getattr(W, cfg_name)
+    inp = gen()
+    is_decode = args.workload.startswith("decode")
+    step, keep = (build_decode if is_decode else build_prefill)(args, inp, torch, ops)
+
+    log(f"[bench] warmup {args.warmup}")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    trace = not args.no_trace
+    if trace:
+        ops.trace_reset()
+        ops.trace_begin(16 * args.steps + 64)
+    log(f"[bench] timing {args.steps} steps")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if trace:
+        ops.trace_end()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"[bench] {ms_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us/step)")
+
+    kern = {}
+    if trace:
+        for k in ops.trace_kernels():
+            n, ms = ops.trace_summary(k)
+            kern[k] = {"launches_per_step": n / args.steps, "avg_us": ms * 1e3}
+        ops.trace_reset()
+
+    out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f32" if args.workload == "tiny_fp32" else "bf16",
+           "data": "synthetic (seeded; random-init weights of the stated shapes)"}
+    if is_decode:
+        db = decode_bytes(inp)
+        gb = gate_out_bytes(inp)
+        gf = gate_out_flops(inp)
+        alg = {"decode_attn": db["cache"] + db["q"] + db["out"], **gb}
+        flops = {"decode_attn": decode_attn_flops(inp), **gf}
+        step_bytes = sum(alg.values())
+        value = inp.B / (ms_step * 1e-3)
+        out.update({"value": value, "unit": "tokens/s",
+                    "config": {"workload": desc, "batch": inp.B, "heads": inp.H, "d_c": inp.d_c, "d_r": inp.d_r,
+                               "cached_tokens": db["tokens"], "num_splits": args.num_splits or "auto",
+                               "input_copies": args.copies},
+                    "step_hbm_gbs": step_bytes / (ms_step * 1e-3) / 1e9,
+                    "step_hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        # dominant kernel: largest device time per step
+        if kern:
+            dom = max(kern, key=lambda k: kern[k]["avg_us"] * kern[k]["launches_per_step"])
+            for k, v in kern.items():
+                if k in alg:
+                    v["alg_bytes"] = alg[k]
+                    v["gbs"] = alg[k] / (v["avg_us"] * 1e-6) / 1e9
+                    v["tflops"] = flops[k] / (v["avg_us"] * 1e-6) / 1e12
+            if dom in alg:
+                a = alg[dom] / (kern[dom]["avg_us"] * 1e-6) / 1e9
+                out["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": a / HBM_PEAK_GBS, "traffic": None,
+                                   "alg_bytes_per_launch": alg[dom]}
+        out["kernels"] = kern
+        if not args.no_cpu_baseline:
+            log("[bench] cpu baseline (fp64 oracle)")
+            out["cpu_baseline"] = cpu_baseline_decode(inp, args.cpu_seconds)
+    else:
+        fl = prefill_flops(inp)
+        total = sum(fl.values())
+        out.update({"value": total / (ms_step * 1e-3) / 1e12, "unit": "TFLOP/s",
+                    "config": {"workload": desc, "batch": inp.B, "seq_len": inp.L, "heads": inp.H,
+                               "gflop_per_step": total / 1e9, "input_copies": args.copies}})
+        if kern:
+            peak = F32_VALU_PEAK_TFLOPS if inp.dtype == torch.float32 else BF16_PEAK_TFLOPS
+            for k, v in kern.items():
+                if k in fl:
+                    v["tflops"] = fl[k] / (v["avg_us"] * 1e-6) / 1e12
+            cand = {k: v for k, v in kern.items() if k in fl}
+            if cand:
+                dom = max(cand, key=lambda k: cand[k]["avg_us"] * cand[k]["launches_per_step"])
+                a = fl[dom] / (kern[dom]["avg_us"] * 1e-6) / 1e12
+                out["roofline"] = {"bound": "alu" if inp.dtype == torch.float32 else "mfma", "kernel": dom,
+                                   "achieved": a, "peak": peak, "unit": "TFLOP/s", "frac": a / peak, "traffic": None,
+                                   "alg_flops_per_launch": fl[dom]}
+        out["kernels"] = kern
+        if not args.no_cpu_baseline:
+            log("[bench] cpu baseline (fp64 oracle)")
+            out["cpu_baseline"] = cpu_baseline_prefill(inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

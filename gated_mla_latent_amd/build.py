@@ -18,6 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgmla.so")
+LIB_PATH = LIB
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
