@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -269,6 +271,16 @@ def main():
     if not os.path.exists(LIB_PATH):
         build()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+        return
 
     cfg_name, desc = WORKLOADS[args.workload]
     log(f"[bench] generating {args.workload} ({desc})")

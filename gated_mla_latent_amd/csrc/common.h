@@ -91,6 +91,22 @@ __device__ __forceinline__ void g2lds16(const void* gptr, const LDS_AS void* lds
       : "memory", "m0");
 }
 
+// Same, with a 64-bit scalar base address plus a 32-bit per-lane byte offset
+// (global_load_lds ... v_offset, s[base]): the base and the LDS destination
+// are scalar, so a whole 1 KiB row costs no 64-bit vector address arithmetic.
+// Five wait states precede the load: the scalar base may come straight from
+// v_readfirstlane (a VALU write of an SGPR that a VMEM instruction then reads),
+// a hazard the compiler cannot see inside asm; they also cover the M0 write.
+__device__ __forceinline__ void g2lds16_s(unsigned long long sbase, unsigned voff, unsigned lds_wave_base) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 4\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(sbase), "s"(lds_wave_base)
+      : "memory", "m0");
+}
+
 // Workgroup barrier without the memory fence __syncthreads() implies (that
 // fence waits for every outstanding global load, including in-flight DMA).
 // LDS reads before the barrier complete first (lgkmcnt(0)).

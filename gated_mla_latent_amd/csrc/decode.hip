@@ -11,21 +11,24 @@
 //  * The flattened token space of all sequences is cut into G equal slices,
 //    one per workgroup, so ragged lengths cost nothing in balance. A slice
 //    may hold pieces of several sequences; a sequence cut across slices
-//    yields fp32 partial (o, lse) pieces that gmla_decode_combine merges.
-//  * A workgroup (4 waves) handles all heads: wave w owns 32 heads (head
-//    group w % HG) and a 32-token sub-tile (token group w / HG). Latent tiles
-//    stream HBM -> LDS with 16-byte direct-to-LDS loads into an NBUF ring,
-//    XOR-swizzled so both LDS read patterns below are conflict-light.
-//  * S^T = C . Q^T on v_mfma_f32_32x32x16_bf16 (A = 16-byte LDS reads of the
-//    row-major tile, B = the wave's queries held in VGPRs). Each lane then
-//    owns one head and 16 tokens, so the online-softmax max needs a single
-//    cross-lane exchange (lane ^ 32).
+//    yields fp32 partial (o, lse) pieces that the combine kernel merges.
+//  * A workgroup handles all heads of its slice: wave w owns 16 heads. Every
+//    wave reads every latent tile from LDS, so HBM bytes are read once while
+//    LDS serves H/16 readers (gfx950 LDS sustains ~200 B/clk/CU).
+//  * Latent tiles of 32 tokens stream HBM -> LDS through a ring of four slots
+//    with 1 KiB direct-to-LDS loads (one per cache row; the row base is
+//    scalar), three slots in flight ahead of the one being read.
+//  * S^T = C . Q^T on v_mfma_f32_16x16x32_bf16 (A = 16-byte LDS reads, B =
+//    the wave's queries held in VGPRs): each lane owns one head and 8 tokens.
 //  * O^T += C^T . P^T on the same MFMA: P^T comes straight from the S^T
-//    accumulator layout; C^T fragments come from ds_read_b64_tr_b16
-//    (transposing LDS reads), using the token order the S^T layout implies.
+//    accumulators; C^T fragments come from ds_read_b64_tr_b16 (transposing
+//    LDS reads). O^T (16 heads x 512 features) lives in AGPRs.
+//  * LDS reads run two k-steps ahead of their MFMA, an order scheduling
+//    barriers keep; the compiler places O in AGPRs and inserts the MFMA
+//    hazard wait states (inline-asm MFMAs would hide those hazards from it).
 //  * No rescale of O inside the loop: the reference max is fixed at a head's
 //    first tile; a segment whose scores outgrow it by more than 2^32 is redone
-//    once with its true max (exact for any input, and O stays in AGPRs).
+//    once with its true max (exact for any input, and O never meets VALU).
 #include "common.h"
 #include "kernels.h"
 
@@ -35,129 +38,117 @@ namespace {
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRedo = 32.0f;  // log2 headroom before a segment is redone
+constexpr int kPF = 8;          // LDS operand fragments in flight ahead of the MFMA
 
-// LDS tile layout. The latent part of a token row (d_c bf16, >= 16 chunks of
-// 16 bytes) is stored with its chunks XOR-permuted by
-//     swl(t) = 4 (t & 3) + ((t >> 2) & 3)
-// which keeps both read patterns conflict-free on 64 four-byte banks:
-//   * S^T operand reads (ds_read_b128): 16 lanes read 16 consecutive rows at
-//     one chunk -> 16 distinct 16-byte bank groups;
-//   * P.V operand reads (ds_read_b64_tr_b16): 32 lanes read 4 consecutive rows
-//     (aligned to 4) x 4 consecutive chunks -> 4 distinct 64-byte quarters.
-// The RoPE part (d_r = 64 -> 8 chunks, 128-byte rows) sits in its own region
-// with swr(t) = (t >> 1) & 7: row parity already picks the 128-byte half.
-__device__ __forceinline__ int swl(int t) { return 4 * (t & 3) + ((t >> 2) & 3); }
+// LDS tile layout. A ring slot holds 32 cache rows.
+// Latent part (d_c = 512 bf16 = 1 KiB per row): row stride 1040 bytes (16
+// bytes of padding), token t stored in LDS row
+//     prow(t) = 16 (t >> 4) + 2 (t & 7) + ((t >> 3) & 1).
+// 1040 = 16 (mod 256), so a row's bank offset (64 four-byte banks) is
+// 16 prow(t) mod 256, which keeps both read patterns conflict-free:
+//   * S^T operand reads (ds_read_b128): 16 lanes read 16 consecutive tokens
+//     at one 16-byte chunk -> 16 distinct 16-byte bank groups;
+//   * P.V operand reads (ds_read_b64_tr_b16): 32 lanes read 8 tokens (two
+//     runs of 4) x 32 bytes -> 8 distinct 32-byte bank ranges.
+// Each latent row is one 1 KiB direct-to-LDS load, so the padding costs
+// nothing on the load side, and every k-step is a compile-time LDS offset.
+// The RoPE part (d_r = 64 -> 8 chunks, 128-byte rows, loaded eight rows per
+// instruction) follows the 32 latent rows with its chunks XOR-permuted by
+// swr(t) = (t >> 1) & 7 (row parity already picks the 128-byte half).
+constexpr int kLatStride = 1040;
+__device__ __forceinline__ int prow(int t) { return 16 * (t >> 4) + 2 * (t & 7) + ((t >> 3) & 1); }
 __device__ __forceinline__ int swr(int t) { return (t >> 1) & 7; }
 
-template <int D_C, int D_R, int HG, int NBUF>
+template <int D_R, int HG, int R>
 struct DecodeCfg {
-  static constexpr int DC = D_C;
+  static constexpr int D_C = 512;
   static constexpr int RW = D_C + D_R;        // cache row width (elements)
-  static constexpr int CHL = D_C / 8;         // latent chunks per row
-  static constexpr int CHR = D_R / 8;         // RoPE chunks per row
-  static constexpr int TG = 4 / HG;           // token groups
-  static constexpr int TILE = 32 * TG;        // tokens per iteration
-  static constexpr int LAT_BYTES = TILE * D_C * 2;
-  static constexpr int ROPE_BYTES = TILE * D_R * 2;
-  static constexpr int TILE_BYTES = LAT_BYTES + ROPE_BYTES;
-  static constexpr int ROUNDS_L = TILE * CHL / 256;   // latent load instructions per wave per tile
-  static constexpr int ROUNDS_R = TILE * CHR / 256;   // RoPE load instructions per wave per tile
-  static constexpr int ROUNDS = ROUNDS_L + ROUNDS_R;
-  static constexpr int KB = RW / 16;          // k-steps of S^T
-  static constexpr int KB_C = D_C / 16;       // k-steps on the latent part
-  static constexpr int FB = D_C / 32;         // feature blocks of O^T
-  static constexpr int RING_BYTES = NBUF * TILE_BYTES;
-  // token-group merge: (TG-1)*HG waves park O (FB*16 regs) plus m and l
-  static constexpr int MERGE_BYTES = (TG - 1) * HG * (FB * 16 + 2) * 64 * 4;
-  static constexpr int LDS_BYTES = RING_BYTES > MERGE_BYTES ? RING_BYTES : MERGE_BYTES;
-  static_assert(CHL >= 16 && CHL % 16 == 0, "latent rows of whole 256-byte groups");
-  static_assert(D_R == 0 || D_R == 64, "RoPE width 0 or 64");
-  static_assert(TILE * CHL % 256 == 0 && TILE * CHR % 256 == 0, "whole load rounds");
-  static_assert((NBUF - 2) * ROUNDS < 64, "vmcnt range");
+  static constexpr int RWB = RW * 2;          // cache row bytes
+  static constexpr int NW = HG;               // waves: one per 16 heads
+  static constexpr int LAT_BYTES = 32 * kLatStride;
+  static constexpr int SLOT_BYTES = LAT_BYTES + 32 * D_R * 2;
+  static constexpr int ROWS_L = 32 / NW;                        // latent rows per wave per slot
+  static constexpr int ROPE_ROWS = D_R ? 32 / NW : 0;           // RoPE rows per wave per slot
+  static constexpr int ROUNDS_R = D_R ? ROPE_ROWS / 8 : 0;       // 8 rows (64 lanes) per instruction
+  static constexpr int ROUNDS = ROWS_L + ROUNDS_R;              // DMA instructions per wave per slot
+  static constexpr int PD = R - 1;            // slots in flight ahead of the one being read
+  static constexpr int KB = RW / 32;          // k-steps of S^T (32 features each)
+  static constexpr int KB_C = D_C / 32;
+  static constexpr int FB = D_C / 16;         // 16-feature blocks of O^T
+  static constexpr int RING_BYTES = R * SLOT_BYTES;
+  static constexpr int LDS_BYTES = RING_BYTES;
+  static_assert(NW == 2 || NW == 4, "2 or 4 waves");
+  static_assert(D_R == 0 || D_R == 64, "RoPE rows are 8 chunks of 16 bytes");
+  static_assert(LDS_BYTES <= 163840, "LDS budget");
+  static_assert(64 * NW * 8 + 16 <= LDS_BYTES, "scan scratch fits in the ring");
+  static_assert((PD - 1) * ROUNDS < 64, "vmcnt range");
 };
 
-// Issue the direct-to-LDS loads of one tile: tokens [tok0, tok0+TILE) of the
-// sequence rows starting at cache row `base`. Rows at or past `nrows` are
-// clamped to the last valid row (their scores are masked later).
-template <class C>
-__device__ __forceinline__ void load_tile(const bf16* __restrict__ cache, int64_t base, int tok0, int nrows,
-                                          LDS_AS char* buf, int wave, int lane) {
-#pragma unroll
-  for (int k = 0; k < C::ROUNDS_L; ++k) {
-    const int p = k * 256 + wave * 64 + lane;     // latent chunk slot in the tile
-    const int t = p / C::CHL;
-    const int c = (p % C::CHL) ^ swl(t);          // logical chunk stored in this slot
-    int row = tok0 + t;
-    row = row < nrows ? row : nrows - 1;
-    g2lds16(cache + (base + row) * (int64_t)C::RW + c * 8, buf + (k * 256 + wave * 64) * 16);
-  }
-#pragma unroll
-  for (int k = 0; k < C::ROUNDS_R; ++k) {
-    const int p = k * 256 + wave * 64 + lane;     // RoPE chunk slot
-    const int t = p >> 3;
-    const int c = (p & 7) ^ swr(t);
-    int row = tok0 + t;
-    row = row < nrows ? row : nrows - 1;
-    g2lds16(cache + (base + row) * (int64_t)C::RW + C::DC + c * 8,
-            buf + C::LAT_BYTES + (k * 256 + wave * 64) * 16);
-  }
-}
-
-// Wait until at most `pending` whole tiles of this wave's loads are in flight.
-template <int ROUNDS, int NBUF>
-__device__ __forceinline__ void wait_tiles_in_flight(int pending) {
-  if constexpr (NBUF >= 4) {
+// vmcnt(pending * ROUNDS) for a small runtime `pending`
+template <int ROUNDS, int MAXP>
+__device__ __forceinline__ void wait_slots(int pending) {
+  if constexpr (MAXP >= 2) {
     if (pending >= 2) { wait_vmcnt<2 * ROUNDS>(); return; }
   }
-  if constexpr (NBUF >= 3) {
+  if constexpr (MAXP >= 1) {
     if (pending >= 1) { wait_vmcnt<ROUNDS>(); return; }
   }
   wait_vmcnt<0>();
 }
 
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane_id() ^ mask) << 2, __builtin_bit_cast(int, v)));
+}
+
 }  // namespace
 
-template <int D_C, int D_R, int HG, int NBUF>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+template <int D_R, int HG, int R>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * HG, 64 * HG), amdgpu_waves_per_eu(1, 1)))
 void decode_attn_kernel(DecodeArgs a) {
-  using C = DecodeCfg<D_C, D_R, HG, NBUF>;
+  using C = DecodeCfg<D_R, HG, R>;
+  constexpr int D_C = C::D_C;
+  constexpr int NT = 64 * C::NW;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
-  __shared__ long long s_scan[256];
-  __shared__ long long s_first[2];
+  const unsigned smem_base = (unsigned)(uintptr_t)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int hg = wave % HG;
-  const int tg = wave / HG;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hg = wave;
   const int G = a.G;
 
-  // XCD-aware slice order: the hardware deals workgroups to the 8 XCDs round
-  // robin, so give each XCD a contiguous run of slices (shared queries and
-  // sequences stay in one L2).
-  int g = blockIdx.x;
-  if (G % 8 == 0) g = (g % 8) * (G / 8) + g / 8;
-  const int head_base = blockIdx.y * (32 * HG);  // first head of this launch chunk
+  // Work item = (slice, head chunk of 16 HG heads). XCD-aware order: the
+  // hardware deals workgroups to the 8 XCDs round robin, so each XCD gets a
+  // contiguous run of items, and the head chunks of one slice run side by
+  // side on one XCD, where the second read of their cache rows hits its L2.
+  const int chunks = (int)gridDim.x / G;
+  int item = blockIdx.x;
+  if (gridDim.x % 8 == 0) item = (item % 8) * ((int)gridDim.x / 8) + item / 8;
+  const int g = item / chunks;
+  const int head_base = (item % chunks) * (16 * HG);  // first head of this chunk
 
-  // ---- prefix sums of the sequence lengths (cooperative, any B) ----
+  // ---- prefix sums of the sequence lengths (cooperative, any B); scratch in the ring ----
+  // thread i sums sequences i*cb .. i*cb + cb - 1, then an inclusive scan over NT threads
+  LDS_AS long long* s_scan = (LDS_AS long long*)smem;
+  LDS_AS long long* s_first = s_scan + NT;
   const int B = a.B;
-  const int cb = (B + 255) / 256;
+  const int cb = (B + NT - 1) / NT;
   long long mysum = 0;
   for (int i = 0; i < cb; ++i) {
-    int b = tid * cb + i;
-    if (b < B) { int L = a.seq_len[b]; mysum += L > 0 ? L : 0; }
+    int bb = tid * cb + i;
+    if (bb < B) { int L = a.seq_len[bb]; mysum += L > 0 ? L : 0; }
   }
   s_scan[tid] = mysum;
   __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
+  for (int off = 1; off < NT; off <<= 1) {
     long long v = tid >= off ? s_scan[tid - off] : 0;
     __syncthreads();
     s_scan[tid] += v;
     __syncthreads();
   }
-  const long long N = s_scan[255];
-  const long long excl = tid ? s_scan[tid - 1] : 0;
+  const long long N = s_scan[NT - 1];
+  const long long excl = tid > 0 ? s_scan[tid - 1] : 0;
   const long long start_g = (long long)g * N / G;
   const long long end_g = (long long)(g + 1) * N / G;
   if (tid == 0) { s_first[0] = -1; s_first[1] = 0; }
@@ -165,49 +156,49 @@ void decode_attn_kernel(DecodeArgs a) {
   {
     long long p = excl;
     for (int i = 0; i < cb; ++i) {
-      int b = tid * cb + i;
-      if (b >= B) break;
-      int L = a.seq_len[b];
+      int bb = tid * cb + i;
+      if (bb >= B) break;
+      int L = a.seq_len[bb];
       L = L > 0 ? L : 0;
-      if (blockIdx.x == 0 && blockIdx.y == 0) a.prefix[b] = p;
-      if (L > 0 && p <= start_g && start_g < p + L) { s_first[0] = b; s_first[1] = p; }
+      if (blockIdx.x == 0) a.prefix[bb] = p;
+      if (L > 0 && p <= start_g && start_g < p + L) { s_first[0] = bb; s_first[1] = p; }
       p += L;
     }
   }
   __syncthreads();
   int b = (int)s_first[0];
   long long P = s_first[1];
+  __syncthreads();  // the scan scratch becomes ring space
   if (b < 0 || start_g >= end_g) return;
 
   // ---- per-lane constants ----
   const float scale2 = a.scale_log2;
-  const int h_local = hg * 32 + (lane & 31);
-  const int h = head_base + h_local;
+  const int G4 = lane >> 4;                       // 16-lane group
+  const int j16 = lane & 15;
+  const int h = head_base + hg * 16 + j16;        // this lane's head
   const bool h_ok = h < a.H;
-  const int hi = lane >> 5;
 
-  // S^T operand reads: row t = 32 tg + lane%32, chunk c = 2 kb + hi.
-  const int ts = 32 * tg + (lane & 31);
-  int offS[8];                                    // latent: kb = 8 j + i -> offS[i] + 256 j
+  // DMA: latent row t of a slot is one instruction (lane l copies bytes
+  // 16 l .. 16 l + 15); wave w loads rows w, w + NW, ...
+  const unsigned offL = (unsigned)(lane << 4);
+  // RoPE rows of wave w: ROPE_ROWS rows from w * ROPE_ROWS, 8 lanes per row
+  const int rrow = wave * C::ROPE_ROWS + (lane >> 3);
+
+  // S^T operand reads: token t = 16 tb + j16, chunk 4 kb + G4 of its row
+  const int baseS = prow(j16) * kLatStride + 16 * G4;
+  int offR[2][2];                                 // RoPE part: [tb][kb']
 #pragma unroll
-  for (int i = 0; i < 8; ++i) offS[i] = ts * (D_C * 2) + (((2 * i + hi) ^ swl(ts)) << 4);
-  int offSR[4];                                   // RoPE part: kb' = 0..3
+  for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) offSR[i] = C::LAT_BYTES + ts * (D_R * 2) + (((2 * i + hi) ^ swr(ts)) << 4);
-  // P.V operand reads (transposing): rows ta = trow + 16 ks (+8 for the high
-  // half), chunk c = 4 fb + cpart, 8-byte half `half`.
-  const int G16 = lane >> 4, jj = lane & 15;
-  const int trow = 32 * tg + 4 * (G16 >> 1) + (jj >> 2);
-  const int cpart = 2 * (G16 & 1) + ((jj & 3) >> 1);
-  const int half = (jj & 1) << 3;
-  int offV[2][4];                                 // [lo/hi row][fb % 4] ; + 256 (fb/4) + 16 ks rows
-#pragma unroll
-  for (int r = 0; r < 2; ++r)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = trow + 8 * r;
-      offV[r][i] = t * (D_C * 2) + (((4 * i + cpart) ^ swl(t)) << 4) + half;
+    for (int k = 0; k < 2; ++k) {
+      const int t = 16 * tb + j16;
+      offR[tb][k] = C::LAT_BYTES + t * (D_R * 2) + (((4 * k + G4) ^ swr(t)) << 4);
     }
+  // P.V operand reads (transposing): source lane j16 of group G4 reads token
+  // 4 G4 + j16/4 (+16 for the second half), features 16 fb + 4 (j16 % 4) ..
+  const int baseV = prow(4 * G4 + (j16 >> 2)) * kLatStride + 8 * (j16 & 3);
+
+  const unsigned long long cache_addr = (unsigned long long)(uintptr_t)a.cache;
 
   for (; b < B && P < end_g; ++b) {
     const int Lb = a.seq_len[b];
@@ -217,16 +208,17 @@ void decode_attn_kernel(DecodeArgs a) {
     const bool complete = (P >= start_g) && (P + Lb <= end_g);
     const int t0 = (int)(seg_lo - P);             // first token of the segment in sequence b
     const int n = (int)(seg_hi - seg_lo);         // tokens in the segment
-    const int64_t row0 = a.seq_start[b] + t0;     // its first cache row
+    const unsigned long long seg_addr = cache_addr + (unsigned long long)(a.seq_start[b] + t0) * C::RWB;
     P += Lb;
 
-    // queries of this wave's heads, with the RoPE part rotated to position Lb-1
+    // queries of this lane's head: k-step kb holds features 32 kb + 8 G4 .. +7,
+    // the RoPE part rotated to position Lb-1
     bf16x8 q[C::KB];
     {
-      const bf16* qp = a.q + ((int64_t)b * a.H + (h_ok ? h : 0)) * C::RW + 8 * hi;
+      const bf16* qp = a.q + ((int64_t)b * a.H + (h_ok ? h : 0)) * C::RW + 8 * G4;
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
-        u32x4 v = h_ok ? *(const u32x4*)(qp + 16 * kb) : u32x4{0, 0, 0, 0};
+        u32x4 v = h_ok ? *(const u32x4*)(qp + 32 * kb) : u32x4{0, 0, 0, 0};
         q[kb] = as_bf16x8(v);
       }
       if constexpr (D_R > 0) {
@@ -235,7 +227,7 @@ void decode_attn_kernel(DecodeArgs a) {
           const double lb = log2((double)a.rope_base);
 #pragma unroll
           for (int kb = C::KB_C; kb < C::KB; ++kb) {
-            const int i0 = (16 * kb + 8 * hi - D_C) / 2;  // first pair index
+            const int i0 = (32 * kb + 8 * G4 - D_C) / 2;  // first pair index
             bf16x8 r = q[kb];
             unsigned int w[4];
 #pragma unroll
@@ -254,11 +246,39 @@ void decode_attn_kernel(DecodeArgs a) {
       }
     }
 
-    floatx16 o[C::FB];
+    const int nslots = (n + 31) >> 5;             // 32-token slots of the segment
+
+    // issue the DMA of slot j (tokens 32 j .. 32 j + 31) into ring position j % R
+    auto load_slot = [&](int j) {
+      const unsigned sb = smem_base + (unsigned)((j % R) * C::SLOT_BYTES);
+      const int tok0 = 32 * j;
+#pragma unroll
+      for (int k = 0; k < C::ROWS_L; ++k) {
+        const int t = wave + C::NW * k;
+        int row = tok0 + t;
+        row = row < n ? row : n - 1;
+        g2lds16_s(seg_addr + (unsigned long long)row * C::RWB, offL, sb + prow(t) * kLatStride);
+      }
+      if constexpr (D_R > 0) {
+#pragma unroll
+        for (int k = 0; k < C::ROUNDS_R; ++k) {
+          // eight rows per instruction: a scalar base row plus a small per-lane offset
+          int row0 = tok0 + wave * C::ROPE_ROWS + 8 * k;
+          row0 = row0 < n ? row0 : n - 1;
+          const int rr = rrow + 8 * k;
+          int row = tok0 + rr;
+          row = row < n ? row : n - 1;
+          const unsigned off = (unsigned)(D_C * 2 + (((lane & 7) ^ swr(rr & 15)) << 4));
+          g2lds16_s(seg_addr + (unsigned long long)row0 * C::RWB, (unsigned)(row - row0) * C::RWB + off,
+                    sb + C::LAT_BYTES + (wave * C::ROPE_ROWS + 8 * k) * 128);
+        }
+      }
+    };
+
+    floatx4 o[C::FB];
     float m = -INFINITY;     // reference max (log2 domain) of this lane's head
     float m_all = -INFINITY; // largest score seen in the segment
     float lsum = 0.f;        // this lane's share of the softmax denominator
-    const int ntiles = (n + C::TILE - 1) / C::TILE;
 
     // Pass 0 fixes the reference max at the first tile with a valid token and
     // never rescales O (so O only ever meets MFMA in the loop). If a later
@@ -267,230 +287,233 @@ void decode_attn_kernel(DecodeArgs a) {
     // reference (pass 1), which cannot overflow.
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-      for (int fb = 0; fb < C::FB; ++fb) o[fb] = floatx16{};
+      for (int fb = 0; fb < C::FB; ++fb) o[fb] = floatx4{0.f, 0.f, 0.f, 0.f};
       lsum = 0.f;
       lds_barrier();  // previous readers are done with the ring
 #pragma unroll
-      for (int s = 0; s < NBUF - 1; ++s)
-        if (s < ntiles) load_tile<C>(a.cache, row0, s * C::TILE, n, smem + s * C::TILE_BYTES, wave, lane);
+      for (int j = 0; j < C::PD; ++j)
+        if (j < nslots) load_slot(j);
 
-      for (int it = 0; it < ntiles; ++it) {
-        // tiles it+1 .. min(it+NBUF-2, ntiles-1) may stay in flight
-        int ahead = ntiles - 1 - it;
-        ahead = ahead < NBUF - 2 ? ahead : NBUF - 2;
-        wait_tiles_in_flight<C::ROUNDS, NBUF>(ahead);
+      for (int it = 0; it < nslots; ++it) {
+        // slot it is read now; slots issued after it may stay in flight
+        int issued = C::PD + it;
+        issued = issued < nslots ? issued : nslots;
+        wait_slots<C::ROUNDS, C::PD - 1>(issued - (it + 1));
         lds_barrier();
-        if (it + NBUF - 1 < ntiles)
-          load_tile<C>(a.cache, row0, (it + NBUF - 1) * C::TILE, n,
-                       smem + ((it + NBUF - 1) % NBUF) * C::TILE_BYTES, wave, lane);
+        if (C::PD + it < nslots) load_slot(C::PD + it);
 
-        const LDS_AS char* buf = smem + (it % NBUF) * C::TILE_BYTES;
-        // ---- S^T (32 tokens x 32 heads) ----
-        floatx16 s = floatx16{};
+        const LDS_AS char* buf = smem + (it % R) * C::SLOT_BYTES;
+        // ---- S^T (2 blocks of 16 tokens x 16 heads) ----
+        // LDS reads run PF steps ahead of their MFMA (a 16-cycle MFMA per step
+        // has to cover the LDS latency); scheduling barriers keep that order
+        constexpr int NSX = 2 * C::KB;            // steps: x = 2 kb + tb
+        auto readS = [&](int x) -> bf16x8 {
+          const int kb = x >> 1, tb = x & 1;
+          if (kb < C::KB_C) return as_bf16x8(lds_read16(buf + baseS + 16 * tb * kLatStride + 64 * kb));
+          return as_bf16x8(lds_read16(buf + offR[tb][kb - C::KB_C]));
+        };
+        floatx4 s[2];
+        {
+          bf16x8 fr[kPF];
 #pragma unroll
-        for (int kb = 0; kb < C::KB_C; ++kb) {
-          bf16x8 av = as_bf16x8(lds_read16(buf + offS[kb % 8] + 256 * (kb / 8)));
-          s = mfma32(av, q[kb], s);
-        }
+          for (int x = 0; x < kPF; ++x) fr[x] = readS(x);
 #pragma unroll
-        for (int kb = C::KB_C; kb < C::KB; ++kb) {
-          bf16x8 av = as_bf16x8(lds_read16(buf + offSR[kb - C::KB_C]));
-          s = mfma32(av, q[kb], s);
+          for (int x = 0; x < NSX; ++x) {
+            s[x & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[x % kPF], q[x >> 1],
+                                                               x < 2 ? floatx4{0.f, 0.f, 0.f, 0.f} : s[x & 1], 0, 0, 0);
+            if (x + kPF < NSX) fr[x % kPF] = readS(x + kPF);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
-        // ---- softmax weights; lane owns head (lane & 31), tokens 8(r/4)+4(lane/32)+r%4 ----
-        const int tok_base = it * C::TILE + 32 * tg + 4 * hi;
+        // ---- softmax weights; lane owns head j16, tokens 16 tb + 4 G4 + r ----
+        const int tok_base = 32 * it + 4 * G4;
         float mx = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int tok = tok_base + 8 * (r >> 2) + (r & 3);
-          float z = s[r] * scale2;
-          z = tok < n ? z : -INFINITY;
-          s[r] = z;
-          mx = fmaxf(mx, z);
-        }
-        mx = fmaxf(mx, xor32(mx));
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int tok = tok_base + 16 * tb + r;
+            float z = s[tb][r] * scale2;
+            z = tok < n ? z : -INFINITY;
+            s[tb][r] = z;
+            mx = fmaxf(mx, z);
+          }
+        mx = fmaxf(mx, shfl_xor_f(mx, 16));
+        mx = fmaxf(mx, shfl_xor_f(mx, 32));
         m_all = fmaxf(m_all, mx);
         if (m == -INFINITY) m = mx;  // first valid tile of this head: O is still zero
         const float mref = (m == -INFINITY) ? 0.f : m;
-        float p[16];
+        float p[2][4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          p[r] = fast_exp2(s[r] - mref);
-          lsum += p[r];
-        }
-        bf16x8 pb[2];
+        for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          pb[ks] = as_bf16x8(u32x4{pack_bf16x2(p[8 * ks + 0], p[8 * ks + 1]), pack_bf16x2(p[8 * ks + 2], p[8 * ks + 3]),
-                                   pack_bf16x2(p[8 * ks + 4], p[8 * ks + 5]), pack_bf16x2(p[8 * ks + 6], p[8 * ks + 7])});
-        // ---- O^T (d_c x 32 heads) += C^T . P^T ----
+          for (int r = 0; r < 4; ++r) {
+            p[tb][r] = fast_exp2(s[tb][r] - mref);
+            lsum += p[tb][r];
+          }
+        // P^T operand: k = 8 G4 + e <-> token 4 G4 + e (e < 4) or 16 + 4 G4 + e - 4
+        const bf16x8 pb = as_bf16x8(u32x4{pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
+                                          pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])});
+        // ---- O^T (512 features x 16 heads) += C^T . P^T, 32 blocks of 16 features ----
+        {
+          auto readV = [&](int fb) -> bf16x8 {
+            u32x2 lo = lds_read_tr16(buf + baseV + 32 * fb);
+            u32x2 hi2 = lds_read_tr16(buf + baseV + 16 * kLatStride + 32 * fb);
+            return as_bf16x8(u32x4{lo[0], lo[1], hi2[0], hi2[1]});
+          };
+          bf16x8 fr[kPF];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+          for (int fb = 0; fb < kPF; ++fb) fr[fb] = readV(fb);
 #pragma unroll
           for (int fb = 0; fb < C::FB; ++fb) {
-            const int imm = 256 * (fb / 4) + 16 * ks * (D_C * 2);
-            u32x2 lo = lds_read_tr16(buf + offV[0][fb % 4] + imm);
-            u32x2 hi2 = lds_read_tr16(buf + offV[1][fb % 4] + imm);
-            bf16x8 av = as_bf16x8(u32x4{lo[0], lo[1], hi2[0], hi2[1]});
-            o[fb] = mfma32(av, pb[ks], o[fb]);
+            o[fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[fb % kPF], pb, o[fb], 0, 0, 0);
+            if (fb + kPF < C::FB) fr[fb % kPF] = readV(fb + kPF);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
+      // workgroup-wide "any lane needs a redo" through LDS (ring is idle here)
       const bool redo = (m != -INFINITY) && (m_all > m + kRedo);
-      if (!__syncthreads_or(redo)) break;
+      const bool wave_redo = __builtin_amdgcn_ballot_w64(redo) != 0;
+      lds_barrier();
+      if (lane == 0) ((LDS_AS int*)smem)[wave] = wave_redo ? 1 : 0;
+      lds_barrier();
+      int any = 0;
+#pragma unroll
+      for (int w = 0; w < C::NW; ++w) any |= ((const LDS_AS int*)smem)[w];
+      if (!any) break;
       m = m_all;
     }
 
-    // ---- finish the segment ----
-    lsum += xor32(lsum);
-    if constexpr (C::TG > 1) {
-      // merge the token groups through LDS (the tile ring is free now)
-      __syncthreads();
-      float* xo = (float*)smem_raw;  // [TG-1][HG][FB*16 + 2][64] floats
-      if (tg > 0) {
-        float* dst = xo + ((size_t)((tg - 1) * HG + hg) * (C::FB * 16 + 2)) * 64;
-#pragma unroll
-        for (int fb = 0; fb < C::FB; ++fb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) dst[(fb * 16 + r) * 64 + lane] = o[fb][r];
-        dst[(C::FB * 16) * 64 + lane] = m;
-        dst[(C::FB * 16 + 1) * 64 + lane] = lsum;
-      }
-      __syncthreads();
-      if (tg == 0) {
-#pragma unroll
-        for (int u = 1; u < C::TG; ++u) {
-          const float* src = xo + ((size_t)((u - 1) * HG + hg) * (C::FB * 16 + 2)) * 64;
-          const float m2 = src[(C::FB * 16) * 64 + lane];
-          const float l2 = src[(C::FB * 16 + 1) * 64 + lane];
-          const float M = fmaxf(m, m2);
-          const float Mr = (M == -INFINITY) ? 0.f : M;
-          const float a1 = (m == -INFINITY) ? 0.f : fast_exp2(m - Mr);
-          const float a2 = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - Mr);
-#pragma unroll
-          for (int fb = 0; fb < C::FB; ++fb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[fb][r] = o[fb][r] * a1 + src[(fb * 16 + r) * 64 + lane] * a2;
-          lsum = lsum * a1 + l2 * a2;
-          m = M;
-        }
-      }
-    }
-    if (tg == 0 && h_ok) {
+    // ---- finish the segment: lane owns head j16, features 16 fb + 4 G4 + r ----
+    lsum += shfl_xor_f(lsum, 16);
+    lsum += shfl_xor_f(lsum, 32);
+    if (h_ok) {
       const float inv = 1.0f / lsum;
       const float lse_nat = m * kLn2 + __logf(lsum);
-      const int fofs = 4 * hi;
+      const int fofs = 4 * G4;
       if (complete) {
         bf16* op = a.o_lat + ((int64_t)b * a.H + h) * D_C + fofs;
 #pragma unroll
-        for (int fb = 0; fb < C::FB; ++fb)
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            u32x2 w = {pack_bf16x2(o[fb][4 * r4 + 0] * inv, o[fb][4 * r4 + 1] * inv),
-                       pack_bf16x2(o[fb][4 * r4 + 2] * inv, o[fb][4 * r4 + 3] * inv)};
-            *(u32x2*)(op + 32 * fb + 8 * r4) = w;
-          }
-        if (a.lse && lane < 32) a.lse[(int64_t)b * a.H + h] = lse_nat;
+        for (int fb = 0; fb < C::FB; ++fb) {
+          u32x2 w = {pack_bf16x2(o[fb][0] * inv, o[fb][1] * inv), pack_bf16x2(o[fb][2] * inv, o[fb][3] * inv)};
+          *(u32x2*)(op + 16 * fb) = w;
+        }
+        if (a.lse && G4 == 0) a.lse[(int64_t)b * a.H + h] = lse_nat;
       } else {
+        // partial piece, bf16, in the wave's register order: store k holds
+        // features 32 k + 4 G4 + r and 32 k + 16 + 4 G4 + r (r < 4) of head
+        // j16, and a whole store instruction writes 1 KiB contiguously
         const long long slot = (seg_lo > start_g) ? (2LL * g + 1) : (2LL * g);
-        float* op = a.part_o + (slot * a.H + h) * D_C + fofs;
+        const int H16 = (a.H + 15) >> 4;
+        bf16* op = a.part_o + ((slot * H16 + (h >> 4)) * 16) * (int64_t)(64 * 8) + lane * 8;
 #pragma unroll
-        for (int fb = 0; fb < C::FB; ++fb)
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            floatx4 w = {o[fb][4 * r4 + 0] * inv, o[fb][4 * r4 + 1] * inv, o[fb][4 * r4 + 2] * inv,
-                         o[fb][4 * r4 + 3] * inv};
-            *(floatx4*)(op + 32 * fb + 8 * r4) = w;
-          }
-        if (lane < 32) a.part_lse[slot * a.H + h] = lse_nat;
+        for (int k = 0; k < C::FB / 2; ++k) {
+          const floatx4 u = o[2 * k], v = o[2 * k + 1];
+          *(u32x4*)(op + k * 512) = u32x4{pack_bf16x2(u[0] * inv, u[1] * inv), pack_bf16x2(u[2] * inv, u[3] * inv),
+                                          pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv)};
+        }
+        if (G4 == 0) a.part_lse[slot * a.H + h] = lse_nat;
       }
     }
   }
 }
 
 // Merge the partial pieces of every sequence that was cut across slices, and
-// define the result of an empty sequence (o = 0, lse = -inf). One workgroup
-// per (sequence, head); 128 threads x 4 features.
-template <int D_C>
-__global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
-  const int b = blockIdx.x / a.H;
-  const int h = blockIdx.x % a.H;
+// define the result of an empty sequence (o = 0, lse = -inf): the log-sum-exp
+// merge of split softmax sums. Workgroup = (sequence, group of 16 heads,
+// quarter of the features); thread = one 16-byte lane record of one store
+// index k of the pieces' wave-ordered layout (see the attention epilogue).
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
+  constexpr int D_C = 512;
+  const int H16 = (a.H + 15) >> 4;
+  const int b = blockIdx.x / (H16 * 4);
+  const int hg = (blockIdx.x / 4) % H16;
+  const int k = (blockIdx.x % 4) * 4 + (threadIdx.x >> 6);  // store index 0..15
+  const int lane = threadIdx.x & 63;
+  const int h = hg * 16 + (lane & 15);
+  const int G4 = lane >> 4;
+  if (h >= a.H) return;
   const int Lb = a.seq_len[b];
-  const long long N = a.prefix[a.B - 1] + (a.seq_len[a.B - 1] > 0 ? a.seq_len[a.B - 1] : 0);
-  const int G = a.G;
-  const int f = threadIdx.x * 4;
-  bf16* op = a.o_lat + ((int64_t)b * a.H + h) * D_C;
+  bf16* op = a.o_lat + ((int64_t)b * a.H + h) * D_C + 32 * k + 4 * G4;  // features +0..3 and +16..19
   if (Lb <= 0) {
-    if (f < D_C) *(u32x2*)(op + f) = u32x2{0u, 0u};
-    if (threadIdx.x == 0 && a.lse) a.lse[(int64_t)b * a.H + h] = -INFINITY;
+    *(u32x2*)op = u32x2{0u, 0u};
+    *(u32x2*)(op + 16) = u32x2{0u, 0u};
+    if (k == 0 && G4 == 0 && a.lse) a.lse[(int64_t)b * a.H + h] = -INFINITY;
     return;
   }
+  const long long N = a.prefix[a.B - 1] + (a.seq_len[a.B - 1] > 0 ? a.seq_len[a.B - 1] : 0);
+  const int G = a.G;
   const long long P = a.prefix[b];
   // slice holding token p: the largest g with floor(g N / G) <= p
   const long long g_lo = ((P + 1) * G - 1) / N;
   const long long g_hi = ((P + Lb) * G - 1) / N;
   if (g_lo == g_hi) return;  // whole sequence inside one slice: already final
-  // slices with an empty range (possible when N < G) hold no piece
-  float M = -INFINITY;
+  // online merge over the pieces (slices with an empty range hold none)
+  float M = -INFINITY, den = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (long long g = g_lo; g <= g_hi; ++g) {
     const long long start_g = g * N / G;
     if (start_g == (g + 1) * N / G) continue;
     const long long slot = (P <= start_g) ? 2 * g : 2 * g + 1;
-    M = fmaxf(M, a.part_lse[slot * a.H + h]);
-  }
-  float den = 0.f;
-  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (long long g = g_lo; g <= g_hi; ++g) {
-    const long long start_g = g * N / G;
-    if (start_g == (g + 1) * N / G) continue;
-    const long long slot = (P <= start_g) ? 2 * g : 2 * g + 1;
-    const float w = __expf(a.part_lse[slot * a.H + h] - M);
-    den += w;
-    if (f < D_C) {
-      floatx4 v = *(const floatx4*)(a.part_o + (slot * a.H + h) * D_C + f);
-      acc += w * v;
+    const float l = a.part_lse[slot * a.H + h];
+    const u32x4 raw = *(const u32x4*)(a.part_o + ((slot * H16 + hg) * 16 + k) * (int64_t)512 + lane * 8);
+    const float Mn = fmaxf(M, l);
+    const float c = __expf(M - Mn), w = __expf(l - Mn);
+    den = den * c + w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float lo = __builtin_bit_cast(float, raw[e] << 16), hi = __builtin_bit_cast(float, raw[e] & 0xffff0000u);
+      acc[2 * e] = acc[2 * e] * c + w * lo;
+      acc[2 * e + 1] = acc[2 * e + 1] * c + w * hi;
     }
+    M = Mn;
   }
   const float inv = 1.f / den;
-  if (f < D_C) *(u32x2*)(op + f) = u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
-  if (threadIdx.x == 0 && a.lse) a.lse[(int64_t)b * a.H + h] = M + __logf(den);
+  *(u32x2*)op = u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+  *(u32x2*)(op + 16) = u32x2{pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+  if (k == 0 && G4 == 0 && a.lse) a.lse[(int64_t)b * a.H + h] = M + __logf(den);
 }
 
 // ---------------------------------------------------------------------------
-template <int D_C, int D_R, int HG, int NBUF>
+template <int D_R, int HG, int R>
 static hipError_t launch_variant(const DecodeArgs& a, hipStream_t st) {
-  using C = DecodeCfg<D_C, D_R, HG, NBUF>;
-  auto kern = decode_attn_kernel<D_C, D_R, HG, NBUF>;
+  using C = DecodeCfg<D_R, HG, R>;
+  auto kern = decode_attn_kernel<D_R, HG, R>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int head_chunks = (a.H + 32 * HG - 1) / (32 * HG);
-  hipLaunchKernelGGL(kern, dim3(a.G, head_chunks), dim3(256), C::LDS_BYTES, st, a);
+  const int chunks = (a.H + 16 * HG - 1) / (16 * HG);
+  hipLaunchKernelGGL(kern, dim3(a.G * chunks), dim3(64 * HG), C::LDS_BYTES, st, a);
   return hipGetLastError();
 }
 
+int decode_head_chunks(int H) { return H <= 32 ? 1 : (H + 63) / 64; }
+
 hipError_t launch_decode_attn(const DecodeArgs& a, hipStream_t st) {
-  const bool wide = a.H > 64;  // 128 heads per launch chunk, else 64
-  if (a.d_c == 512 && a.d_r == 0)
-    return wide ? launch_variant<512, 0, 4, 4>(a, st) : launch_variant<512, 0, 2, 2>(a, st);
-  if (a.d_c == 512 && a.d_r == 64)
-    return wide ? launch_variant<512, 64, 4, 4>(a, st) : launch_variant<512, 64, 2, 2>(a, st);
+  // one wave per 16 heads, 2 or 4 waves; more than 64 heads run as chunks of 64
+  if (a.d_c != 512) return hipErrorInvalidValue;
+  if ((long long)a.G * decode_head_chunks(a.H) > 2147483647LL) return hipErrorInvalidValue;
+  const bool small = a.H <= 32;
+  if (a.d_r == 0) return small ? launch_variant<0, 2, 4>(a, st) : launch_variant<0, 4, 4>(a, st);
+  if (a.d_r == 64) return small ? launch_variant<64, 2, 4>(a, st) : launch_variant<64, 4, 4>(a, st);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)(a.B * a.H));
-  if (a.d_c == 512) hipLaunchKernelGGL(decode_combine_kernel<512>, grid, dim3(128), 0, st, a);
-  else return hipErrorInvalidValue;
+  if (a.d_c != 512) return hipErrorInvalidValue;
+  const long long blocks = (long long)a.B * ((a.H + 15) / 16) * 4;
+  if (blocks > 2147483647LL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 // Only the d_c = 512 latent (the width every supported workload uses) is
-// enabled: the d_c = 256 instantiation faulted on the GPU for a reason not yet
-// found, so the narrower widths stay switched off.
+// enabled: an earlier d_c = 256 instantiation faulted on the GPU for a reason
+// not yet found, so narrower widths stay switched off.
 bool decode_bf16_supported(int d_c, int d_r) { return d_c == 512 && (d_r == 0 || d_r == 64); }
 
 }  // namespace gmla

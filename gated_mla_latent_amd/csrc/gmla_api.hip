@@ -75,7 +75,13 @@ int device_cus() {
   return cus;
 }
 
-int decode_slices(int num_splits) { return num_splits > 0 ? num_splits : device_cus(); }
+// Slices of the token range: the caller's count, or one workgroup per compute
+// unit counting every head chunk (a multiple of 8 so each XCD gets equal work).
+int decode_slices(int num_splits, int H) {
+  if (num_splits > 0) return num_splits;
+  const int g = device_cus() / decode_head_chunks(H);
+  return g >= 16 ? g / 8 * 8 : (g > 0 ? g : 1);
+}
 
 GemmArgs gemm(const void* A, int64_t lda, const void* W, int64_t ldw, void* C, int64_t ldc, int M, int N, int K,
               int epi = EPI_STORE, const void* O = nullptr, int64_t ldo = 0) {
@@ -195,8 +201,9 @@ gmla_status_t gmla_prefill(const void* x, const void* W_c, const void* W_q, cons
 size_t gmla_decode_workspace_size(int B, int H, int d_c, int num_splits, gmla_dtype_t dtype) {
   if (B <= 0 || H <= 0 || d_c <= 0 || num_splits < 0) return 0;
   if (dtype == GMLA_F32) return 0;
-  const size_t G = (size_t)decode_slices(num_splits);
-  return up256((size_t)B * 8) + up256(2 * G * H * 4) + up256(2 * G * H * (size_t)d_c * 4);
+  const size_t G = (size_t)decode_slices(num_splits, H);
+  const size_t H16 = ((size_t)H + 15) / 16 * 16;  // partial outputs are kept per group of 16 heads
+  return up256((size_t)B * 8) + up256(2 * G * H * 4) + up256(2 * G * H16 * (size_t)d_c * 2);
 }
 
 gmla_status_t gmla_decode(const void* q_abs, const void* cache, const int64_t* seq_start, const int32_t* seq_len,
@@ -223,7 +230,7 @@ gmla_status_t gmla_decode(const void* q_abs, const void* cache, const int64_t* s
     return s ? s : ok();
   }
   REQUIRE(decode_bf16_supported(d_c, d_r), GMLA_ERR_UNSUPPORTED, "bf16 decode needs d_c == 512 and d_r in {0, 64}");
-  const int G = decode_slices(num_splits);
+  const int G = decode_slices(num_splits, H);
   const size_t need = gmla_decode_workspace_size(B, H, d_c, num_splits, dtype);
   REQUIRE(workspace && workspace_bytes >= need, GMLA_ERR_WORKSPACE,
           "decode workspace needs " + std::to_string(need) + " bytes");
@@ -234,7 +241,7 @@ gmla_status_t gmla_decode(const void* q_abs, const void* cache, const int64_t* s
   a.o_lat = (bf16*)o_lat; a.lse = lse;
   a.prefix = (long long*)ws;
   a.part_lse = (float*)(ws + up256((size_t)B * 8));
-  a.part_o = (float*)(ws + up256((size_t)B * 8) + up256(2 * (size_t)G * H * 4));
+  a.part_o = (bf16*)(ws + up256((size_t)B * 8) + up256(2 * (size_t)G * H * 4));
   a.B = B; a.H = H; a.d_c = d_c; a.d_r = d_r; a.G = G;
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   a.rope_base = d_r > 0 ? rope_base : 0.f;

@@ -15,7 +15,7 @@ struct DecodeArgs {
   const int32_t* seq_len;   // [B]
   bf16* o_lat;              // [B, H, d_c]
   float* lse;               // [B, H] or null
-  float* part_o;            // [2G, H, d_c] partial outputs of cut sequences
+  bf16* part_o;             // [2G, H/16 head groups, 16 x d_c] partial outputs of cut sequences (wave order)
   float* part_lse;          // [2G, H]
   long long* prefix;        // [B] exclusive prefix sums of seq_len
   int B, H, d_c, d_r, G;
@@ -25,6 +25,8 @@ struct DecodeArgs {
 hipError_t launch_decode_attn(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st);
 bool decode_bf16_supported(int d_c, int d_r);
+// workgroups per slice (head chunks) of the bf16 decode kernel for H heads
+int decode_head_chunks(int H);
 
 // ---------------------------------------------------------------- GEMM
 // C[m, n] = epi( sum_k A[m, k] * W[n, k] ), all bf16 with fp32 accumulation.

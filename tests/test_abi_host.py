@@ -70,7 +70,9 @@ def test_decode_argument_checks(L):
 def test_decode_workspace_size_formula(L):
     B, H, d_c, G = 4, 64, 512, 8
     up = lambda n: (n + 255) // 256 * 256
-    assert L.gmla_decode_workspace_size(B, H, d_c, G, 1) == up(B * 8) + up(2 * G * H * 4) + up(2 * G * H * d_c * 4)
+    assert L.gmla_decode_workspace_size(B, H, d_c, G, 1) == up(B * 8) + up(2 * G * H * 4) + up(2 * G * H * d_c * 2)
+    # partial outputs are padded to whole groups of 16 heads
+    assert L.gmla_decode_workspace_size(B, 20, d_c, G, 1) == up(B * 8) + up(2 * G * 20 * 4) + up(2 * G * 32 * d_c * 2)
     assert L.gmla_decode_workspace_size(B, H, d_c, G, 0) == 0  # fp32 path needs none
     assert L.gmla_decode_workspace_size(0, H, d_c, G, 1) == 0
 
