@@ -9,23 +9,30 @@
 //
 // Design (MI355X):
 //  * The flattened token space of all sequences is cut into G equal slices,
-//    one per workgroup, so ragged lengths cost nothing in balance. A slice
-//    may hold pieces of several sequences; a sequence cut across slices
-//    yields fp32 partial (o, lse) pieces that the combine kernel merges.
-//  * A workgroup handles all heads of its slice: wave w owns 16 heads. Every
-//    wave reads every latent tile from LDS, so HBM bytes are read once while
-//    LDS serves H/16 readers (gfx950 LDS sustains ~200 B/clk/CU).
-//  * Latent tiles of 32 tokens stream HBM -> LDS through a ring of four slots
-//    with 1 KiB direct-to-LDS loads (one per cache row; the row base is
-//    scalar), three slots in flight ahead of the one being read.
+//    so ragged lengths cost nothing in balance. A slice may hold pieces of
+//    several sequences; a sequence cut across slices yields partial (o, lse)
+//    pieces that the combine kernel merges.
+//  * A workgroup takes one slice for up to 64 heads (more heads run as
+//    further workgroups placed beside it on the same XCD). It has 8 waves,
+//    two per SIMD, so one wave's memory-issue stalls leave its SIMD to the
+//    other. Wave w computes the scores and softmax weights of head group
+//    w % 4 (16 heads) for token half w / 4 (16 of a tile's 32 tokens); the
+//    weights are exchanged through LDS and wave w accumulates O for all 64
+//    heads over its eighth of the latent features (64 of 512).
+//  * Latent tiles of 32 tokens stream HBM -> LDS through a ring of four
+//    slots with 1 KiB direct-to-LDS loads (one per cache row; the row base
+//    is scalar). Two slots are being read (scores of tile i, P.V of tile
+//    i - 1) and two are in flight; each wave's share of the next slot's
+//    loads is interleaved with its score MFMAs.
 //  * S^T = C . Q^T on v_mfma_f32_16x16x32_bf16 (A = 16-byte LDS reads, B =
-//    the wave's queries held in VGPRs): each lane owns one head and 8 tokens.
-//  * O^T += C^T . P^T on the same MFMA: P^T comes straight from the S^T
-//    accumulators; C^T fragments come from ds_read_b64_tr_b16 (transposing
-//    LDS reads). O^T (16 heads x 512 features) lives in AGPRs.
-//  * LDS reads run two k-steps ahead of their MFMA, an order scheduling
-//    barriers keep; the compiler places O in AGPRs and inserts the MFMA
-//    hazard wait states (inline-asm MFMAs would hide those hazards from it).
+//    the wave's queries in VGPRs): each lane owns one head and 4 tokens.
+//  * O^T += C^T . P^T on the same MFMA: P^T is the head group's weights read
+//    back in exactly the B-operand lane layout; C^T fragments come from
+//    ds_read_b64_tr_b16 (transposing LDS reads).
+//  * Software pipeline with one barrier per tile: the P.V of tile i - 1 runs
+//    between the scores and the softmax of tile i. LDS reads run ahead of
+//    their MFMA, an order scheduling barriers keep; the compiler inserts the
+//    MFMA hazard wait states (inline-asm MFMAs would hide them from it).
 //  * No rescale of O inside the loop: the reference max is fixed at a head's
 //    first tile; a segment whose scores outgrow it by more than 2^32 is redone
 //    once with its true max (exact for any input, and O never meets VALU).
@@ -39,48 +46,59 @@ namespace {
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRedo = 32.0f;  // log2 headroom before a segment is redone
 constexpr int kPF = 8;          // LDS operand fragments in flight ahead of the MFMA
+constexpr bool kSpreadDMA = true;  // interleave the next slot's DMA with the score MFMAs
+constexpr int kRing = 4;           // LDS ring slots (slots in flight = kRing - 2)
 
 // LDS tile layout. A ring slot holds 32 cache rows.
-// Latent part (d_c = 512 bf16 = 1 KiB per row): row stride 1040 bytes (16
-// bytes of padding), token t stored in LDS row
-//     prow(t) = 16 (t >> 4) + 2 (t & 7) + ((t >> 3) & 1).
-// 1040 = 16 (mod 256), so a row's bank offset (64 four-byte banks) is
-// 16 prow(t) mod 256, which keeps both read patterns conflict-free:
-//   * S^T operand reads (ds_read_b128): 16 lanes read 16 consecutive tokens
-//     at one 16-byte chunk -> 16 distinct 16-byte bank groups;
-//   * P.V operand reads (ds_read_b64_tr_b16): 32 lanes read 8 tokens (two
-//     runs of 4) x 32 bytes -> 8 distinct 32-byte bank ranges.
+// gfx950's LDS behaves as 128 four-byte banks (measured with the bank-conflict
+// counter on probe patterns): a 64-lane ds_read_b128 (1 KiB) is conflict-free
+// when every 16-byte bank group, address mod 512, is hit exactly twice, and a
+// ds_read_b64_tr_b16 (512 B) when every 8-byte unit is hit once.
+// Latent part (d_c = 512 bf16 = 1 KiB per row): token t in row t, row stride
+// 1056 bytes (32 bytes of padding; 1056 = 32 mod 512). Then
+//   * score operand reads: 16 lanes read tokens t0..t0+15 at 16-byte chunk c,
+//     the four 16-lane groups chunks c..c+3 -> bank groups 2t + c cover each
+//     group twice;
+//   * P.V operand reads (transposing): 64 lanes read 16 tokens x 4 units of
+//     8 bytes -> 8-byte units 4t + u, all distinct.
 // Each latent row is one 1 KiB direct-to-LDS load, so the padding costs
 // nothing on the load side, and every k-step is a compile-time LDS offset.
 // The RoPE part (d_r = 64 -> 8 chunks, 128-byte rows, loaded eight rows per
 // instruction) follows the 32 latent rows with its chunks XOR-permuted by
-// swr(t) = (t >> 1) & 7 (row parity already picks the 128-byte half).
-constexpr int kLatStride = 1040;
-__device__ __forceinline__ int prow(int t) { return 16 * (t >> 4) + 2 * (t & 7) + ((t >> 3) & 1); }
-__device__ __forceinline__ int swr(int t) { return (t >> 1) & 7; }
+// swr(t) = 4 ((t >> 2) & 1): of the four tokens that share a bank offset
+// (t mod 4), two keep chunks 4k..4k+3 in place and two swap the halves.
+constexpr int kLatStride = 1056;
+__device__ __forceinline__ int swr(int t) { return ((t >> 2) & 1) << 2; }
 
 template <int D_R, int HG, int R>
 struct DecodeCfg {
   static constexpr int D_C = 512;
   static constexpr int RW = D_C + D_R;        // cache row width (elements)
   static constexpr int RWB = RW * 2;          // cache row bytes
-  static constexpr int NW = HG;               // waves: one per 16 heads
+  // wave w: head group w % HG (16 heads) for the scores of token half w / HG
+  // (16 of the tile's 32 tokens), and features (512 / NW) w .. of P.V
+  static constexpr int NW = 2 * HG;
   static constexpr int LAT_BYTES = 32 * kLatStride;
   static constexpr int SLOT_BYTES = LAT_BYTES + 32 * D_R * 2;
-  static constexpr int ROWS_L = 32 / NW;                        // latent rows per wave per slot
-  static constexpr int ROPE_ROWS = D_R ? 32 / NW : 0;           // RoPE rows per wave per slot
-  static constexpr int ROUNDS_R = D_R ? ROPE_ROWS / 8 : 0;       // 8 rows (64 lanes) per instruction
-  static constexpr int ROUNDS = ROWS_L + ROUNDS_R;              // DMA instructions per wave per slot
-  static constexpr int PD = R - 1;            // slots in flight ahead of the one being read
-  static constexpr int KB = RW / 32;          // k-steps of S^T (32 features each)
+  static constexpr int ROWS_L = 32 / NW;                 // latent rows per wave per slot
+  static constexpr int ROPE_ROWS = D_R ? 32 / NW : 0;    // RoPE rows per wave per slot (one instruction)
+  static constexpr int ROUNDS = ROWS_L + (D_R ? 1 : 0);  // DMA instructions per wave per slot
+  // slots in flight ahead of the one being read: the slot read for scores in
+  // one iteration is read again for P.V in the next, so two stay resident
+  static constexpr int PD = R - 2;
+  static constexpr int KB = RW / 32;          // k-steps of the scores (32 features each)
   static constexpr int KB_C = D_C / 32;
-  static constexpr int FB = D_C / 16;         // 16-feature blocks of O^T
+  static constexpr int FBW = 32 / NW;         // 16-feature blocks of O per wave
   static constexpr int RING_BYTES = R * SLOT_BYTES;
-  static constexpr int LDS_BYTES = RING_BYTES;
-  static_assert(NW == 2 || NW == 4, "2 or 4 waves");
+  static constexpr int P_OFF = RING_BYTES;    // weights: 2 buffers x HG head groups x 1 KiB
+  static constexpr int X_OFF = P_OFF + 2 * HG * 1024;  // per-head exchange: max and sum, [2 halves][16 HG]
+  static constexpr int LDS_BYTES = X_OFF + 2 * 2 * 16 * HG * 4;
+  static_assert(HG == 2 || HG == 4, "32 or 64 heads per workgroup");
   static_assert(D_R == 0 || D_R == 64, "RoPE rows are 8 chunks of 16 bytes");
+  static_assert(ROPE_ROWS * 8 <= 64, "RoPE rows of a wave fit one instruction");
   static_assert(LDS_BYTES <= 163840, "LDS budget");
   static_assert(64 * NW * 8 + 16 <= LDS_BYTES, "scan scratch fits in the ring");
+  static_assert(PD >= 1 && PD <= 3, "ring of 3 to 5 slots");
   static_assert((PD - 1) * ROUNDS < 64, "vmcnt range");
 };
 
@@ -100,10 +118,20 @@ __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane_id() ^ mask) << 2, __builtin_bit_cast(int, v)));
 }
 
+// max / sum over the four 16-lane groups (the lanes of one head)
+__device__ __forceinline__ float head_max(float v) {
+  v = fmaxf(v, shfl_xor_f(v, 16));
+  return fmaxf(v, shfl_xor_f(v, 32));
+}
+__device__ __forceinline__ float head_sum(float v) {
+  v += shfl_xor_f(v, 16);
+  return v + shfl_xor_f(v, 32);
+}
+
 }  // namespace
 
 template <int D_R, int HG, int R>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * HG, 64 * HG), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(128 * HG, 128 * HG), amdgpu_waves_per_eu(HG / 2, HG / 2)))
 void decode_attn_kernel(DecodeArgs a) {
   using C = DecodeCfg<D_R, HG, R>;
   constexpr int D_C = C::D_C;
@@ -115,7 +143,8 @@ void decode_attn_kernel(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hg = wave;
+  const int hg = wave % HG;   // head group of this wave's scores
+  const int th = wave / HG;   // token half of this wave's scores
   const int G = a.G;
 
   // Work item = (slice, head chunk of 16 HG heads). XCD-aware order: the
@@ -175,28 +204,29 @@ void decode_attn_kernel(DecodeArgs a) {
   const float scale2 = a.scale_log2;
   const int G4 = lane >> 4;                       // 16-lane group
   const int j16 = lane & 15;
-  const int h = head_base + hg * 16 + j16;        // this lane's head
+  const int h = head_base + hg * 16 + j16;        // this lane's head for the scores
   const bool h_ok = h < a.H;
 
   // DMA: latent row t of a slot is one instruction (lane l copies bytes
-  // 16 l .. 16 l + 15); wave w loads rows w, w + NW, ...
+  // 16 l .. 16 l + 15); wave w loads rows w, w + NW, ... and RoPE rows
+  // w * ROPE_ROWS .. + ROPE_ROWS - 1 (8 lanes per row) in one more.
   const unsigned offL = (unsigned)(lane << 4);
-  // RoPE rows of wave w: ROPE_ROWS rows from w * ROPE_ROWS, 8 lanes per row
   const int rrow = wave * C::ROPE_ROWS + (lane >> 3);
 
-  // S^T operand reads: token t = 16 tb + j16, chunk 4 kb + G4 of its row
-  const int baseS = prow(j16) * kLatStride + 16 * G4;
-  int offR[2][2];                                 // RoPE part: [tb][kb']
+  // score operand reads: token 16 th + j16, chunk 4 kb + G4 of its row
+  const int t_s = 16 * th + j16;
+  const int baseS = t_s * kLatStride + 16 * G4;
+  int offR[2];                                    // RoPE part, k-steps KB_C, KB_C + 1
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int t = 16 * tb + j16;
-      offR[tb][k] = C::LAT_BYTES + t * (D_R * 2) + (((4 * k + G4) ^ swr(t)) << 4);
-    }
+  for (int k = 0; k < 2; ++k) offR[k] = C::LAT_BYTES + t_s * (D_R * 2) + (((4 * k + G4) ^ swr(t_s)) << 4);
   // P.V operand reads (transposing): source lane j16 of group G4 reads token
-  // 4 G4 + j16/4 (+16 for the second half), features 16 fb + 4 (j16 % 4) ..
-  const int baseV = prow(4 * G4 + (j16 >> 2)) * kLatStride + 8 * (j16 & 3);
+  // 4 G4 + j16/4 (+16 for the second half), features fw + 16 fb + 4 (j16 % 4)
+  // .. + 3, where wave w owns the features fw = (512 / NW) w .. + 512 / NW - 1
+  const int fw = (D_C / C::NW) * wave;
+  const int baseV = (4 * G4 + (j16 >> 2)) * kLatStride + 8 * (j16 & 3) + 2 * fw;
+  LDS_AS float* s_mx = (LDS_AS float*)(smem + C::X_OFF);  // [2][16 HG] per-half head maxima
+  LDS_AS float* s_ls = s_mx + 2 * 16 * HG;                  // [2][16 HG] per-half head sums
+  const int xi = 16 * hg + j16;                             // this lane's head in the exchange arrays
 
   const unsigned long long cache_addr = (unsigned long long)(uintptr_t)a.cache;
 
@@ -248,174 +278,212 @@ void decode_attn_kernel(DecodeArgs a) {
 
     const int nslots = (n + 31) >> 5;             // 32-token slots of the segment
 
-    // issue the DMA of slot j (tokens 32 j .. 32 j + 31) into ring position j % R
-    auto load_slot = [&](int j) {
+    // DMA instruction k (< ROUNDS) of slot j (tokens 32 j .. 32 j + 31), into
+    // ring position j % R: latent rows first, then the RoPE rows
+    auto load_part = [&](int j, int k) {
       const unsigned sb = smem_base + (unsigned)((j % R) * C::SLOT_BYTES);
       const int tok0 = 32 * j;
-#pragma unroll
-      for (int k = 0; k < C::ROWS_L; ++k) {
+      if (k < C::ROWS_L) {
         const int t = wave + C::NW * k;
         int row = tok0 + t;
         row = row < n ? row : n - 1;
-        g2lds16_s(seg_addr + (unsigned long long)row * C::RWB, offL, sb + prow(t) * kLatStride);
-      }
-      if constexpr (D_R > 0) {
-#pragma unroll
-        for (int k = 0; k < C::ROUNDS_R; ++k) {
-          // eight rows per instruction: a scalar base row plus a small per-lane offset
-          int row0 = tok0 + wave * C::ROPE_ROWS + 8 * k;
-          row0 = row0 < n ? row0 : n - 1;
-          const int rr = rrow + 8 * k;
-          int row = tok0 + rr;
-          row = row < n ? row : n - 1;
-          const unsigned off = (unsigned)(D_C * 2 + (((lane & 7) ^ swr(rr & 15)) << 4));
+        g2lds16_s(seg_addr + (unsigned long long)row * C::RWB, offL, sb + t * kLatStride);
+      } else if constexpr (D_R > 0) {
+        // a scalar base row plus a small per-lane row offset
+        int row0 = tok0 + wave * C::ROPE_ROWS;
+        row0 = row0 < n ? row0 : n - 1;
+        int row = tok0 + rrow;
+        row = row < n ? row : n - 1;
+        const unsigned off = (unsigned)(D_C * 2 + (((lane & 7) ^ swr(rrow)) << 4));
+        if (C::ROPE_ROWS * 8 == 64 || lane < C::ROPE_ROWS * 8)
           g2lds16_s(seg_addr + (unsigned long long)row0 * C::RWB, (unsigned)(row - row0) * C::RWB + off,
-                    sb + C::LAT_BYTES + (wave * C::ROPE_ROWS + 8 * k) * 128);
-        }
+                    sb + C::LAT_BYTES + wave * C::ROPE_ROWS * 128);
       }
     };
+    auto load_slot = [&](int j) {
+#pragma unroll
+      for (int k = 0; k < C::ROUNDS; ++k) load_part(j, k);
+    };
 
-    floatx4 o[C::FB];
+    // O^T of every head of the workgroup over this wave's features:
+    // o[fb * HG + hb] = features fw + 16 fb + 4 G4 + r, head 16 hb + j16
+    floatx4 o[C::FBW * HG];
     float m = -INFINITY;     // reference max (log2 domain) of this lane's head
-    float m_all = -INFINITY; // largest score seen in the segment
+    float m_all = -INFINITY; // largest score of this lane (its head, its tokens) in the pass
     float lsum = 0.f;        // this lane's share of the softmax denominator
 
-    // Pass 0 fixes the reference max at the first tile with a valid token and
-    // never rescales O (so O only ever meets MFMA in the loop). If a later
-    // score exceeds the reference by more than 2^kRedo the pass may have lost
-    // range; the workgroup then repeats the segment once with the true max as
-    // reference (pass 1), which cannot overflow.
+    // Pass 0 fixes each head's reference max at its first tile and never
+    // rescales O. If a later score exceeds the reference by more than
+    // 2^kRedo the pass may have lost range; the workgroup then repeats the
+    // segment once with the true max as reference (pass 1), which cannot
+    // overflow.
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-      for (int fb = 0; fb < C::FB; ++fb) o[fb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < C::FBW * HG; ++i) o[i] = floatx4{0.f, 0.f, 0.f, 0.f};
       lsum = 0.f;
+      m_all = -INFINITY;
       lds_barrier();  // previous readers are done with the ring
 #pragma unroll
       for (int j = 0; j < C::PD; ++j)
         if (j < nslots) load_slot(j);
 
+      // O^T (this wave's features x all heads) += C^T . P^T for the tile in
+      // ring slot `slot`, with the weights published in P buffer `pbi` (each
+      // head group's B operand, written half by half by its two waves)
+      auto pv = [&](int slot, int pbi) {
+        const LDS_AS char* vbuf = smem + slot * C::SLOT_BYTES;
+        const LDS_AS char* pbuf = smem + C::P_OFF + pbi * (HG * 1024);
+        bf16x8 pt[HG];
+#pragma unroll
+        for (int hb = 0; hb < HG; ++hb) pt[hb] = as_bf16x8(lds_read16(pbuf + hb * 1024 + lane * 16));
+        auto readV = [&](int fb) -> bf16x8 {
+          u32x2 lo = lds_read_tr16(vbuf + baseV + 32 * fb);
+          u32x2 hi2 = lds_read_tr16(vbuf + baseV + 16 * kLatStride + 32 * fb);
+          return as_bf16x8(u32x4{lo[0], lo[1], hi2[0], hi2[1]});
+        };
+        constexpr int PFV = C::FBW < 4 ? C::FBW : 4;  // each fragment feeds HG MFMAs
+        bf16x8 fr[PFV];
+#pragma unroll
+        for (int fb = 0; fb < PFV; ++fb) fr[fb] = readV(fb);
+#pragma unroll
+        for (int fb = 0; fb < C::FBW; ++fb) {
+#pragma unroll
+          for (int hb = 0; hb < HG; ++hb)
+            o[fb * HG + hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[fb % PFV], pt[hb], o[fb * HG + hb], 0, 0, 0);
+          if (fb + PFV < C::FBW) fr[fb % PFV] = readV(fb + PFV);
+        }
+      };
+
+      // Software pipeline, one barrier per tile: iteration `it` computes the
+      // scores and weights of tile it and the P.V product of tile it - 1
+      // (whose weights the barrier has just made visible), so the softmax
+      // arithmetic of one tile overlaps the P.V MFMAs of the previous one.
       for (int it = 0; it < nslots; ++it) {
         // slot it is read now; slots issued after it may stay in flight
         int issued = C::PD + it;
         issued = issued < nslots ? issued : nslots;
         wait_slots<C::ROUNDS, C::PD - 1>(issued - (it + 1));
         lds_barrier();
-        if (C::PD + it < nslots) load_slot(C::PD + it);
+        // the next slot's DMA is issued one instruction at a time between the
+        // score MFMAs: an issue that waits for room in the memory queue then
+        // holds up this wave only, while the other wave of its SIMD computes
+        const bool load_next = C::PD + it < nslots;
+        if (!kSpreadDMA && load_next) load_slot(C::PD + it);
 
         const LDS_AS char* buf = smem + (it % R) * C::SLOT_BYTES;
-        // ---- S^T (2 blocks of 16 tokens x 16 heads) ----
-        // LDS reads run PF steps ahead of their MFMA (a 16-cycle MFMA per step
-        // has to cover the LDS latency); scheduling barriers keep that order
-        constexpr int NSX = 2 * C::KB;            // steps: x = 2 kb + tb
-        auto readS = [&](int x) -> bf16x8 {
-          const int kb = x >> 1, tb = x & 1;
-          if (kb < C::KB_C) return as_bf16x8(lds_read16(buf + baseS + 16 * tb * kLatStride + 64 * kb));
-          return as_bf16x8(lds_read16(buf + offR[tb][kb - C::KB_C]));
+        // ---- S^T (16 tokens x 16 heads) ----
+        // LDS reads run kPF steps ahead of their MFMA; scheduling barriers
+        // keep that order
+        auto readS = [&](int kb) -> bf16x8 {
+          if (kb < C::KB_C) return as_bf16x8(lds_read16(buf + baseS + 64 * kb));
+          return as_bf16x8(lds_read16(buf + offR[kb - C::KB_C]));
         };
-        floatx4 s[2];
+        floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
         {
-          bf16x8 fr[kPF];
+          constexpr int PF = kPF < C::KB ? kPF : C::KB;
+          bf16x8 fr[PF];
 #pragma unroll
-          for (int x = 0; x < kPF; ++x) fr[x] = readS(x);
+          for (int x = 0; x < PF; ++x) fr[x] = readS(x);
 #pragma unroll
-          for (int x = 0; x < NSX; ++x) {
-            s[x & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[x % kPF], q[x >> 1],
-                                                               x < 2 ? floatx4{0.f, 0.f, 0.f, 0.f} : s[x & 1], 0, 0, 0);
-            if (x + kPF < NSX) fr[x % kPF] = readS(x + kPF);
+          for (int x = 0; x < C::KB; ++x) {
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[x % PF], q[x], s, 0, 0, 0);
+            if (x + PF < C::KB) fr[x % PF] = readS(x + PF);
+            if constexpr (kSpreadDMA) {
+              constexpr int SP = C::KB / C::ROUNDS;  // score steps per DMA instruction
+              if (x % SP == 0 && x / SP < C::ROUNDS && load_next) load_part(C::PD + it, x / SP);
+            }
             __builtin_amdgcn_sched_barrier(0);
           }
         }
-        // ---- softmax weights; lane owns head j16, tokens 16 tb + 4 G4 + r ----
-        const int tok_base = 32 * it + 4 * G4;
+        // ---- P.V of the previous tile ----
+        if (it > 0) pv((it - 1) % R, (it - 1) & 1);
+        // ---- softmax weights; lane owns head j16, tokens 32 it + 16 th + 4 G4 + r ----
+        const int tok_base = 32 * it + 16 * th + 4 * G4;
+        float z[4];
         float mx = -INFINITY;
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int tok = tok_base + 16 * tb + r;
-            float z = s[tb][r] * scale2;
-            z = tok < n ? z : -INFINITY;
-            s[tb][r] = z;
-            mx = fmaxf(mx, z);
-          }
-        mx = fmaxf(mx, shfl_xor_f(mx, 16));
-        mx = fmaxf(mx, shfl_xor_f(mx, 32));
-        m_all = fmaxf(m_all, mx);
-        if (m == -INFINITY) m = mx;  // first valid tile of this head: O is still zero
-        const float mref = (m == -INFINITY) ? 0.f : m;
-        float p[2][4];
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            p[tb][r] = fast_exp2(s[tb][r] - mref);
-            lsum += p[tb][r];
-          }
-        // P^T operand: k = 8 G4 + e <-> token 4 G4 + e (e < 4) or 16 + 4 G4 + e - 4
-        const bf16x8 pb = as_bf16x8(u32x4{pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
-                                          pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])});
-        // ---- O^T (512 features x 16 heads) += C^T . P^T, 32 blocks of 16 features ----
-        {
-          auto readV = [&](int fb) -> bf16x8 {
-            u32x2 lo = lds_read_tr16(buf + baseV + 32 * fb);
-            u32x2 hi2 = lds_read_tr16(buf + baseV + 16 * kLatStride + 32 * fb);
-            return as_bf16x8(u32x4{lo[0], lo[1], hi2[0], hi2[1]});
-          };
-          bf16x8 fr[kPF];
-#pragma unroll
-          for (int fb = 0; fb < kPF; ++fb) fr[fb] = readV(fb);
-#pragma unroll
-          for (int fb = 0; fb < C::FB; ++fb) {
-            o[fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[fb % kPF], pb, o[fb], 0, 0, 0);
-            if (fb + kPF < C::FB) fr[fb % kPF] = readV(fb + kPF);
-            __builtin_amdgcn_sched_barrier(0);
-          }
+        for (int r = 0; r < 4; ++r) {
+          z[r] = tok_base + r < n ? s[r] * scale2 : -INFINITY;
+          mx = fmaxf(mx, z[r]);
         }
+        if (pass == 0 && it == 0) {
+          // reference max: the head's max over the first tile, from both halves
+          mx = head_max(mx);
+          if (G4 == 0) s_mx[th * 16 * HG + xi] = mx;
+          lds_barrier();
+          m = fmaxf(s_mx[xi], s_mx[16 * HG + xi]);
+        }
+        m_all = fmaxf(m_all, mx);
+        const float mref = (m == -INFINITY) ? 0.f : m;
+        float p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[r] = fast_exp2(z[r] - mref);
+          lsum += p[r];
+        }
+        // this half of the head group's P^T operand: k = 8 G4 + 4 th + r <->
+        // token 16 th + 4 G4 + r
+        *(LDS_AS u32x2*)(smem + C::P_OFF + (it & 1) * (HG * 1024) + hg * 1024 + lane * 16 + th * 8) =
+            u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
       }
-      // workgroup-wide "any lane needs a redo" through LDS (ring is idle here)
+      // ---- P.V of the last tile ----
+      lds_barrier();
+      if (nslots > 0) pv((nslots - 1) % R, (nslots - 1) & 1);
+      // ---- overflow check: any head whose scores outgrew its reference ----
+      m_all = head_max(m_all);
       const bool redo = (m != -INFINITY) && (m_all > m + kRedo);
       const bool wave_redo = __builtin_amdgcn_ballot_w64(redo) != 0;
-      lds_barrier();
+      lds_barrier();  // every wave is done with the ring and the exchange arrays
       if (lane == 0) ((LDS_AS int*)smem)[wave] = wave_redo ? 1 : 0;
+      if (G4 == 0) s_mx[th * 16 * HG + xi] = m_all;
       lds_barrier();
       int any = 0;
 #pragma unroll
       for (int w = 0; w < C::NW; ++w) any |= ((const LDS_AS int*)smem)[w];
       if (!any) break;
-      m = m_all;
+      m = fmaxf(s_mx[xi], s_mx[16 * HG + xi]);
     }
 
-    // ---- finish the segment: lane owns head j16, features 16 fb + 4 G4 + r ----
-    lsum += shfl_xor_f(lsum, 16);
-    lsum += shfl_xor_f(lsum, 32);
-    if (h_ok) {
-      const float inv = 1.0f / lsum;
-      const float lse_nat = m * kLn2 + __logf(lsum);
-      const int fofs = 4 * G4;
-      if (complete) {
-        bf16* op = a.o_lat + ((int64_t)b * a.H + h) * D_C + fofs;
+    // ---- finish the segment ----
+    // both halves publish their sums; every wave then scales and stores its
+    // features of all heads
+    lsum = head_sum(lsum);
+    if (G4 == 0) s_ls[th * 16 * HG + xi] = lsum;
+    lds_barrier();
+    const long long slot = (seg_lo > start_g) ? (2LL * g + 1) : (2LL * g);
+    if (th == 0 && h_ok && G4 == 0) {
+      const float lse_nat = m * kLn2 + __logf(s_ls[xi] + s_ls[16 * HG + xi]);
+      if (!complete) a.part_lse[slot * a.H + h] = lse_nat;
+      else if (a.lse) a.lse[(int64_t)b * a.H + h] = lse_nat;
+    }
+    const int H16 = (a.H + 15) >> 4;
 #pragma unroll
-        for (int fb = 0; fb < C::FB; ++fb) {
-          u32x2 w = {pack_bf16x2(o[fb][0] * inv, o[fb][1] * inv), pack_bf16x2(o[fb][2] * inv, o[fb][3] * inv)};
-          *(u32x2*)(op + 16 * fb) = w;
-        }
-        if (a.lse && G4 == 0) a.lse[(int64_t)b * a.H + h] = lse_nat;
-      } else {
-        // partial piece, bf16, in the wave's register order: store k holds
-        // features 32 k + 4 G4 + r and 32 k + 16 + 4 G4 + r (r < 4) of head
-        // j16, and a whole store instruction writes 1 KiB contiguously
-        const long long slot = (seg_lo > start_g) ? (2LL * g + 1) : (2LL * g);
-        const int H16 = (a.H + 15) >> 4;
-        bf16* op = a.part_o + ((slot * H16 + (h >> 4)) * 16) * (int64_t)(64 * 8) + lane * 8;
+    for (int hb = 0; hb < HG; ++hb) {
+      const int hh = head_base + 16 * hb + j16;  // head of this lane's column in block hb
+      if (hh < a.H) {
+        const float inv = 1.0f / (s_ls[16 * hb + j16] + s_ls[16 * HG + 16 * hb + j16]);
+        if (complete) {
+          bf16* op = a.o_lat + ((int64_t)b * a.H + hh) * D_C + fw + 4 * G4;
 #pragma unroll
-        for (int k = 0; k < C::FB / 2; ++k) {
-          const floatx4 u = o[2 * k], v = o[2 * k + 1];
-          *(u32x4*)(op + k * 512) = u32x4{pack_bf16x2(u[0] * inv, u[1] * inv), pack_bf16x2(u[2] * inv, u[3] * inv),
-                                          pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv)};
+          for (int fb = 0; fb < C::FBW; ++fb) {
+            const floatx4 u = o[fb * HG + hb];
+            *(u32x2*)(op + 16 * fb) = u32x2{pack_bf16x2(u[0] * inv, u[1] * inv), pack_bf16x2(u[2] * inv, u[3] * inv)};
+          }
+        } else {
+          // partial piece, bf16, in register order: record K = fw / 32 + k of
+          // head group hh / 16 holds features 32 K + 4 G4 + r and
+          // 32 K + 16 + 4 G4 + r (r < 4) of head hh; one store writes 1 KiB
+          bf16* op = a.part_o + ((slot * H16 + (hh >> 4)) * 16 + fw / 32) * (int64_t)512 + lane * 8;
+#pragma unroll
+          for (int k = 0; k < C::FBW / 2; ++k) {
+            const floatx4 u = o[(2 * k) * HG + hb], v = o[(2 * k + 1) * HG + hb];
+            *(u32x4*)(op + k * 512) = u32x4{pack_bf16x2(u[0] * inv, u[1] * inv), pack_bf16x2(u[2] * inv, u[3] * inv),
+                                            pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv)};
+          }
         }
-        if (G4 == 0) a.part_lse[slot * a.H + h] = lse_nat;
       }
     }
+    lds_barrier();  // the exchange arrays are rewritten by the next segment
   }
 }
 
@@ -487,19 +555,19 @@ static hipError_t launch_variant(const DecodeArgs& a, hipStream_t st) {
     attr_set = true;
   }
   const int chunks = (a.H + 16 * HG - 1) / (16 * HG);
-  hipLaunchKernelGGL(kern, dim3(a.G * chunks), dim3(64 * HG), C::LDS_BYTES, st, a);
+  hipLaunchKernelGGL(kern, dim3(a.G * chunks), dim3(C::NW * 64), C::LDS_BYTES, st, a);
   return hipGetLastError();
 }
 
 int decode_head_chunks(int H) { return H <= 32 ? 1 : (H + 63) / 64; }
 
 hipError_t launch_decode_attn(const DecodeArgs& a, hipStream_t st) {
-  // one wave per 16 heads, 2 or 4 waves; more than 64 heads run as chunks of 64
+  // 32 or 64 heads per workgroup (4 or 8 waves); more heads run as chunks of 64
   if (a.d_c != 512) return hipErrorInvalidValue;
   if ((long long)a.G * decode_head_chunks(a.H) > 2147483647LL) return hipErrorInvalidValue;
   const bool small = a.H <= 32;
-  if (a.d_r == 0) return small ? launch_variant<0, 2, 4>(a, st) : launch_variant<0, 4, 4>(a, st);
-  if (a.d_r == 64) return small ? launch_variant<64, 2, 4>(a, st) : launch_variant<64, 4, 4>(a, st);
+  if (a.d_r == 0) return small ? launch_variant<0, 2, kRing>(a, st) : launch_variant<0, 4, kRing>(a, st);
+  if (a.d_r == 64) return small ? launch_variant<64, 2, kRing>(a, st) : launch_variant<64, 4, kRing>(a, st);
   return hipErrorInvalidValue;
 }
 
