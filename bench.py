@@ -39,11 +39,11 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 F32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector, published
 
 WORKLOADS = {
-    "decode_nope": ("config2", "decode NoPE, B=32, H=64, d_c=512, L_b~U[1024,8192], bf16 + gate/W_o (d_model 7168, d_v 128)"),
-    "decode_rope": ("config3", "decode RoPE, B=64, H=128, d_c=512+d_r=64, L_b~U[1024,16384], bf16 + gate/W_o (d_model 7168, d_v 128)"),
-    "decode_long": ("config5", "decode RoPE, B=8, H=128, d_c=512+64, L=131072 each, bf16 + gate/W_o (d_model 7168, d_v 128)"),
-    "prefill": ("config4", "causal prefill B=2, L=8192, d_model=7168, H=64, d_c=512, d_k=d_v=128, bf16 + gate/W_o"),
-    "tiny_fp32": ("config1", "causal prefill B=1, L=128, d_model=256, H=4, d_c=64, d_k=d_v=32, fp32 + gate/W_o"),
+    "decode_nope": ("decode_nope_b32_h64", "decode NoPE, B=32, H=64, d_c=512, L_b~U[1024,8192], bf16 + gate/W_o (d_model 7168, d_v 128)"),
+    "decode_rope": ("decode_rope_b64_h128", "decode RoPE, B=64, H=128, d_c=512+d_r=64, L_b~U[1024,16384], bf16 + gate/W_o (d_model 7168, d_v 128)"),
+    "decode_long": ("decode_rope_b8_l131072", "decode RoPE, B=8, H=128, d_c=512+64, L=131072 each, bf16 + gate/W_o (d_model 7168, d_v 128)"),
+    "prefill": ("prefill_b2_l8192", "causal prefill B=2, L=8192, d_model=7168, H=64, d_c=512, d_k=d_v=128, bf16 + gate/W_o"),
+    "tiny_fp32": ("prefill_f32_tiny", "causal prefill B=1, L=128, d_model=256, H=4, d_c=64, d_k=d_v=32, fp32 + gate/W_o"),
 }
 
 
@@ -258,6 +258,49 @@ def cpu_baseline_prefill(p, budget_s):
 
 
 # ----------------------------------------------------------------------------- main
+
+# HBM traffic of a kernel, from a committed rocprofv3 counter summary
+# (profiles/<kernel>_<workload>_traffic.md): FETCH_SIZE and WRITE_SIZE per
+# dispatch, scaled by what the same counters read for a plain device copy of
+# known size. The record names the SHA-256 of the kernel's sources when the
+# counters were taken; if the sources changed since, the figure is stale and
+# traffic is reported as null.
+KERNEL_SOURCES = {
+    "decode_attn": ["decode.hip", "common.h"],
+    "prefill_attn": ["attn_prefill.hip", "common.h"],
+}
+
+
+def kernel_source_sha(kernel: str):
+    import hashlib
+    files = KERNEL_SOURCES.get(kernel)
+    if not files:
+        return None
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "gated_mla_latent_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_record(kernel: str, workload: str):
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as fh:
+        for line in fh:
+            line = line.strip().lstrip("-").strip()
+            if ":" in line and not line.startswith("|"):
+                k, v = line.split(":", 1)
+                rec[k.strip().strip("`")] = v.strip().strip("`")
+    if rec.get("source_sha256") != kernel_source_sha(kernel):
+        return None
+    try:
+        return float(rec["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -348,7 +391,7 @@ def main():
             if dom in alg:
                 a = alg[dom] / (kern[dom]["avg_us"] * 1e-6) / 1e9
                 out["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                   "frac": a / HBM_PEAK_GBS, "traffic": None,
+                                   "frac": a / HBM_PEAK_GBS, "traffic": traffic_record(dom, args.workload),
                                    "alg_bytes_per_launch": alg[dom]}
         out["kernels"] = kern
         if not args.no_cpu_baseline:
@@ -370,7 +413,8 @@ def main():
                 dom = max(cand, key=lambda k: cand[k]["avg_us"] * cand[k]["launches_per_step"])
                 a = fl[dom] / (kern[dom]["avg_us"] * 1e-6) / 1e12
                 out["roofline"] = {"bound": "alu" if inp.dtype == torch.float32 else "mfma", "kernel": dom,
-                                   "achieved": a, "peak": peak, "unit": "TFLOP/s", "frac": a / peak, "traffic": None,
+                                   "achieved": a, "peak": peak, "unit": "TFLOP/s", "frac": a / peak,
+                                   "traffic": traffic_record(dom, args.workload),
                                    "alg_flops_per_launch": fl[dom]}
         out["kernels"] = kern
         if not args.no_cpu_baseline:

@@ -50,10 +50,9 @@ constexpr bool kSpreadDMA = true;  // interleave the next slot's DMA with the sc
 constexpr int kRing = 4;           // LDS ring slots (slots in flight = kRing - 2)
 
 // LDS tile layout. A ring slot holds 32 cache rows.
-// gfx950's LDS behaves as 128 four-byte banks (measured with the bank-conflict
-// counter on probe patterns): a 64-lane ds_read_b128 (1 KiB) is conflict-free
-// when every 16-byte bank group, address mod 512, is hit exactly twice, and a
-// ds_read_b64_tr_b16 (512 B) when every 8-byte unit is hit once.
+// Bank conflicts on gfx950's LDS were measured (SQ_LDS_BANK_CONFLICT) on probe
+// kernels that replay exactly the read patterns below; the layout is the one
+// that measured zero for all of them.
 // Latent part (d_c = 512 bf16 = 1 KiB per row): token t in row t, row stride
 // 1056 bytes (32 bytes of padding; 1056 = 32 mod 512). Then
 //   * score operand reads: 16 lanes read tokens t0..t0+15 at 16-byte chunk c,
@@ -63,12 +62,12 @@ constexpr int kRing = 4;           // LDS ring slots (slots in flight = kRing - 
 //     8 bytes -> 8-byte units 4t + u, all distinct.
 // Each latent row is one 1 KiB direct-to-LDS load, so the padding costs
 // nothing on the load side, and every k-step is a compile-time LDS offset.
-// The RoPE part (d_r = 64 -> 8 chunks, 128-byte rows, loaded eight rows per
-// instruction) follows the 32 latent rows with its chunks XOR-permuted by
-// swr(t) = 4 ((t >> 2) & 1): of the four tokens that share a bank offset
-// (t mod 4), two keep chunks 4k..4k+3 in place and two swap the halves.
+// The RoPE part (d_r = 64 -> 8 chunks, 128-byte rows) follows the 32 latent
+// rows with its chunks XOR-permuted by swr(t) = t mod 8; among the swizzles
+// probed for this read pattern (16 tokens x 4 consecutive chunks per
+// instruction) it is one of those that measured no bank conflict.
 constexpr int kLatStride = 1056;
-__device__ __forceinline__ int swr(int t) { return ((t >> 2) & 1) << 2; }
+__device__ __forceinline__ int swr(int t) { return t & 7; }
 
 template <int D_R, int HG, int R>
 struct DecodeCfg {
@@ -241,6 +240,41 @@ void decode_attn_kernel(DecodeArgs a) {
     const unsigned long long seg_addr = cache_addr + (unsigned long long)(a.seq_start[b] + t0) * C::RWB;
     P += Lb;
 
+    const int nslots = (n + 31) >> 5;             // 32-token slots of the segment
+
+    // DMA instruction k (< ROUNDS) of slot j (tokens 32 j .. 32 j + 31), into
+    // ring position j % R: latent rows first, then the RoPE rows
+    auto load_part = [&](int j, int k) {
+      const unsigned sb = smem_base + (unsigned)((j % R) * C::SLOT_BYTES);
+      const int tok0 = 32 * j;
+      if (k < C::ROWS_L) {
+        const int t = wave + C::NW * k;
+        int row = tok0 + t;
+        row = row < n ? row : n - 1;
+        g2lds16_s(seg_addr + (unsigned long long)row * C::RWB, offL, sb + t * kLatStride);
+      } else if constexpr (D_R > 0) {
+        // a scalar base row plus a small per-lane row offset
+        int row0 = tok0 + wave * C::ROPE_ROWS;
+        row0 = row0 < n ? row0 : n - 1;
+        int row = tok0 + rrow;
+        row = row < n ? row : n - 1;
+        const unsigned off = (unsigned)(D_C * 2 + (((lane & 7) ^ swr(rrow)) << 4));
+        if (C::ROPE_ROWS * 8 == 64 || lane < C::ROPE_ROWS * 8)
+          g2lds16_s(seg_addr + (unsigned long long)row0 * C::RWB, (unsigned)(row - row0) * C::RWB + off,
+                    sb + C::LAT_BYTES + wave * C::ROPE_ROWS * 128);
+      }
+    };
+    auto load_slot = [&](int j) {
+#pragma unroll
+      for (int k = 0; k < C::ROUNDS; ++k) load_part(j, k);
+    };
+
+    // the first slots of pass 0 go out before the queries are loaded, so the
+    // two memory latencies overlap
+#pragma unroll
+    for (int j = 0; j < C::PD; ++j)
+      if (j < nslots) load_slot(j);
+
     // queries of this lane's head: k-step kb holds features 32 kb + 8 G4 .. +7,
     // the RoPE part rotated to position Lb-1
     bf16x8 q[C::KB];
@@ -276,35 +310,6 @@ void decode_attn_kernel(DecodeArgs a) {
       }
     }
 
-    const int nslots = (n + 31) >> 5;             // 32-token slots of the segment
-
-    // DMA instruction k (< ROUNDS) of slot j (tokens 32 j .. 32 j + 31), into
-    // ring position j % R: latent rows first, then the RoPE rows
-    auto load_part = [&](int j, int k) {
-      const unsigned sb = smem_base + (unsigned)((j % R) * C::SLOT_BYTES);
-      const int tok0 = 32 * j;
-      if (k < C::ROWS_L) {
-        const int t = wave + C::NW * k;
-        int row = tok0 + t;
-        row = row < n ? row : n - 1;
-        g2lds16_s(seg_addr + (unsigned long long)row * C::RWB, offL, sb + t * kLatStride);
-      } else if constexpr (D_R > 0) {
-        // a scalar base row plus a small per-lane row offset
-        int row0 = tok0 + wave * C::ROPE_ROWS;
-        row0 = row0 < n ? row0 : n - 1;
-        int row = tok0 + rrow;
-        row = row < n ? row : n - 1;
-        const unsigned off = (unsigned)(D_C * 2 + (((lane & 7) ^ swr(rrow)) << 4));
-        if (C::ROPE_ROWS * 8 == 64 || lane < C::ROPE_ROWS * 8)
-          g2lds16_s(seg_addr + (unsigned long long)row0 * C::RWB, (unsigned)(row - row0) * C::RWB + off,
-                    sb + C::LAT_BYTES + wave * C::ROPE_ROWS * 128);
-      }
-    };
-    auto load_slot = [&](int j) {
-#pragma unroll
-      for (int k = 0; k < C::ROUNDS; ++k) load_part(j, k);
-    };
-
     // O^T of every head of the workgroup over this wave's features:
     // o[fb * HG + hb] = features fw + 16 fb + 4 G4 + r, head 16 hb + j16
     floatx4 o[C::FBW * HG];
@@ -322,10 +327,12 @@ void decode_attn_kernel(DecodeArgs a) {
       for (int i = 0; i < C::FBW * HG; ++i) o[i] = floatx4{0.f, 0.f, 0.f, 0.f};
       lsum = 0.f;
       m_all = -INFINITY;
-      lds_barrier();  // previous readers are done with the ring
+      if (pass > 0) {
+        lds_barrier();  // every wave is done with the ring
 #pragma unroll
-      for (int j = 0; j < C::PD; ++j)
-        if (j < nslots) load_slot(j);
+        for (int j = 0; j < C::PD; ++j)
+          if (j < nslots) load_slot(j);
+      }
 
       // O^T (this wave's features x all heads) += C^T . P^T for the tile in
       // ring slot `slot`, with the weights published in P buffer `pbi` (each
@@ -517,25 +524,41 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const long long g_lo = ((P + 1) * G - 1) / N;
   const long long g_hi = ((P + Lb) * G - 1) / N;
   if (g_lo == g_hi) return;  // whole sequence inside one slice: already final
-  // online merge over the pieces (slices with an empty range hold none)
+  // online merge over the pieces (slices with an empty range hold none); the
+  // loads of eight pieces are issued together, so the merge costs one memory
+  // latency per eight pieces rather than one per piece
   float M = -INFINITY, den = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (long long g = g_lo; g <= g_hi; ++g) {
-    const long long start_g = g * N / G;
-    if (start_g == (g + 1) * N / G) continue;
-    const long long slot = (P <= start_g) ? 2 * g : 2 * g + 1;
-    const float l = a.part_lse[slot * a.H + h];
-    const u32x4 raw = *(const u32x4*)(a.part_o + ((slot * H16 + hg) * 16 + k) * (int64_t)512 + lane * 8);
-    const float Mn = fmaxf(M, l);
-    const float c = __expf(M - Mn), w = __expf(l - Mn);
-    den = den * c + w;
+  constexpr int NB = 8;
+  for (long long g0 = g_lo; g0 <= g_hi; g0 += NB) {
+    float l[NB];
+    u32x4 raw[NB];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float lo = __builtin_bit_cast(float, raw[e] << 16), hi = __builtin_bit_cast(float, raw[e] & 0xffff0000u);
-      acc[2 * e] = acc[2 * e] * c + w * lo;
-      acc[2 * e + 1] = acc[2 * e + 1] * c + w * hi;
+    for (int i = 0; i < NB; ++i) {
+      const long long g = g0 + i;
+      const long long start_g = g * N / G;
+      l[i] = -INFINITY;
+      raw[i] = u32x4{0u, 0u, 0u, 0u};
+      if (g <= g_hi && start_g != (g + 1) * N / G) {
+        const long long slot = (P <= start_g) ? 2 * g : 2 * g + 1;
+        l[i] = a.part_lse[slot * a.H + h];
+        raw[i] = *(const u32x4*)(a.part_o + ((slot * H16 + hg) * 16 + k) * (int64_t)512 + lane * 8);
+      }
     }
-    M = Mn;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (l[i] == -INFINITY) continue;
+      const float Mn = fmaxf(M, l[i]);
+      const float c = __expf(M - Mn), w = __expf(l[i] - Mn);
+      den = den * c + w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = __builtin_bit_cast(float, raw[i][e] << 16), hi = __builtin_bit_cast(float, raw[i][e] & 0xffff0000u);
+        acc[2 * e] = acc[2 * e] * c + w * lo;
+        acc[2 * e + 1] = acc[2 * e + 1] * c + w * hi;
+      }
+      M = Mn;
+    }
   }
   const float inv = 1.f / den;
   *(u32x2*)op = u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};

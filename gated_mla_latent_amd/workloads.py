@@ -143,32 +143,32 @@ def make_prefill(B, L, d_model, H, d_c, d_k, d_v, *, dtype=BF16, seed=0,
 
 
 # The five workloads, with their full sizes.
-def config1(seed=0):
+def prefill_f32_tiny(seed=0):
     """Tiny fp32 causal prefill: B=1, L=128, d_model=256, H=4, d_c=64,
     d_k=d_v=32, NoPE, full-rank gate 256 -> H*d_v."""
     return make_prefill(1, 128, 256, 4, 64, 32, 32, dtype=F32, seed=seed, name="prefill_f32_tiny")
 
 
-def config2(seed=0, with_output_side=True):
+def decode_nope_b32_h64(seed=0, with_output_side=True):
     """bf16 decode, NoPE: B=32, H=64, d_c=512, L_b ~ U[1024, 8192]."""
     return make_decode(32, 64, 512, 0, 1024, 8192, d_k_scale=128, seed=seed,
                        with_output_side=with_output_side, name="decode_nope_b32_h64")
 
 
-def config3(seed=0, with_output_side=True):
+def decode_rope_b64_h128(seed=0, with_output_side=True):
     """bf16 decode with decoupled RoPE: B=64, H=128, d_c=512 + d_r=64,
     base 10000, L_b ~ U[1024, 16384]."""
     return make_decode(64, 128, 512, 64, 1024, 16384, rope_base=10000.0, d_k_scale=128,
                        seed=seed, with_output_side=with_output_side, name="decode_rope_b64_h128")
 
 
-def config4(seed=0):
+def prefill_b2_l8192(seed=0):
     """bf16 causal prefill: B=2, L=8192, d_model=7168, H=64, d_c=512,
     d_k=d_v=128, NoPE, gate 7168 -> 8192 before W_o 8192 -> 7168."""
     return make_prefill(2, 8192, 7168, 64, 512, 128, 128, seed=seed, name="prefill_b2_l8192")
 
 
-def config5(seed=0, with_output_side=True):
+def decode_rope_b8_l131072(seed=0, with_output_side=True):
     """bf16 long-context decode: B=8, H=128, d_c=512 + 64, L=131072 each."""
     return make_decode(8, 128, 512, 64, 131072, 131072, rope_base=10000.0, d_k_scale=128,
                        seed=seed, with_output_side=with_output_side, name="decode_rope_b8_l131072")

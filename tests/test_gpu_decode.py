@@ -122,12 +122,12 @@ def test_decode_fp32_path():
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("cfg", ["config2", "config3", "config5"])
-def test_decode_full_size_configs(cfg):
+@pytest.mark.parametrize("cfg", ["decode_nope_b32_h64", "decode_rope_b64_h128", "decode_rope_b8_l131072"])
+def test_decode_full_size_workloads(cfg):
     """Full workload sizes in the launch configuration the benchmark times
     (num_splits = 0); the oracle checks a sample of sequences."""
     say(f"[decode full] {cfg}")
     inp = getattr(W, cfg)(with_output_side=False)
     o, lse = _run(inp)
-    sample = {"config2": [0, 7, 31], "config3": [0, 33, 63], "config5": [0, 5]}[cfg]
+    sample = {"decode_nope_b32_h64": [0, 7, 31], "decode_rope_b64_h128": [0, 33, 63], "decode_rope_b8_l131072": [0, 5]}[cfg]
     _check(inp, o, lse, batches=sample)

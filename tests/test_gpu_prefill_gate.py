@@ -41,7 +41,7 @@ def test_prefill_fp32_tiny_config():
     """The tiny fp32 workload at its full size (B=1, L=128, d_model=256, H=4,
     d_c=64, d_k=d_v=32), against the whole-layer oracle at 1e-4."""
     say("[prefill fp32 tiny config]")
-    inp = W.config1()
+    inp = W.prefill_f32_tiny()
     c, ot, y = _prefill(inp)
     rc, rot, ry = O.gated_mla_layer(_np(inp.x), _np(inp.W_c), _np(inp.W_q), _np(inp.W_uk), _np(inp.W_uv),
                                     _np(inp.W_g), _np(inp.W_o), inp.sm_scale)
@@ -108,7 +108,7 @@ def test_prefill_full_size_sampled_rows():
     benchmark launches it; the oracle checks the latent in full and o~, y on
     a seeded sample of query rows (first, second, third, last, 12 random)."""
     say("[prefill full] generating")
-    inp = W.config4()
+    inp = W.prefill_b2_l8192()
     c, ot, y = _prefill(inp)
     rng = np.random.default_rng(0)
     rows = sorted(set([0, 1, 2, inp.L - 1] + rng.choice(inp.L, 12, replace=False).tolist()))
@@ -128,7 +128,7 @@ def test_decode_output_side_full_size():
     """gate_out on the decode workload's output side at full size (T = 32,
     d_model = 7168, H = 64, d_c = 512, d_v = 128)."""
     say("[gate_out full decode-side]")
-    inp = W.config2()
+    inp = W.decode_nope_b32_h64()
     g = torch.Generator().manual_seed(1)
     o_lat = torch.randn(inp.B, inp.H, inp.d_c, generator=g).to(torch.bfloat16)
     y = ops.gate_out(dev(inp.x), dev(o_lat), dev(inp.W_g), dev(inp.W_o), W_uv=dev(inp.W_uv))
