@@ -15,9 +15,9 @@
 //  * gemm_tile: LDS-tiled (BN x BM x 64 tiles, 2 stages, direct-to-LDS
 //    16-byte loads, XOR-swizzled rows) for token counts >= 65.
 //  * gemm_skinny: M <= 64 (decode-step projections). Weight-streaming bound:
-//    each workgroup owns 32 output columns, its 4 waves split K, fragments go
-//    straight from global memory to VGPRs (64 contiguous bytes per lane, with
-//    K permuted identically on both operands), partial sums meet in LDS.
+//    each workgroup owns 32 output columns, its 4 waves split K and stream
+//    their chunks through private LDS rings (several chunks in flight per
+//    wave, no barrier in the loop), partial sums meet in LDS.
 #include "common.h"
 #include "kernels.h"
 
@@ -150,62 +150,114 @@ void gemm_tile_kernel(GemmArgs g) {
 }
 
 // ----------------------------------------------------------------------------
+// Skinny GEMM (M <= 64): pure weight streaming. A workgroup owns 32 output
+// columns and all M rows; its 4 waves split K into 64-wide chunks (wave w
+// takes chunks w, w + 4, ...). Each wave streams its chunks HBM -> LDS
+// through a private ring of NBUF buffers with 1 KiB direct-to-LDS loads
+// (4 KiB of weights + 32 MT rows of A per chunk), so up to NBUF chunks per
+// wave are in flight and no barrier is needed until the final reduction.
+// Rows are 128 bytes; the 16-byte piece p of row r is stored at piece
+// p ^ ((r >> 2) & 7), which makes the fragment reads (32 rows at one piece
+// per half-wave) hit 32 distinct bank groups.
+template <int MT>
+struct SkinnyCfg {
+  static constexpr int NBUF = MT == 1 ? 4 : 3;
+  static constexpr int W_BYTES = 32 * 128;           // 32 weight rows x 64 K
+  static constexpr int A_BYTES = MT * 32 * 128;      // 32 MT rows of A x 64 K
+  static constexpr int BUF_BYTES = W_BYTES + A_BYTES;
+  static constexpr int WAVE_BYTES = NBUF * BUF_BYTES;
+  static constexpr int RPC = (W_BYTES + A_BYTES) / 1024;  // DMA instructions per chunk
+  static constexpr int LDS_BYTES = 4 * WAVE_BYTES;
+  static_assert(LDS_BYTES <= 163840, "LDS budget");
+  static_assert(LDS_BYTES >= 4 * MT * 16 * 64 * 4, "reduction fits in the ring");
+  static_assert((NBUF - 1) * RPC < 64, "vmcnt range");
+};
+
+template <int RPC, int MAXP>
+__device__ __forceinline__ void skinny_wait(int pending) {
+  if constexpr (MAXP >= 3) { if (pending >= 3) { wait_vmcnt<3 * RPC>(); return; } }
+  if constexpr (MAXP >= 2) { if (pending >= 2) { wait_vmcnt<2 * RPC>(); return; } }
+  if constexpr (MAXP >= 1) { if (pending >= 1) { wait_vmcnt<RPC>(); return; } }
+  wait_vmcnt<0>();
+}
+
 template <int MT, int EPI>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
-  __shared__ float red[4][MT][16][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  using C = SkinnyCfg<MT>;
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  LDS_AS char* smem = (LDS_AS char*)smem_raw;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n0 = blockIdx.x * 32;
   const int batch = blockIdx.y;
   const bf16* A = g.A + batch * g.sA;
   const bf16* W = g.W + batch * g.sW;
   bf16* Cp = g.C + batch * g.sC;
   const bf16* Op = (EPI == EPI_GATE) ? g.O + batch * g.sO : nullptr;
+  LDS_AS char* ring = smem + wave * C::WAVE_BYTES;
+  const unsigned ring_addr = (unsigned)(uintptr_t)ring;
 
-  int wr = n0 + (lane & 31);
-  wr = wr < g.N ? wr : g.N - 1;
-  const bf16* wrow = W + (int64_t)wr * g.ldw + 32 * (lane >> 5);
-  const bf16* arow[MT];
+  // DMA: instruction q of a 32-row tile moves rows 8q .. 8q + 7; lane l
+  // writes physical piece l % 8 of row 8q + l / 8, i.e. logical piece
+  // (l % 8) ^ ((row >> 2) & 7). Rows past the end re-read the last row.
+  const int lr = lane >> 3;
+  auto piece_off = [&](int row) { return ((lane & 7) ^ ((row >> 2) & 7)) * 16; };
+  const int chunks = g.K / 64;
+  auto issue = [&](int b, int j) {
+    const unsigned dst = ring_addr + b * C::BUF_BYTES;
 #pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    int ar = t * 32 + (lane & 31);
-    ar = ar < g.M ? ar : g.M - 1;
-    arow[t] = A + (int64_t)ar * g.lda + 32 * (lane >> 5);
-  }
+    for (int q = 0; q < 4; ++q) {
+      int row = n0 + 8 * q + lr;
+      row = row < g.N ? row : g.N - 1;
+      const unsigned long long base = (unsigned long long)(uintptr_t)(W + (int64_t)j * 64);
+      g2lds16_s(base, (unsigned)(row * g.ldw * 2 + piece_off(8 * q + lr)), dst + q * 1024);
+    }
+#pragma unroll
+    for (int q = 0; q < 4 * MT; ++q) {
+      int row = 8 * q + lr;
+      row = row < g.M ? row : g.M - 1;
+      const unsigned long long base = (unsigned long long)(uintptr_t)(A + (int64_t)j * 64);
+      g2lds16_s(base, (unsigned)(row * g.lda * 2 + piece_off(8 * q + lr)), dst + C::W_BYTES + q * 1024);
+    }
+  };
+  // fragment read: row r (32 rows per MFMA operand), logical piece p
+  auto frag = [&](const LDS_AS char* tile, int r, int p) -> bf16x8 {
+    return as_bf16x8(lds_read16(tile + r * 128 + ((p ^ ((r >> 2) & 7)) << 4)));
+  };
 
   floatx16 acc[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = floatx16{};
-
-  const int chunks = g.K / 64;
-  u32x4 wv[2][4], av[2][MT][4];
-  auto fetch = [&](int buf, int j) {
+  const int nmy = (chunks - wave + 3) / 4;  // this wave's chunks: wave, wave + 4, ...
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) wv[buf][kk] = *(const u32x4*)(wrow + 64 * j + 8 * kk);
+  for (int b = 0; b < C::NBUF; ++b)
+    if (b < nmy) issue(b, wave + 4 * b);
+  const int r32 = lane & 31, hk = lane >> 5;
+  for (int i = 0; i < nmy; ++i) {
+    const int b = i % C::NBUF;
+    int pend = nmy - 1 - i;
+    pend = pend < C::NBUF - 1 ? pend : C::NBUF - 1;
+    skinny_wait<C::RPC, C::NBUF - 1>(pend);
+    const LDS_AS char* wt = ring + b * C::BUF_BYTES;
+    const LDS_AS char* at = wt + C::W_BYTES;
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
+    for (int kk = 0; kk < 4; ++kk) {
+      const bf16x8 wf = frag(wt, r32, 2 * kk + hk);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) av[buf][t][kk] = *(const u32x4*)(arow[t] + 64 * j + 8 * kk);
-  };
-  auto compute = [&](int buf) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int t = 0; t < MT; ++t) acc[t] = mfma32(as_bf16x8(wv[buf][kk]), as_bf16x8(av[buf][t][kk]), acc[t]);
-  };
-  int j = wave;
-  if (j < chunks) fetch(0, j);
-  for (; j < chunks; j += 8) {
-    if (j + 4 < chunks) fetch(1, j + 4);
-    compute(0);
-    if (j + 4 >= chunks) break;
-    if (j + 8 < chunks) fetch(0, j + 8);
-    compute(1);
+      for (int t = 0; t < MT; ++t) acc[t] = mfma32(wf, frag(at, 32 * t + r32, 2 * kk + hk), acc[t]);
+    }
+    if (i + C::NBUF < nmy) {
+      wait_lgkm0();  // this buffer's fragments are in registers before it is refilled
+      issue(b, wave + 4 * (i + C::NBUF));
+    }
   }
 
+  __syncthreads();  // every wave is done with its ring: reuse it for the reduction
+  LDS_AS float* red = (LDS_AS float*)smem;  // [4 waves][MT][16][64]
 #pragma unroll
   for (int t = 0; t < MT; ++t)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) red[wave][t][r][lane] = acc[t][r];
+    for (int r = 0; r < 16; ++r) red[((wave * MT + t) * 16 + r) * 64 + lane] = acc[t][r];
   __syncthreads();
   // wave w finishes register group r4 = w (4 consecutive columns per lane)
 #pragma unroll
@@ -214,12 +266,28 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * wave + e;
-      v[e] = red[0][t][r][lane] + red[1][t][r][lane] + red[2][t][r][lane] + red[3][t][r][lane];
+      v[e] = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) v[e] += red[((w * MT + t) * 16 + r) * 64 + lane];
     }
-    const int m = t * 32 + (lane & 31);
+    const int m = 32 * t + (lane & 31);
     const int n = n0 + 8 * wave + 4 * (lane >> 5);
     store4<EPI>(g, Cp, Op, m, n, v[0], v[1], v[2], v[3]);
   }
+}
+
+template <int MT, int EPI>
+static hipError_t launch_skinny(const GemmArgs& g, hipStream_t st) {
+  using C = SkinnyCfg<MT>;
+  auto kern = gemm_skinny_kernel<MT, EPI>;
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((g.N + 31) / 32, g.batches), dim3(256), C::LDS_BYTES, st, g);
+  return hipGetLastError();
 }
 
 // ----------------------------------------------------------------------------
@@ -241,10 +309,10 @@ static hipError_t launch_tile(const GemmArgs& g, hipStream_t st) {
 template <int EPI>
 static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
   if (g.M <= 64) {
-    const dim3 grid((g.N + 31) / 32, g.batches);
-    if (g.M <= 32) hipLaunchKernelGGL((gemm_skinny_kernel<1, EPI>), grid, dim3(256), 0, st, g);
-    else hipLaunchKernelGGL((gemm_skinny_kernel<2, EPI>), grid, dim3(256), 0, st, g);
-    return hipGetLastError();
+    // the DMA offsets are 32-bit: every row start must be below 4 GiB
+    if ((long long)g.N * g.ldw * 2 >= (1LL << 32) || (long long)g.M * g.lda * 2 >= (1LL << 32))
+      return hipErrorInvalidValue;
+    return g.M <= 32 ? launch_skinny<1, EPI>(g, st) : launch_skinny<2, EPI>(g, st);
   }
   const long long big_tiles = (long long)((g.N + 255) / 256) * ((g.M + 255) / 256) * g.batches;
   if (big_tiles >= 256) return launch_tile<256, 256, EPI>(g, st);
