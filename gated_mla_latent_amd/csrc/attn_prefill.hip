@@ -9,17 +9,27 @@
 // second equation) when the output strides say so.
 //
 // Design (MI355X):
-//  * One workgroup = (b, h, 256 queries); wave w owns 64 queries (two 32-row
-//    MFMA blocks), so every K/V fragment read from LDS feeds two MFMAs.
-//  * K and V tiles of 64 keys stream through a 2-stage LDS ring with 16-byte
-//    direct-to-LDS loads, rows XOR-swizzled on 16-byte chunks.
+//  * One workgroup = (b, h, 256 queries), 8 waves, two per SIMD: wave w owns
+//    32 queries. With O^T (D x 32) and the scores (64 keys x 32) per wave the
+//    registers fit two waves per SIMD, so one wave's softmax arithmetic runs
+//    while the other wave's MFMAs do.
+//  * K and V tiles of 64 keys stream through a 3-stage LDS ring with 1 KiB
+//    direct-to-LDS loads (two tiles in flight), one barrier per tile.
 //  * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16: each lane owns one query and
-//    16 keys, so the softmax max needs one exchange with lane ^ 32.
-//  * O^T += V^T . P^T: P^T is the S^T accumulator (rounded to bf16) and V^T
-//    fragments come from ds_read_b64_tr_b16 transposing reads.
-//  * No rescale of O inside the loop: each query's reference max is fixed at
+//    16 keys per 32-key block, so the first-tile max needs one exchange with
+//    lane ^ 32.
+//  * O^T += V^T . P^T: P^T is the S^T accumulator rounded to bf16, with the
+//    keys of each MFMA k-step taken in the accumulator's own order; V^T
+//    fragments come from ds_read_b64_tr_b16 transposing reads in that order.
+//  * K and V rows are 16-byte-chunk XOR-swizzled, each with its own pattern
+//    (the score reads and the transposing reads need different ones), so
+//    neither read conflicts in LDS.
+//  * Softmax: the scale (log2 e included) is folded into one FMA per score,
+//    exp2(|c| s - |c| m); a negative scale is handled by negating Q on load.
+//    No rescale of O inside the loop: each query's reference max is fixed at
 //    its first key tile; if a later score outgrows it by more than 2^32 the
-//    workgroup redoes the pass once with the true maxima (exact for any input).
+//    workgroup redoes the pass once with the true maxima (exact for any
+//    input).
 //  * Query tiles are issued longest-first (largest t first) to even out the
 //    triangular work.
 #include "common.h"
@@ -27,207 +37,242 @@
 
 namespace gmla {
 
+namespace {
+
 template <int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+struct FaCfg {
+  static constexpr int BQ = 256, BK = 64, NW = 8, NST = 3;
+  static constexpr int CH = D / 8;             // 16-byte chunks per row
+  static constexpr int ROWB = 2 * D;           // bytes per row
+  static constexpr int TILE = BK * ROWB;       // one K (or V) tile
+  static constexpr int STAGE = 2 * TILE;
+  static constexpr int LDS = NST * STAGE;
+  static constexpr int KS = D / 16;            // k-steps of S^T
+  static constexpr int DB = D / 32;            // 32-row blocks of O^T
+  static constexpr int RND = BK * CH / (64 * NW);  // 1 KiB loads per wave per K (or V) tile
+  static_assert(RND >= 1, "at least one load per wave");
+  static_assert(LDS <= 163840, "LDS budget");
+};
+
+// Chunk swizzles (physical chunk = logical chunk ^ f(row)). The K tile is
+// read as 32 rows x one chunk per half-wave, the V tile by transposing reads
+// of 8 rows x 4 chunks. The XORs were picked by measuring the LDS
+// bank-conflict counter on probe kernels that replay exactly these two read
+// patterns for sixteen candidate swizzles: these measured zero conflicts.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) { return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((r >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int swz_v(int r) { return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : (((r >> 1) & 1) << 2); }
+
+template <int MAXP, int PER>
+__device__ __forceinline__ void fa_wait(int pending) {
+  if constexpr (MAXP >= 2) { if (pending >= 2) { wait_vmcnt<2 * PER>(); return; } }
+  if constexpr (MAXP >= 1) { if (pending >= 1) { wait_vmcnt<PER>(); return; } }
+  wait_vmcnt<0>();
+}
+
+}  // namespace
+
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void prefill_attn_kernel(AttnArgs a) {
-  constexpr int BQ = 256, BKEY = 64;
-  constexpr int ROWB = D * 2, CH = D / 8;       // bytes and 16-byte chunks per row
-  constexpr int TILE = BKEY * ROWB;             // one K (or V) tile
-  constexpr int STAGE = 2 * TILE;
-  constexpr int ROUNDS = BKEY * CH / 256;
-  constexpr int KS = D / 16;                    // k-steps of S^T
-  constexpr int DB = D / 32;                    // output blocks of O^T
-  static_assert(CH == 16 || CH == 8, "row of 8 or 16 chunks");
+  using C = FaCfg<D>;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
+  const unsigned smem_base = (unsigned)(uintptr_t)smem;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nqt = (a.L + BQ - 1) / BQ;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nqt = (a.L + C::BQ - 1) / C::BQ;
   const int qt = nqt - 1 - (int)(blockIdx.x % nqt);  // longest first
   const int bh = blockIdx.x / nqt;
   const int b = bh / a.H, h = bh % a.H;
-  const int q0 = qt * BQ;
-  const int wq0 = q0 + 64 * wave;                    // this wave's first query
+  const int q0 = qt * C::BQ;
+  const int wq0 = q0 + 32 * wave;                    // this wave's first query
 
   const bf16* qb = a.q + b * a.sqb + h * a.sqh;
   const bf16* kb = a.k + b * a.skb + h * a.skh;
   const bf16* vb = a.v + b * a.svb + h * a.svh;
   bf16* ob = a.o + b * a.sob + h * a.soh;
 
-  auto swz = [](int row) { return CH == 16 ? (row & 15) : ((row >> 1) & 7); };
+  // softmax constant: |scale| log2 e; a negative scale negates the queries
+  const float cabs = fabsf(a.scale_log2);
+  const unsigned qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 
-  // queries of this wave: Q^T fragments for two 32-query blocks
-  bf16x8 qf[2][KS];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    int t = wq0 + 32 * j + (lane & 31);
+  // this wave's queries as the B operand of S^T: query wq0 + lane % 32,
+  // features 16 kk + 8 (lane / 32) .. + 7
+  bf16x8 qf[C::KS];
+  {
+    int t = wq0 + (lane & 31);
     t = t < a.L ? t : a.L - 1;
     const bf16* qp = qb + (int64_t)t * a.sqt + 8 * (lane >> 5);
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) qf[j][kk] = as_bf16x8(*(const u32x4*)(qp + 16 * kk));
+    for (int kk = 0; kk < C::KS; ++kk) {
+      u32x4 v = *(const u32x4*)(qp + 16 * kk);
+      qf[kk] = as_bf16x8(u32x4{v[0] ^ qsign, v[1] ^ qsign, v[2] ^ qsign, v[3] ^ qsign});
+    }
   }
 
+  // DMA of key tile kt into stage s: 1 KiB load n covers chunks 64 n + lane,
+  // i.e. physical chunk p % CH of row p / CH (logical chunk p % CH ^ swz(row))
   auto load_tile = [&](int s, int kt) {
-    LDS_AS char* kt_l = smem + s * STAGE;
-    LDS_AS char* vt_l = kt_l + TILE;
+    const unsigned kdst = smem_base + s * C::STAGE;
+    const unsigned vdst = kdst + C::TILE;
+    const int t0 = kt * C::BK;
+    const unsigned long long kbase = (unsigned long long)(uintptr_t)(kb + (int64_t)t0 * a.skt);
+    const unsigned long long vbase = (unsigned long long)(uintptr_t)(vb + (int64_t)t0 * a.svt);
 #pragma unroll
-    for (int r = 0; r < ROUNDS; ++r) {
-      const int p = r * 256 + wave * 64 + lane;
-      const int row = p / CH, c = (p % CH) ^ swz(p / CH);
-      int t = kt * BKEY + row;
-      t = t < a.L ? t : a.L - 1;
-      g2lds16(kb + (int64_t)t * a.skt + c * 8, kt_l + (r * 256 + wave * 64) * 16);
-      g2lds16(vb + (int64_t)t * a.svt + c * 8, vt_l + (r * 256 + wave * 64) * 16);
+    for (int r = 0; r < C::RND; ++r) {
+      const int n = r * C::NW + wave;
+      const int p = 64 * n + lane;
+      const int row = p / C::CH, pc = p % C::CH;
+      int rr = t0 + row;
+      rr = (rr < a.L ? rr : a.L - 1) - t0;
+      g2lds16_s(kbase, (unsigned)((rr * a.skt + (pc ^ swz_k<D>(row)) * 8) * 2), kdst + n * 1024);
+      g2lds16_s(vbase, (unsigned)((rr * a.svt + (pc ^ swz_v<D>(row)) * 8) * 2), vdst + n * 1024);
     }
   };
 
-  floatx16 o[2][DB];
-  float m[2] = {-INFINITY, -INFINITY};      // reference max per query (log2 domain)
-  float m_all[2] = {-INFINITY, -INFINITY};  // largest score seen
-  float lsum[2] = {0.f, 0.f};
+  floatx16 o[C::DB];
+  float m = -INFINITY;      // reference max per query (raw score units)
+  float m_all = -INFINITY;  // largest raw score of this lane's keys
+  float lsum = 0.f;
 
-  int last_q = q0 + BQ - 1;
+  int last_q = q0 + C::BQ - 1;
   last_q = last_q < a.L - 1 ? last_q : a.L - 1;
-  const int ntiles = last_q / BKEY + 1;                  // tiles the workgroup needs
-  int my_last = wq0 + 63;
+  const int ntiles = last_q / C::BK + 1;                   // tiles the workgroup needs
+  int my_last = wq0 + 31;
   my_last = my_last < a.L - 1 ? my_last : a.L - 1;
-  const int my_tiles = wq0 < a.L ? my_last / BKEY + 1 : 0;  // tiles this wave needs
+  const int my_tiles = wq0 < a.L ? my_last / C::BK + 1 : 0;  // tiles this wave needs
+  const int tq = wq0 + (lane & 31);                          // this lane's query
 
-  // Pass 0 fixes each query's reference max at its first key tile and never
-  // rescales O inside the loop; if a later score outgrows the reference by
-  // more than 2^32 the workgroup repeats the pass with the true maxima.
+  // P.V operand addressing (transposing reads): see the MFMA layout note at
+  // the O^T product below
+  const int G16 = lane >> 4, jj = lane & 15;
+  const int trow = 4 * (G16 >> 1) + (jj >> 2);
+  const int cpart = 2 * (G16 & 1) + ((jj & 3) >> 1);
+  const int vhalf = (jj & 1) << 3;
+
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-      for (int d = 0; d < DB; ++d) o[j][d] = floatx16{};
-      lsum[j] = 0.f;
-    }
+    for (int d = 0; d < C::DB; ++d) o[d] = floatx16{};
+    lsum = 0.f;
+    m_all = -INFINITY;
     lds_barrier();
-    load_tile(0, 0);
+#pragma unroll
+    for (int j = 0; j < C::NST - 1; ++j)
+      if (j < ntiles) load_tile(j, j);
     for (int it = 0; it < ntiles; ++it) {
-      wait_vmcnt<0>();
+      int pend = ntiles - 1 - it;
+      pend = pend < C::NST - 2 ? pend : C::NST - 2;
+      fa_wait<C::NST - 2, 2 * C::RND>(pend);
       lds_barrier();
-      if (it + 1 < ntiles) load_tile((it + 1) & 1, it + 1);
+      if (it + C::NST - 1 < ntiles) load_tile((it + C::NST - 1) % C::NST, it + C::NST - 1);
       if (it >= my_tiles) continue;
-      const LDS_AS char* kt_l = smem + (it & 1) * STAGE;
-      const LDS_AS char* vt_l = kt_l + TILE;
+      const LDS_AS char* kt_l = smem + (it % C::NST) * C::STAGE;
+      const LDS_AS char* vt_l = kt_l + C::TILE;
 
-      // ---- S^T: 64 keys (2 blocks) x 64 queries (2 blocks) ----
-      floatx16 s[2][2];
+      // ---- S^T: 64 keys (2 blocks of 32) x 32 queries ----
+      floatx16 s[2] = {floatx16{}, floatx16{}};
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) s[i][j] = floatx16{};
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
+      for (int kk = 0; kk < C::KS; ++kk) {
         const int c = 2 * kk + (lane >> 5);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int row = 32 * i + (lane & 31);
-          bf16x8 kf = as_bf16x8(lds_read16(kt_l + row * ROWB + ((c ^ swz(row)) << 4)));
-#pragma unroll
-          for (int j = 0; j < 2; ++j) s[i][j] = mfma32(kf, qf[j][kk], s[i][j]);
+          const bf16x8 kf = as_bf16x8(lds_read16(kt_l + row * C::ROWB + ((c ^ swz_k<D>(row)) << 4)));
+          s[i] = mfma32(kf, qf[kk], s[i]);
         }
       }
-      // ---- softmax weights per query (lane owns query 32j + lane%32) ----
-      const bool diag = (it + 1) * BKEY > wq0;  // some key may lie past some query
-      bf16x8 pb[2][4];
+      // ---- softmax weights (lane owns query tq and keys
+      //      it*64 + 32 i + 8 (r/4) + 4 (lane/32) + r%4) ----
+      const bool diag = it * C::BK + C::BK - 1 > wq0;  // some key may lie past some query
+      float mx = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int tq = wq0 + 32 * j + (lane & 31);
-        float mx = -INFINITY;
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = it * BKEY + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            float z = s[i][j][r] * a.scale_log2;
-            if (diag) z = key <= tq ? z : -INFINITY;
-            s[i][j][r] = z;
-            mx = fmaxf(mx, z);
+        for (int r = 0; r < 16; ++r) {
+          float z = s[i][r];
+          if (diag) {
+            const int key = it * C::BK + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            z = key <= tq ? z : -INFINITY;
           }
-        mx = fmaxf(mx, xor32(mx));
-        m_all[j] = fmaxf(m_all[j], mx);
-        if (m[j] == -INFINITY) m[j] = mx;  // O is still zero for this query
-        const float mref = (m[j] == -INFINITY) ? 0.f : m[j];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          float p[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            p[r] = fast_exp2(s[i][j][r] - mref);
-            lsum[j] += p[r];
-          }
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf)
-            pb[j][2 * i + hf] = as_bf16x8(u32x4{pack_bf16x2(p[8 * hf + 0], p[8 * hf + 1]),
-                                                pack_bf16x2(p[8 * hf + 2], p[8 * hf + 3]),
-                                                pack_bf16x2(p[8 * hf + 4], p[8 * hf + 5]),
-                                                pack_bf16x2(p[8 * hf + 6], p[8 * hf + 7])});
+          s[i][r] = z;
+          mx = fmaxf(mx, z);
         }
+      if (pass == 0 && it == 0) m = fmaxf(mx, xor32(mx));  // key 0 is visible to every query
+      m_all = fmaxf(m_all, mx);
+      const float mc = m * cabs;
+      bf16x8 pb[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          p[r] = fast_exp2(__builtin_fmaf(s[i][r], cabs, -mc));
+          lsum += p[r];
+        }
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+          pb[2 * i + hf] = as_bf16x8(u32x4{pack_bf16x2(p[8 * hf + 0], p[8 * hf + 1]), pack_bf16x2(p[8 * hf + 2], p[8 * hf + 3]),
+                                           pack_bf16x2(p[8 * hf + 4], p[8 * hf + 5]), pack_bf16x2(p[8 * hf + 6], p[8 * hf + 7])});
       }
-      // ---- O^T (D x 64 queries) += V^T . P^T ----
-      {
-        const int G16 = lane >> 4, jj = lane & 15;
-        const int trow = 4 * (G16 >> 1) + (jj >> 2);
-        const int cpart = 2 * (G16 & 1) + ((jj & 3) >> 1);
-        const int half = (jj & 1) << 3;
+      // ---- O^T (D x 32 queries) += V^T . P^T ----
+      // k-step ks uses the accumulator registers 8 (ks % 2) .. + 7 of key
+      // block ks / 2, i.e. keys 16 ks + 8 e' / 4 ... in accumulator order;
+      // the transposing reads fetch V rows in that same order: lane group
+      // G16 of the read supplies rows trow (+8 for the second half) and the
+      // four features of chunk 4 d + cpart, half vhalf.
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int ta = trow + 16 * ks, tb = ta + 8;
-          const LDS_AS char* ra = vt_l + ta * ROWB + half;
-          const LDS_AS char* rb = vt_l + tb * ROWB + half;
-          const int sa = swz(ta), sb = swz(tb);
+      for (int ks = 0; ks < 4; ++ks) {
+        const int ta = trow + 16 * ks, tb = ta + 8;
+        const LDS_AS char* ra = vt_l + ta * C::ROWB + vhalf;
+        const LDS_AS char* rb = vt_l + tb * C::ROWB + vhalf;
+        const int sa = swz_v<D>(ta), sb = swz_v<D>(tb);
 #pragma unroll
-          for (int d = 0; d < DB; ++d) {
-            const int c = 4 * d + cpart;
-            u32x2 lo = lds_read_tr16(ra + ((c ^ sa) << 4));
-            u32x2 hi = lds_read_tr16(rb + ((c ^ sb) << 4));
-            bf16x8 vf = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-            for (int j = 0; j < 2; ++j) o[j][d] = mfma32(vf, pb[j][ks], o[j][d]);
-          }
+        for (int d = 0; d < C::DB; ++d) {
+          const int c = 4 * d + cpart;
+          const u32x2 lo = lds_read_tr16(ra + ((c ^ sa) << 4));
+          const u32x2 hi = lds_read_tr16(rb + ((c ^ sb) << 4));
+          o[d] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[ks], o[d]);
         }
       }
     }
-    bool redo = false;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) redo |= (m[j] != -INFINITY) && (m_all[j] > m[j] + 32.0f);
+    const float mall = fmaxf(m_all, xor32(m_all));
+    const bool redo = (m != -INFINITY) && ((mall - m) * cabs > 32.0f);
     if (!__syncthreads_or(redo)) break;
-    m[0] = m_all[0];
-    m[1] = m_all[1];
+    m = mall;
   }
 
   // ---- write o~ ----
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const float l = lsum[j] + xor32(lsum[j]);
-    const int tq = wq0 + 32 * j + (lane & 31);
-    if (tq >= a.L) continue;
+  const float l = lsum + xor32(lsum);
+  if (tq < a.L) {
     const float inv = 1.0f / l;
     bf16* op = ob + (int64_t)tq * a.sot + 4 * (lane >> 5);
 #pragma unroll
-    for (int d = 0; d < DB; ++d)
+    for (int d = 0; d < C::DB; ++d)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4)
-        *(u32x2*)(op + 32 * d + 8 * r4) = u32x2{pack_bf16x2(o[j][d][4 * r4] * inv, o[j][d][4 * r4 + 1] * inv),
-                                                pack_bf16x2(o[j][d][4 * r4 + 2] * inv, o[j][d][4 * r4 + 3] * inv)};
+        *(u32x2*)(op + 32 * d + 8 * r4) = u32x2{pack_bf16x2(o[d][4 * r4] * inv, o[d][4 * r4 + 1] * inv),
+                                                pack_bf16x2(o[d][4 * r4 + 2] * inv, o[d][4 * r4 + 3] * inv)};
   }
 }
 
 template <int D>
 static hipError_t launch_d(const AttnArgs& a, hipStream_t st) {
-  constexpr int LDS = 2 * 2 * 64 * D * 2;
+  using C = FaCfg<D>;
   auto kern = prefill_attn_kernel<D>;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  const int nqt = (a.L + 255) / 256;
-  hipLaunchKernelGGL(kern, dim3(nqt * a.B * a.H), dim3(256), LDS, st, a);
+  // the loads use 32-bit offsets from a per-tile scalar base
+  if ((long long)C::BK * a.skt * 2 >= (1LL << 31) || (long long)C::BK * a.svt * 2 >= (1LL << 31))
+    return hipErrorInvalidValue;
+  const int nqt = (a.L + C::BQ - 1) / C::BQ;
+  hipLaunchKernelGGL(kern, dim3(nqt * a.B * a.H), dim3(64 * C::NW), C::LDS, st, a);
   return hipGetLastError();
 }
 
