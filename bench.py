@@ -13,9 +13,11 @@ A step is one pass of the hot path over one batch of synthetic input:
 Inputs are resident in HBM before timing starts; several copies of every
 input that is read in the step rotate so that the 256 MB Infinity Cache
 cannot serve a step from the previous one. The library is called through
-its C ABI (argument tuples marshalled once). Per-kernel device times come
-from the library's event trace, recorded on the launch stream around every
-kernel during the timed steps.
+its C ABI (argument tuples marshalled once). ms_per_step comes from events
+around the timed steps alone; per-kernel device times come from a second
+pass over as many steps with the library's event trace on (hipEvents
+recorded on the launch stream around every kernel), since those events add
+work to the stream themselves.
 
 Prints one JSON line (rank 0). The fp64 CPU oracle is timed on a bounded
 sample of the same workload on the host cores (cpu_baseline).
@@ -337,7 +339,33 @@ def main():
         step(i)
     torch.cuda.synchronize()
     trace = not args.no_trace
+    # timed region 1: the steps alone (this gives ms_per_step and value)
+    log(f"[bench] timing {args.steps} steps")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"[bench] {ms_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us/step)")
+
+    # timed region 2: the same steps again with the library's launch trace on
+    # (hipEvents recorded on the launch stream around every kernel); the
+    # events add work to the stream, so the step time is taken from region 1
+    kern = {}
     if trace:
+        ops.trace_begin(16 * args.steps + 64)
+        for i in range(args.steps):
+            step(args.warmup + args.steps + i)
+        torch.cuda.synchronize()
+        ops.trace_end()
+        for k in ops.trace_kernels():
+            n, ms = ops.trace_summary(k)
+            kern[k] = {"launches_per_step": n / args.steps, "avg_us": ms * 1e3}
         ops.trace_reset()
         ops.trace_begin(16 * args.steps + 64)
     log(f"[bench] timing {args.steps} steps")

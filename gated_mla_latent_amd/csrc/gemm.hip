@@ -13,7 +13,7 @@
 //
 // Two kernels:
 //  * gemm_tile: LDS-tiled (BN x BM x 64 tiles, 2 stages, direct-to-LDS
-//    16-byte loads, XOR-swizzled rows) for token counts >= 65.
+//    16-byte loads, XOR-swizzled rows, 8 waves) for token counts >= 65.
 //  * gemm_skinny: M <= 64 (decode-step projections). Weight-streaming bound:
 //    each workgroup owns 32 output columns, its 4 waves split K and stream
 //    their chunks through private LDS rings (several chunks in flight per
@@ -26,6 +26,8 @@ namespace gmla {
 namespace {
 
 __device__ __forceinline__ float sigmoidf_fast(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+constexpr int EPI_LDS_MAX = 163840;
 
 // Store 4 consecutive columns (n .. n+3) of row m, applying the epilogue.
 template <int EPI>
@@ -47,17 +49,22 @@ __device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
 }  // namespace
 
 // ----------------------------------------------------------------------------
+// 8 waves, two per SIMD (a wave held up issuing its share of the next
+// stage's loads leaves its SIMD to the other); wave (wn, wm) of a 2 x 4 grid
+// owns BN/2 x BM/4 of the output tile.
 template <int BN, int BM, int EPI>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void gemm_tile_kernel(GemmArgs g) {
   constexpr int BK = 64;
-  constexpr int TN = BN / 64, TM = BM / 64;
+  constexpr int TN = BN / 64, TM = BM / 128;
   constexpr int W_BYTES = BN * BK * 2, A_BYTES = BM * BK * 2, STAGE = W_BYTES + A_BYTES;
-  constexpr int W_ROUNDS = BN * 8 / 256, A_ROUNDS = BM * 8 / 256;
+  constexpr int W_ROUNDS = BN * 8 / 512, A_ROUNDS = BM * 8 / 512;
+  static_assert(TM >= 1 && W_ROUNDS >= 1 && A_ROUNDS >= 1, "tile too small for 8 waves");
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave & 1, wm = wave >> 1;
   const int tiles_n = (g.N + BN - 1) / BN, tiles_m = (g.M + BM - 1) / BM;
   const int total = tiles_n * tiles_m;
@@ -84,19 +91,19 @@ void gemm_tile_kernel(GemmArgs g) {
     LDS_AS char* at = wt + W_BYTES;
 #pragma unroll
     for (int r = 0; r < W_ROUNDS; ++r) {
-      const int p = r * 256 + wave * 64 + lane;
+      const int p = r * 512 + wave * 64 + lane;
       const int row = p >> 3, c = (p & 7) ^ swz8(row);
       int gr = n0 + row;
       gr = gr < g.N ? gr : g.N - 1;
-      g2lds16(W + (int64_t)gr * g.ldw + k0 + c * 8, wt + (r * 256 + wave * 64) * 16);
+      g2lds16(W + (int64_t)gr * g.ldw + k0 + c * 8, wt + (r * 512 + wave * 64) * 16);
     }
 #pragma unroll
     for (int r = 0; r < A_ROUNDS; ++r) {
-      const int p = r * 256 + wave * 64 + lane;
+      const int p = r * 512 + wave * 64 + lane;
       const int row = p >> 3, c = (p & 7) ^ swz8(row);
       int gr = m0 + row;
       gr = gr < g.M ? gr : g.M - 1;
-      g2lds16(A + (int64_t)gr * g.lda + k0 + c * 8, at + (r * 256 + wave * 64) * 16);
+      g2lds16(A + (int64_t)gr * g.lda + k0 + c * 8, at + (r * 512 + wave * 64) * 16);
     }
   };
 
@@ -125,7 +132,7 @@ void gemm_tile_kernel(GemmArgs g) {
       }
 #pragma unroll
       for (int j = 0; j < TM; ++j) {
-        const int row = wm * (BM / 2) + j * 32 + (lane & 31);
+        const int row = wm * (BM / 4) + j * 32 + (lane & 31);
         af[j] = as_bf16x8(lds_read16(at + row * 128 + ((c ^ swz8(row)) << 4)));
       }
 #pragma unroll
@@ -135,18 +142,60 @@ void gemm_tile_kernel(GemmArgs g) {
     }
   }
 
+  // Epilogue through LDS, one column half (BN/2) at a time: the waves that
+  // own the half write their fp32 accumulators as [BM][BN/2] rows (padded by
+  // 16 bytes), then every thread takes 8 consecutive columns of a row, applies
+  // the epilogue and stores 16 contiguous bytes, so C (and O) move in whole
+  // cache lines instead of 16-byte pieces of 32 rows.
+  constexpr int HN = BN / 2, RS = HN * 4 + 16;  // half width, row stride in bytes
+  static_assert(BM * RS <= EPI_LDS_MAX, "epilogue tile fits in LDS");
+  LDS_AS float* ct = (LDS_AS float*)smem;
+  // 16-byte row segments need 16-byte aligned row starts
+  const bool vec16 = g.ldc % 8 == 0 && g.sC % 8 == 0 && (EPI != EPI_GATE || (g.ldo % 8 == 0 && g.sO % 8 == 0));
 #pragma unroll
-  for (int i = 0; i < TN; ++i)
+  for (int half = 0; half < 2; ++half) {
+    lds_barrier();  // the ring (or the previous half) is free
+    if (wn == half) {
 #pragma unroll
-    for (int j = 0; j < TM; ++j) {
-      const int m = m0 + wm * (BM / 2) + j * 32 + (lane & 31);
+      for (int i = 0; i < TN; ++i)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int n = n0 + wn * (BN / 2) + i * 32 + 8 * r4 + 4 * (lane >> 5);
-        store4<EPI>(g, Cp, Op, m, n, acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2],
-                    acc[i][j][4 * r4 + 3]);
+        for (int j = 0; j < TM; ++j) {
+          const int ml = wm * (BM / 4) + j * 32 + (lane & 31);
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int nl = i * 32 + 8 * r4 + 4 * (lane >> 5);
+            *(LDS_AS floatx4*)((LDS_AS char*)ct + ml * RS + nl * 4) =
+                floatx4{acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
+          }
+        }
+    }
+    lds_barrier();
+    constexpr int ITEMS = BM * HN / 8;  // 8 columns per item
+#pragma unroll
+    for (int it = tid; it < ITEMS; it += 512) {
+      const int ml = it / (HN / 8), nl = (it % (HN / 8)) * 8;
+      const int m = m0 + ml, n = n0 + half * HN + nl;
+      if (m >= g.M || n >= g.N) continue;
+      const floatx4 v0 = *(const LDS_AS floatx4*)((const LDS_AS char*)ct + ml * RS + nl * 4);
+      const floatx4 v1 = *(const LDS_AS floatx4*)((const LDS_AS char*)ct + ml * RS + nl * 4 + 16);
+      float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      if (vec16 && n + 8 <= g.N) {
+        if constexpr (EPI == EPI_GATE) {
+          const u32x4 ov = *(const u32x4*)(Op + (int64_t)m * g.ldo + n);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[2 * e] = sigmoidf_fast(v[2 * e]) * bf16_bits_to_f32((unsigned short)(ov[e] & 0xffff));
+            v[2 * e + 1] = sigmoidf_fast(v[2 * e + 1]) * bf16_bits_to_f32((unsigned short)(ov[e] >> 16));
+          }
+        }
+        *(u32x4*)(Cp + (int64_t)m * g.ldc + n) =
+            u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+      } else {
+        store4<EPI>(g, Cp, Op, m, n, v[0], v[1], v[2], v[3]);  // N is a multiple of 4
+        store4<EPI>(g, Cp, Op, m, n + 4, v[4], v[5], v[6], v[7]);
       }
     }
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -293,7 +342,8 @@ static hipError_t launch_skinny(const GemmArgs& g, hipStream_t st) {
 // ----------------------------------------------------------------------------
 template <int BN, int BM, int EPI>
 static hipError_t launch_tile(const GemmArgs& g, hipStream_t st) {
-  constexpr int LDS = 2 * (BN + BM) * 64 * 2;
+  constexpr int RING = 2 * (BN + BM) * 64 * 2, EPIL = BM * ((BN / 2) * 4 + 16);
+  constexpr int LDS = RING > EPIL ? RING : EPIL;
   auto kern = gemm_tile_kernel<BN, BM, EPI>;
   static bool attr = false;
   if (!attr) {
@@ -302,7 +352,7 @@ static hipError_t launch_tile(const GemmArgs& g, hipStream_t st) {
     attr = true;
   }
   const int tiles = ((g.N + BN - 1) / BN) * ((g.M + BM - 1) / BM);
-  hipLaunchKernelGGL(kern, dim3(tiles, g.batches), dim3(256), LDS, st, g);
+  hipLaunchKernelGGL(kern, dim3(tiles, g.batches), dim3(512), LDS, st, g);
   return hipGetLastError();
 }
 
