@@ -367,28 +367,6 @@ def main():
             n, ms = ops.trace_summary(k)
             kern[k] = {"launches_per_step": n / args.steps, "avg_us": ms * 1e3}
         ops.trace_reset()
-        ops.trace_begin(16 * args.steps + 64)
-    log(f"[bench] timing {args.steps} steps")
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    if trace:
-        ops.trace_end()
-    ms_step = ev0.elapsed_time(ev1) / args.steps
-    log(f"[bench] {ms_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us/step)")
-
-    kern = {}
-    if trace:
-        for k in ops.trace_kernels():
-            n, ms = ops.trace_summary(k)
-            kern[k] = {"launches_per_step": n / args.steps, "avg_us": ms * 1e3}
-        ops.trace_reset()
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,

@@ -272,8 +272,7 @@ static hipError_t launch_d(const AttnArgs& a, hipStream_t st) {
   if ((long long)C::BK * a.skt * 2 >= (1LL << 31) || (long long)C::BK * a.svt * 2 >= (1LL << 31))
     return hipErrorInvalidValue;
   const int nqt = (a.L + C::BQ - 1) / C::BQ;
-  hipLaunchKernelGGL(kern, dim3(nqt * a.B * a.H), dim3(64 * C::NW), C::LDS, st, a);
-  return hipGetLastError();
+  return launch(kern, dim3(nqt * a.B * a.H), dim3(64 * C::NW), C::LDS, st, a);
 }
 
 hipError_t launch_prefill_attn_bf16(const AttnArgs& a, hipStream_t st) {

@@ -578,8 +578,7 @@ static hipError_t launch_variant(const DecodeArgs& a, hipStream_t st) {
     attr_set = true;
   }
   const int chunks = (a.H + 16 * HG - 1) / (16 * HG);
-  hipLaunchKernelGGL(kern, dim3(a.G * chunks), dim3(C::NW * 64), C::LDS_BYTES, st, a);
-  return hipGetLastError();
+  return launch(kern, dim3(a.G * chunks), dim3(C::NW * 64), C::LDS_BYTES, st, a);
 }
 
 int decode_head_chunks(int H) { return H <= 32 ? 1 : (H + 63) / 64; }
@@ -598,8 +597,7 @@ hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st) {
   if (a.d_c != 512) return hipErrorInvalidValue;
   const long long blocks = (long long)a.B * ((a.H + 15) / 16) * 4;
   if (blocks > 2147483647LL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
-  return hipGetLastError();
+  return launch(decode_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
 }
 
 // Only the d_c = 512 latent (the width every supported workload uses) is

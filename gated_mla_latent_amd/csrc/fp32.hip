@@ -58,8 +58,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args g) {
 hipError_t launch_gemm_f32(const GemmF32Args& g, hipStream_t st) {
   if (g.M <= 0 || g.N <= 0 || g.batches <= 0) return hipSuccess;
   const dim3 grid((g.N + 63) / 64, (g.M + 63) / 64, g.batches);
-  hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, st, g);
-  return hipGetLastError();
+  return launch(gemm_f32_kernel, grid, dim3(256), 0, st, g);
 }
 
 // --------------------------------------------------------------------------
@@ -167,14 +166,12 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeF32Args a) {
 
 hipError_t launch_prefill_attn_f32(const AttnF32Args& a, hipStream_t st) {
   if (a.Dk > kMaxDk || a.Dv > kMaxDv) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(prefill_attn_f32_kernel, dim3(a.B * a.H * a.L), dim3(256), 0, st, a);
-  return hipGetLastError();
+  return launch(prefill_attn_f32_kernel, dim3(a.B * a.H * a.L), dim3(256), 0, st, a);
 }
 
 hipError_t launch_decode_f32(const DecodeF32Args& a, hipStream_t st) {
   if (a.d_c + a.d_r > kMaxDk || a.d_c > kMaxDv) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(decode_f32_kernel, dim3(a.B * a.H), dim3(256), 0, st, a);
-  return hipGetLastError();
+  return launch(decode_f32_kernel, dim3(a.B * a.H), dim3(256), 0, st, a);
 }
 
 }  // namespace gmla

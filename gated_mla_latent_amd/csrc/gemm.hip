@@ -335,8 +335,7 @@ static hipError_t launch_skinny(const GemmArgs& g, hipStream_t st) {
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipLaunchKernelGGL(kern, dim3((g.N + 31) / 32, g.batches), dim3(256), C::LDS_BYTES, st, g);
-  return hipGetLastError();
+  return launch(kern, dim3((g.N + 31) / 32, g.batches), dim3(256), C::LDS_BYTES, st, g);
 }
 
 // ----------------------------------------------------------------------------
@@ -352,8 +351,7 @@ static hipError_t launch_tile(const GemmArgs& g, hipStream_t st) {
     attr = true;
   }
   const int tiles = ((g.N + BN - 1) / BN) * ((g.M + BM - 1) / BM);
-  hipLaunchKernelGGL(kern, dim3(tiles, g.batches), dim3(512), LDS, st, g);
-  return hipGetLastError();
+  return launch(kern, dim3(tiles, g.batches), dim3(512), LDS, st, g);
 }
 
 template <int EPI>

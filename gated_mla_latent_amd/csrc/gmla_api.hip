@@ -12,6 +12,9 @@
 
 #include "kernels.h"
 
+namespace gmla {
+thread_local LaunchEvents* g_launch_events = nullptr;
+}
 using namespace gmla;
 
 namespace {
@@ -38,7 +41,7 @@ size_t esize(gmla_dtype_t dt) { return dt == GMLA_F32 ? 4 : 2; }
 // ---------------------------------------------------------------- trace
 struct TraceRec {
   const char* name;
-  hipEvent_t start, stop;
+  LaunchEvents ev;
 };
 std::mutex g_tr_mu;
 bool g_tr_on = false;
@@ -46,18 +49,20 @@ std::vector<TraceRec> g_tr;
 int g_tr_used = 0;
 std::string g_tr_names;
 
-int trace_pre(const char* name, hipStream_t st) {
+// A traced call hands its event pair to launch() (which has the kernel's
+// dispatch record it) through g_launch_events; a call that launched nothing
+// leaves launched == 0 and is left out of the summary.
+int trace_pre(const char* name, hipStream_t) {
   if (!g_tr_on) return -1;
   std::lock_guard<std::mutex> lk(g_tr_mu);
   if (g_tr_used >= (int)g_tr.size()) return -1;
   const int i = g_tr_used++;
   g_tr[i].name = name;
-  hipEventRecord(g_tr[i].start, st);
+  g_tr[i].ev.launched = 0;
+  g_launch_events = &g_tr[i].ev;
   return i;
 }
-void trace_post(int i, hipStream_t st) {
-  if (i >= 0) hipEventRecord(g_tr[i].stop, st);
-}
+void trace_post(int, hipStream_t) { g_launch_events = nullptr; }
 
 template <class F>
 gmla_status_t run(const char* name, hipStream_t st, F&& f) {
@@ -312,8 +317,8 @@ gmla_status_t gmla_trace_begin(int max_launches) {
   REQUIRE(max_launches > 0 && max_launches <= (1 << 20), GMLA_ERR_INVALID_ARG, "max_launches out of range");
   std::lock_guard<std::mutex> lk(g_tr_mu);
   while ((int)g_tr.size() < max_launches) {
-    TraceRec r{nullptr, nullptr, nullptr};
-    if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess)
+    TraceRec r{nullptr, {nullptr, nullptr, 0}};
+    if (hipEventCreate(&r.ev.start) != hipSuccess || hipEventCreate(&r.ev.stop) != hipSuccess)
       return fail(GMLA_ERR_HIP, "hipEventCreate failed");
     g_tr.push_back(r);
   }
@@ -333,10 +338,10 @@ gmla_status_t gmla_trace_summary(const char* name, int* count, double* mean_ms) 
   int n = 0;
   double sum = 0;
   for (int i = 0; i < g_tr_used; ++i) {
-    if (!g_tr[i].name || std::strcmp(g_tr[i].name, name) != 0) continue;
-    if (hipEventSynchronize(g_tr[i].stop) != hipSuccess) return fail(GMLA_ERR_HIP, "hipEventSynchronize failed");
+    if (!g_tr[i].name || std::strcmp(g_tr[i].name, name) != 0 || g_tr[i].ev.launched == 0) continue;
+    if (hipEventSynchronize(g_tr[i].ev.stop) != hipSuccess) return fail(GMLA_ERR_HIP, "hipEventSynchronize failed");
     float ms = 0.f;
-    if (hipEventElapsedTime(&ms, g_tr[i].start, g_tr[i].stop) != hipSuccess)
+    if (hipEventElapsedTime(&ms, g_tr[i].ev.start, g_tr[i].ev.stop) != hipSuccess)
       return fail(GMLA_ERR_HIP, "hipEventElapsedTime failed");
     sum += ms;
     ++n;
@@ -362,12 +367,13 @@ const char* gmla_trace_kernels(void) {
 void gmla_trace_reset(void) {
   std::lock_guard<std::mutex> lk(g_tr_mu);
   for (auto& r : g_tr) {
-    if (r.start) hipEventDestroy(r.start);
-    if (r.stop) hipEventDestroy(r.stop);
+    if (r.ev.start) hipEventDestroy(r.ev.start);
+    if (r.ev.stop) hipEventDestroy(r.ev.stop);
   }
   g_tr.clear();
   g_tr_used = 0;
   g_tr_on = false;
+  g_launch_events = nullptr;
 }
 
 }  // extern "C"

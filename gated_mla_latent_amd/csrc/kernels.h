@@ -1,9 +1,31 @@
 // Internal launch interface between the C-ABI layer and the kernels.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 namespace gmla {
+
+// Every kernel goes out through launch(). While the C-ABI layer traces a
+// call it points g_launch_events at a pair of events, and launch() has the
+// kernel's own dispatch record them (hipExtLaunchKernelGGL), so the pair
+// brackets that kernel alone rather than also the queue work around it.
+struct LaunchEvents {
+  hipEvent_t start, stop;
+  int launched;
+};
+extern thread_local LaunchEvents* g_launch_events;
+
+template <typename K, typename... Args>
+inline hipError_t launch(K kern, dim3 grid, dim3 block, unsigned shmem, hipStream_t st, Args... args) {
+  if (LaunchEvents* ev = g_launch_events) {
+    hipExtLaunchKernelGGL(kern, grid, block, shmem, st, ev->start, ev->stop, 0, args...);
+    ++ev->launched;
+  } else {
+    hipLaunchKernelGGL(kern, grid, block, shmem, st, args...);
+  }
+  return hipGetLastError();
+}
 
 typedef __bf16 bf16;
 
