@@ -30,8 +30,8 @@
 //    its first key tile; if a later score outgrows it by more than 2^32 the
 //    workgroup redoes the pass once with the true maxima (exact for any
 //    input).
-//  * Query tiles are issued longest-first (largest t first) to even out the
-//    triangular work.
+//  * Each workgroup takes two query tiles, the k-th longest and the k-th
+//    shortest, so all workgroups carry the same causal work.
 #include "common.h"
 #include "kernels.h"
 
@@ -83,12 +83,13 @@ void prefill_attn_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // work item = (b, h, pair of query tiles {nqt - 1 - p, p}): a long and a
+  // short causal tile per workgroup, so every workgroup has the same work
   const int nqt = (a.L + C::BQ - 1) / C::BQ;
-  const int qt = nqt - 1 - (int)(blockIdx.x % nqt);  // longest first
-  const int bh = blockIdx.x / nqt;
+  const int npair = (nqt + 1) / 2;
+  const int pair = (int)(blockIdx.x % npair);
+  const int bh = blockIdx.x / npair;
   const int b = bh / a.H, h = bh % a.H;
-  const int q0 = qt * C::BQ;
-  const int wq0 = q0 + 32 * wave;                    // this wave's first query
 
   const bf16* qb = a.q + b * a.sqb + h * a.sqh;
   const bf16* kb = a.k + b * a.skb + h * a.skh;
@@ -99,6 +100,11 @@ void prefill_attn_kernel(AttnArgs a) {
   const float cabs = fabsf(a.scale_log2);
   const unsigned qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 
+  for (int rep = 0; rep < 2; ++rep) {
+  const int qt = rep == 0 ? nqt - 1 - pair : pair;
+  if (rep == 1 && qt == nqt - 1 - pair) break;  // odd tile count: the middle tile alone
+  const int q0 = qt * C::BQ;
+  const int wq0 = q0 + 32 * wave;                    // this wave's first query
   // this wave's queries as the B operand of S^T: query wq0 + lane % 32,
   // features 16 kk + 8 (lane / 32) .. + 7
   bf16x8 qf[C::KS];
@@ -256,6 +262,7 @@ void prefill_attn_kernel(AttnArgs a) {
         *(u32x2*)(op + 32 * d + 8 * r4) = u32x2{pack_bf16x2(o[d][4 * r4] * inv, o[d][4 * r4 + 1] * inv),
                                                 pack_bf16x2(o[d][4 * r4 + 2] * inv, o[d][4 * r4 + 3] * inv)};
   }
+  }
 }
 
 template <int D>
@@ -271,8 +278,8 @@ static hipError_t launch_d(const AttnArgs& a, hipStream_t st) {
   // the loads use 32-bit offsets from a per-tile scalar base
   if ((long long)C::BK * a.skt * 2 >= (1LL << 31) || (long long)C::BK * a.svt * 2 >= (1LL << 31))
     return hipErrorInvalidValue;
-  const int nqt = (a.L + C::BQ - 1) / C::BQ;
-  return launch(kern, dim3(nqt * a.B * a.H), dim3(64 * C::NW), C::LDS, st, a);
+  const int npair = ((a.L + C::BQ - 1) / C::BQ + 1) / 2;
+  return launch(kern, dim3(npair * a.B * a.H), dim3(64 * C::NW), C::LDS, st, a);
 }
 
 hipError_t launch_prefill_attn_bf16(const AttnArgs& a, hipStream_t st) {
