@@ -17,13 +17,16 @@
 //    direct-to-LDS loads (two tiles in flight), one barrier per tile.
 //  * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16: each lane owns one query and
 //    16 keys per 32-key block, so the first-tile max needs one exchange with
-//    lane ^ 32.
-//  * O^T += V^T . P^T: P^T is the S^T accumulator rounded to bf16, with the
-//    keys of each MFMA k-step taken in the accumulator's own order; V^T
-//    fragments come from ds_read_b64_tr_b16 transposing reads in that order.
-//  * K and V rows are 16-byte-chunk XOR-swizzled, each with its own pattern
-//    (the score reads and the transposing reads need different ones), so
-//    neither read conflicts in LDS.
+//    lane ^ 32. The K rows enter the MFMA in an order (bits 2 and 3 of the
+//    key swapped within each 16) that leaves every lane's accumulator
+//    holding runs of 8 consecutive keys.
+//  * O^T += V^T . P^T: P^T is the S^T accumulator rounded to bf16, so each
+//    MFMA k-step covers 16 consecutive keys. V arrives transposed (keys
+//    contiguous, written so by the value reconstruction GEMM), so each V^T
+//    fragment is one plain 16-byte LDS read: transposing LDS reads run at
+//    half the rate and would make LDS, not the MFMAs, the bound.
+//  * K and V^T rows are 16-byte-chunk XOR-swizzled so that neither read
+//    conflicts in LDS.
 //  * Softmax: the scale (log2 e included) is folded into one FMA per score,
 //    exp2(|c| s - |c| m); a negative scale is handled by negating Q on load.
 //    No rescale of O inside the loop: each query's reference max is fixed at
@@ -44,7 +47,7 @@ struct FaCfg {
   static constexpr int BQ = 256, BK = 64, NW = 8, NST = 3;
   static constexpr int CH = D / 8;             // 16-byte chunks per row
   static constexpr int ROWB = 2 * D;           // bytes per row
-  static constexpr int TILE = BK * ROWB;       // one K (or V) tile
+  static constexpr int TILE = BK * ROWB;       // one K tile (64 rows of D), or one V^T tile (D rows of 64)
   static constexpr int STAGE = 2 * TILE;
   static constexpr int LDS = NST * STAGE;
   static constexpr int KS = D / 16;            // k-steps of S^T
@@ -54,15 +57,16 @@ struct FaCfg {
   static_assert(LDS <= 163840, "LDS budget");
 };
 
-// Chunk swizzles (physical chunk = logical chunk ^ f(row)). The K tile is
-// read as 32 rows x one chunk per half-wave, the V tile by transposing reads
-// of 8 rows x 4 chunks. The XORs were picked by measuring the LDS
-// bank-conflict counter on probe kernels that replay exactly these two read
-// patterns for sixteen candidate swizzles: these measured zero conflicts.
+// Chunk swizzles (physical chunk = logical chunk ^ f(row)). The K and V^T
+// tiles are read as 32 rows x one chunk per half-wave. The XORs were picked
+// by measuring the LDS bank-conflict counter on probe kernels that replay
+// this read pattern for sixteen candidate swizzles: these measured zero
+// conflicts.
 template <int D>
 __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((r >> 1) & 7); }
-template <int D>
-__device__ __forceinline__ int swz_v(int r) { return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : (((r >> 1) & 1) << 2); }
+// V^T tiles have 128-byte rows (64 keys) read 32 rows x one chunk per
+// half-wave, the pattern of the D = 64 K tile, so they take its swizzle
+__device__ __forceinline__ int swz_vt(int r) { return (r >> 1) & 7; }
 
 template <int MAXP, int PER>
 __device__ __forceinline__ void fa_wait(int pending) {
@@ -119,14 +123,17 @@ void prefill_attn_kernel(AttnArgs a) {
     }
   }
 
-  // DMA of key tile kt into stage s: 1 KiB load n covers chunks 64 n + lane,
-  // i.e. physical chunk p % CH of row p / CH (logical chunk p % CH ^ swz(row))
+  // DMA of key tile kt into stage s. K: 1 KiB load n covers chunks 64 n +
+  // lane, i.e. physical chunk p % CH of key row p / CH (logical chunk
+  // p % CH ^ swz_k(row)). V^T: load n covers feature rows 8 n .. 8 n + 7,
+  // physical chunk lane % 8 of row 8 n + lane / 8 (logical chunk ^ swz_vt);
+  // the padded V^T rows hold every key of the last tile.
   auto load_tile = [&](int s, int kt) {
     const unsigned kdst = smem_base + s * C::STAGE;
     const unsigned vdst = kdst + C::TILE;
     const int t0 = kt * C::BK;
     const unsigned long long kbase = (unsigned long long)(uintptr_t)(kb + (int64_t)t0 * a.skt);
-    const unsigned long long vbase = (unsigned long long)(uintptr_t)(vb + (int64_t)t0 * a.svt);
+    const unsigned long long vbase = (unsigned long long)(uintptr_t)(vb + t0);
 #pragma unroll
     for (int r = 0; r < C::RND; ++r) {
       const int n = r * C::NW + wave;
@@ -135,7 +142,8 @@ void prefill_attn_kernel(AttnArgs a) {
       int rr = t0 + row;
       rr = (rr < a.L ? rr : a.L - 1) - t0;
       g2lds16_s(kbase, (unsigned)((rr * a.skt + (pc ^ swz_k<D>(row)) * 8) * 2), kdst + n * 1024);
-      g2lds16_s(vbase, (unsigned)((rr * a.svt + (pc ^ swz_v<D>(row)) * 8) * 2), vdst + n * 1024);
+      const int vrow = 8 * n + (lane >> 3);
+      g2lds16_s(vbase, (unsigned)((vrow * a.svj + ((lane & 7) ^ swz_vt(vrow)) * 8) * 2), vdst + n * 1024);
     }
   };
 
@@ -152,12 +160,10 @@ void prefill_attn_kernel(AttnArgs a) {
   const int my_tiles = wq0 < a.L ? my_last / C::BK + 1 : 0;  // tiles this wave needs
   const int tq = wq0 + (lane & 31);                          // this lane's query
 
-  // P.V operand addressing (transposing reads): see the MFMA layout note at
-  // the O^T product below
-  const int G16 = lane >> 4, jj = lane & 15;
-  const int trow = 4 * (G16 >> 1) + (jj >> 2);
-  const int cpart = 2 * (G16 & 1) + ((jj & 3) >> 1);
-  const int vhalf = (jj & 1) << 3;
+  // key row this lane feeds into row lane % 32 of each 32-key S^T block:
+  // bits 2 and 3 swapped, so accumulator register r of lane l holds key
+  // 16 (r / 8) + 8 (l / 32) + r % 8 of the block
+  const int krow = ((lane & 31) & 0x13) | ((lane & 4) << 1) | ((lane & 8) >> 1);
 
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -185,13 +191,13 @@ void prefill_attn_kernel(AttnArgs a) {
         const int c = 2 * kk + (lane >> 5);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          const int row = 32 * i + (lane & 31);
+          const int row = 32 * i + krow;
           const bf16x8 kf = as_bf16x8(lds_read16(kt_l + row * C::ROWB + ((c ^ swz_k<D>(row)) << 4)));
           s[i] = mfma32(kf, qf[kk], s[i]);
         }
       }
       // ---- softmax weights (lane owns query tq and keys
-      //      it*64 + 32 i + 8 (r/4) + 4 (lane/32) + r%4) ----
+      //      it*64 + 32 i + 16 (r/8) + 8 (lane/32) + r%8) ----
       const bool diag = it * C::BK + C::BK - 1 > wq0;  // some key may lie past some query
       float mx = -INFINITY;
 #pragma unroll
@@ -200,7 +206,7 @@ void prefill_attn_kernel(AttnArgs a) {
         for (int r = 0; r < 16; ++r) {
           float z = s[i][r];
           if (diag) {
-            const int key = it * C::BK + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const int key = it * C::BK + 32 * i + 16 * (r >> 3) + 8 * (lane >> 5) + (r & 7);
             z = key <= tq ? z : -INFINITY;
           }
           s[i][r] = z;
@@ -224,23 +230,18 @@ void prefill_attn_kernel(AttnArgs a) {
                                            pack_bf16x2(p[8 * hf + 4], p[8 * hf + 5]), pack_bf16x2(p[8 * hf + 6], p[8 * hf + 7])});
       }
       // ---- O^T (D x 32 queries) += V^T . P^T ----
-      // k-step ks uses the accumulator registers 8 (ks % 2) .. + 7 of key
-      // block ks / 2, i.e. keys 16 ks + 8 e' / 4 ... in accumulator order;
-      // the transposing reads fetch V rows in that same order: lane group
-      // G16 of the read supplies rows trow (+8 for the second half) and the
-      // four features of chunk 4 d + cpart, half vhalf.
+      // k-step ks: P^T operand = accumulator registers 8 (ks % 2) .. + 7 of
+      // key block ks / 2, i.e. keys 16 ks + 8 (lane / 32) + e; the V^T
+      // operand of lane l is feature row 32 d + l % 32 at those same keys,
+      // chunk 2 ks + l / 32 of the row.
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const int ta = trow + 16 * ks, tb = ta + 8;
-        const LDS_AS char* ra = vt_l + ta * C::ROWB + vhalf;
-        const LDS_AS char* rb = vt_l + tb * C::ROWB + vhalf;
-        const int sa = swz_v<D>(ta), sb = swz_v<D>(tb);
+        const int c = 2 * ks + (lane >> 5);
 #pragma unroll
         for (int d = 0; d < C::DB; ++d) {
-          const int c = 4 * d + cpart;
-          const u32x2 lo = lds_read_tr16(ra + ((c ^ sa) << 4));
-          const u32x2 hi = lds_read_tr16(rb + ((c ^ sb) << 4));
-          o[d] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[ks], o[d]);
+          const int row = 32 * d + (lane & 31);
+          const bf16x8 vf = as_bf16x8(lds_read16(vt_l + row * 128 + ((c ^ swz_vt(row)) << 4)));
+          o[d] = mfma32(vf, pb[ks], o[d]);
         }
       }
     }
@@ -276,7 +277,7 @@ static hipError_t launch_d(const AttnArgs& a, hipStream_t st) {
     attr = true;
   }
   // the loads use 32-bit offsets from a per-tile scalar base
-  if ((long long)C::BK * a.skt * 2 >= (1LL << 31) || (long long)C::BK * a.svt * 2 >= (1LL << 31))
+  if ((long long)C::BK * a.skt * 2 >= (1LL << 31) || (long long)D * a.svj * 2 >= (1LL << 31))
     return hipErrorInvalidValue;
   const int npair = ((a.L + C::BQ - 1) / C::BQ + 1) / 2;
   return launch(kern, dim3(npair * a.B * a.H), dim3(64 * C::NW), C::LDS, st, a);

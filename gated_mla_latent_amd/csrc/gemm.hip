@@ -29,11 +29,15 @@ __device__ __forceinline__ float sigmoidf_fast(float x) { return 1.0f / (1.0f + 
 
 constexpr int EPI_LDS_MAX = 163840;
 
+// Columns of C that are written: N, or npad with zeros past N (plain store).
+template <int EPI>
+__device__ __forceinline__ int c_cols(const GemmArgs& g) { return (EPI == EPI_STORE && g.npad > g.N) ? g.npad : g.N; }
+
 // Store 4 consecutive columns (n .. n+3) of row m, applying the epilogue.
 template <int EPI>
 __device__ __forceinline__ void store4(const GemmArgs& g, bf16* C, const bf16* O, int m, int n, float v0, float v1,
                                       float v2, float v3) {
-  if (m >= g.M || n >= g.N) return;
+  if (m >= g.M || n >= c_cols<EPI>(g)) return;
   if constexpr (EPI == EPI_GATE) {
     u32x2 ov = *(const u32x2*)(O + (int64_t)m * g.ldo + n);
     v0 = sigmoidf_fast(v0) * bf16_bits_to_f32((unsigned short)(ov[0] & 0xffff));
@@ -66,7 +70,7 @@ void gemm_tile_kernel(GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave & 1, wm = wave >> 1;
-  const int tiles_n = (g.N + BN - 1) / BN, tiles_m = (g.M + BM - 1) / BM;
+  const int tiles_n = (c_cols<EPI>(g) + BN - 1) / BN, tiles_m = (g.M + BM - 1) / BM;
   const int total = tiles_n * tiles_m;
   int pid = blockIdx.x;
   // XCD-contiguous tile ranges, then grouped rasterisation (8 m-tiles per group)
@@ -171,15 +175,20 @@ void gemm_tile_kernel(GemmArgs g) {
     }
     lds_barrier();
     constexpr int ITEMS = BM * HN / 8;  // 8 columns per item
+    const int ncols = c_cols<EPI>(g);
 #pragma unroll
     for (int it = tid; it < ITEMS; it += 512) {
       const int ml = it / (HN / 8), nl = (it % (HN / 8)) * 8;
       const int m = m0 + ml, n = n0 + half * HN + nl;
-      if (m >= g.M || n >= g.N) continue;
+      if (m >= g.M || n >= ncols) continue;
       const floatx4 v0 = *(const LDS_AS floatx4*)((const LDS_AS char*)ct + ml * RS + nl * 4);
       const floatx4 v1 = *(const LDS_AS floatx4*)((const LDS_AS char*)ct + ml * RS + nl * 4 + 16);
       float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-      if (vec16 && n + 8 <= g.N) {
+      if (n + 8 > g.N) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = n + e < g.N ? v[e] : 0.f;  // padding columns
+      }
+      if (vec16 && n + 8 <= ncols) {
         if constexpr (EPI == EPI_GATE) {
           const u32x4 ov = *(const u32x4*)(Op + (int64_t)m * g.ldo + n);
 #pragma unroll
@@ -191,7 +200,7 @@ void gemm_tile_kernel(GemmArgs g) {
         *(u32x4*)(Cp + (int64_t)m * g.ldc + n) =
             u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
       } else {
-        store4<EPI>(g, Cp, Op, m, n, v[0], v[1], v[2], v[3]);  // N is a multiple of 4
+        store4<EPI>(g, Cp, Op, m, n, v[0], v[1], v[2], v[3]);  // the written width is a multiple of 4
         store4<EPI>(g, Cp, Op, m, n + 4, v[4], v[5], v[6], v[7]);
       }
     }
@@ -350,13 +359,14 @@ static hipError_t launch_tile(const GemmArgs& g, hipStream_t st) {
     if (e != hipSuccess) return e;
     attr = true;
   }
-  const int tiles = ((g.N + BN - 1) / BN) * ((g.M + BM - 1) / BM);
+  const int ncols = (EPI == EPI_STORE && g.npad > g.N) ? g.npad : g.N;
+  const int tiles = ((ncols + BN - 1) / BN) * ((g.M + BM - 1) / BM);
   return launch(kern, dim3(tiles, g.batches), dim3(512), LDS, st, g);
 }
 
 template <int EPI>
 static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
-  if (g.M <= 64) {
+  if (g.M <= 64 && !(EPI == EPI_STORE && g.npad > g.N)) {
     // the DMA offsets are 32-bit: every row start must be below 4 GiB
     if ((long long)g.N * g.ldw * 2 >= (1LL << 32) || (long long)g.M * g.lda * 2 >= (1LL << 32))
       return hipErrorInvalidValue;
@@ -369,7 +379,8 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t st) {
   if (g.M <= 0 || g.N <= 0 || g.batches <= 0) return hipSuccess;
-  if (g.K % 64 != 0 || g.N % 4 != 0) return hipErrorInvalidValue;
+  if (g.npad > g.N && (g.epi != EPI_STORE || g.npad % 4 != 0)) return hipErrorInvalidValue;
+  if (g.K % 64 != 0 || (g.npad > g.N ? g.npad : g.N) % 4 != 0) return hipErrorInvalidValue;
   return g.epi == EPI_GATE ? launch_epi<EPI_GATE>(g, st) : launch_epi<EPI_STORE>(g, st);
 }
 

@@ -127,11 +127,16 @@ const char* gmla_last_error(void) { return g_err.c_str(); }
 int gmla_version(void) { return 10000; }
 
 // ============================================================ prefill
+// bf16 keeps V transposed per (sequence, head): [B][H d_v][Lp], keys
+// contiguous, rows padded with zeros to Lp = L rounded up to 64 (one key tile)
+static size_t prefill_vt_ld(int L) { return ((size_t)L + 63) / 64 * 64; }
+
 size_t gmla_prefill_workspace_size(int B, int L, int H, int d_k, int d_v, gmla_dtype_t dtype) {
   if (B <= 0 || L <= 0 || H <= 0 || d_k <= 0 || d_v <= 0) return 0;
   const size_t T = (size_t)B * L;
   const size_t es = esize(dtype);
-  return up256(T * H * d_k * es) * 2 + up256(T * H * d_v * es);
+  const size_t v_elems = dtype == GMLA_BF16 ? (size_t)B * H * d_v * prefill_vt_ld(L) : T * H * d_v;
+  return up256(T * H * d_k * es) * 2 + up256(v_elems * es);
 }
 
 gmla_status_t gmla_prefill(const void* x, const void* W_c, const void* W_q, const void* W_uk, const void* W_uv,
@@ -174,13 +179,20 @@ gmla_status_t gmla_prefill(const void* x, const void* W_c, const void* W_q, cons
     if ((s = run("gemm_latent", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_c, d_model, latent_out, d_c, T, d_c, d_model), st); }))) return s;
     if ((s = run("gemm_query", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_q, d_model, q, HK, T, HK, d_model), st); }))) return s;
     if ((s = run("gemm_key_recon", st, [&] { return launch_gemm_bf16(gemm(latent_out, d_c, W_uk, d_c, k, HK, T, HK, d_c), st); }))) return s;
-    if ((s = run("gemm_value_recon", st, [&] { return launch_gemm_bf16(gemm(latent_out, d_c, W_uv, d_c, v, HV, T, HV, d_c), st); }))) return s;
+    // V^T per sequence: [H d_v, Lp] = W_UV c^T (the operands swapped), the
+    // columns past L written as zeros
+    const int64_t Lp = (int64_t)prefill_vt_ld(L);
+    if ((s = run("gemm_value_recon", st, [&] {
+           GemmArgs g = gemm(W_uv, d_c, latent_out, d_c, v, Lp, HV, L, d_c);
+           g.batches = B; g.sA = 0; g.sW = (int64_t)L * d_c; g.sC = (int64_t)HV * Lp; g.npad = (int)Lp;
+           return launch_gemm_bf16(g, st);
+         }))) return s;
     AttnArgs a{};
     a.q = (const bf16*)q; a.k = (const bf16*)k; a.v = (const bf16*)v; a.o = (bf16*)o_tilde;
     a.B = B; a.L = L; a.H = H; a.D = d_k;
     a.sqb = (int64_t)L * HK; a.sqt = HK; a.sqh = d_k;
     a.skb = (int64_t)L * HK; a.skt = HK; a.skh = d_k;
-    a.svb = (int64_t)L * HV; a.svt = HV; a.svh = d_v;
+    a.svb = (int64_t)HV * Lp; a.svj = Lp; a.svh = (int64_t)d_v * Lp;
     a.sob = (int64_t)L * HV; a.sot = HV; a.soh = d_v;
     a.scale_log2 = sm_scale * 1.4426950408889634f;
     if ((s = run("prefill_attn", st, [&] { return launch_prefill_attn_bf16(a, st); }))) return s;

@@ -64,16 +64,19 @@ struct GemmArgs {
   int64_t lda, ldw, ldc, ldo;
   int64_t sA, sW, sC, sO;   // batch strides (elements)
   int epi;
+  int npad;                 // EPI_STORE: columns N .. npad - 1 of C are written as zeros (<= N: none)
 };
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t st);
 
 // ---------------------------------------------------------------- prefill attention
 // Causal flash attention, one head per (b, h): q,k,v rows of width D.
-// Element (b, t, h, :) of X lives at X + b*sXb + t*sXt + h*sXh.
+// Element (b, t, h, j) of q, k and o lives at X + b*sXb + t*sXt + h*sXh + j. V is transposed:
+// element (b, key t, h, j) at b svb + h svh + j svj + t, each row (b, h, j)
+// holding at least L rounded up to 64 keys, zeros past L.
 struct AttnArgs {
   const bf16* q; const bf16* k; const bf16* v; bf16* o;
   int B, L, H, D;
-  int64_t sqb, sqt, sqh, skb, skt, skh, svb, svt, svh, sob, sot, soh;
+  int64_t sqb, sqt, sqh, skb, skt, skh, svb, svj, svh, sob, sot, soh;
   float scale_log2;
 };
 hipError_t launch_prefill_attn_bf16(const AttnArgs& a, hipStream_t st);

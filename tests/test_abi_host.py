@@ -77,6 +77,16 @@ def test_decode_workspace_size_formula(L):
     assert L.gmla_decode_workspace_size(0, H, d_c, G, 1) == 0
 
 
+def test_prefill_workspace_size_formula(L):
+    up = lambda n: (n + 255) // 256 * 256
+    for B, Lq, H, d in [(2, 100, 3, 64), (1, 8192, 64, 128), (3, 64, 1, 128)]:
+        T, Lp = B * Lq, (Lq + 63) // 64 * 64
+        # bf16: q and K as [T, H d], V transposed per sequence as [B, H d, Lp]
+        assert L.gmla_prefill_workspace_size(B, Lq, H, d, d, 1) == 2 * up(T * H * d * 2) + up(B * H * d * Lp * 2)
+        assert L.gmla_prefill_workspace_size(B, Lq, H, d, d, 0) == 3 * up(T * H * d * 4)
+    assert L.gmla_prefill_workspace_size(0, 16, 2, 64, 64, 1) == 0
+
+
 def _pre(L, **kw):
     a = dict(x=A, Wc=A, Wq=A, Wuk=A, Wuv=A, lat=A, ot=A, ws=A, wsb=1 << 40, B=1, Lq=16, D=256, H=2, d_c=128, d_k=128,
              d_v=128, scale=0.1, dt=1)
@@ -96,7 +106,7 @@ def test_prefill_argument_checks(L):
     assert _pre(L, d_v=2048, d_k=2048, dt=0) == UNSUPPORTED
     assert _pre(L, wsb=100) == WORKSPACE
     need = L.gmla_prefill_workspace_size(1, 16, 2, 128, 128, 1)
-    assert need == 3 * 16 * 2 * 128 * 2
+    assert need == 2 * 16 * 2 * 128 * 2 + 2 * 128 * 64 * 2  # q, K, and V^T padded to 64 keys
 
 
 def _gate(L, **kw):
