@@ -68,10 +68,9 @@ __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (((r & 3) << 2) 
 // half-wave, the pattern of the D = 64 K tile, so they take its swizzle
 __device__ __forceinline__ int swz_vt(int r) { return (r >> 1) & 7; }
 
-template <int MAXP, int PER>
+template <int PER>
 __device__ __forceinline__ void fa_wait(int pending) {
-  if constexpr (MAXP >= 2) { if (pending >= 2) { wait_vmcnt<2 * PER>(); return; } }
-  if constexpr (MAXP >= 1) { if (pending >= 1) { wait_vmcnt<PER>(); return; } }
+  if (pending >= 1) { wait_vmcnt<PER>(); return; }
   wait_vmcnt<0>();
 }
 
@@ -165,6 +164,25 @@ void prefill_attn_kernel(AttnArgs a) {
   // 16 (r / 8) + 8 (l / 32) + r % 8 of the block
   const int krow = ((lane & 31) & 0x13) | ((lane & 4) << 1) | ((lane & 8) >> 1);
 
+  // O^T (D x 32 queries) += V^T . P^T for the key tile in ring stage `st`.
+  // k-step ks: P^T operand = accumulator registers 8 (ks % 2) .. + 7 of key
+  // block ks / 2, i.e. keys 16 ks + 8 (lane / 32) + e; the V^T operand of
+  // lane l is feature row 32 d + l % 32 at those same keys, chunk
+  // 2 ks + l / 32 of the row.
+  auto pv = [&](int st, const bf16x8* pw) {
+    const LDS_AS char* vt_l = smem + st * C::STAGE + C::TILE;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int c = 2 * ks + (lane >> 5);
+#pragma unroll
+      for (int d = 0; d < C::DB; ++d) {
+        const int row = 32 * d + (lane & 31);
+        const bf16x8 vf = as_bf16x8(lds_read16(vt_l + row * 128 + ((c ^ swz_vt(row)) << 4)));
+        o[d] = mfma32(vf, pw[ks], o[d]);
+      }
+    }
+  };
+
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
     for (int d = 0; d < C::DB; ++d) o[d] = floatx16{};
@@ -172,17 +190,16 @@ void prefill_attn_kernel(AttnArgs a) {
     m_all = -INFINITY;
     lds_barrier();
 #pragma unroll
-    for (int j = 0; j < C::NST - 1; ++j)
+    for (int j = 0; j < 2; ++j)
       if (j < ntiles) load_tile(j, j);
     for (int it = 0; it < ntiles; ++it) {
-      int pend = ntiles - 1 - it;
-      pend = pend < C::NST - 2 ? pend : C::NST - 2;
-      fa_wait<C::NST - 2, 2 * C::RND>(pend);
+      // tile it has landed; tile it + 1 may still be in flight. Stage
+      // (it + 2) % 3 last held tile it - 1, which every wave is done with.
+      fa_wait<2 * C::RND>(ntiles - 1 - it);
       lds_barrier();
-      if (it + C::NST - 1 < ntiles) load_tile((it + C::NST - 1) % C::NST, it + C::NST - 1);
+      if (it + 2 < ntiles) load_tile((it + 2) % C::NST, it + 2);
       if (it >= my_tiles) continue;
       const LDS_AS char* kt_l = smem + (it % C::NST) * C::STAGE;
-      const LDS_AS char* vt_l = kt_l + C::TILE;
 
       // ---- S^T: 64 keys (2 blocks of 32) x 32 queries ----
       floatx16 s[2] = {floatx16{}, floatx16{}};
@@ -199,19 +216,23 @@ void prefill_attn_kernel(AttnArgs a) {
       // ---- softmax weights (lane owns query tq and keys
       //      it*64 + 32 i + 16 (r/8) + 8 (lane/32) + r%8) ----
       const bool diag = it * C::BK + C::BK - 1 > wq0;  // some key may lie past some query
+      if (diag) {
+        // a real branch (the empty asm cannot be speculated): the compiler
+        // would otherwise turn the mask into selects on every tile
+        asm volatile("");
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = it * C::BK + 32 * i + 16 * (r >> 3) + 8 * (lane >> 5) + (r & 7);
+            s[i][r] = key <= tq ? s[i][r] : -INFINITY;
+          }
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float z = s[i][r];
-          if (diag) {
-            const int key = it * C::BK + 32 * i + 16 * (r >> 3) + 8 * (lane >> 5) + (r & 7);
-            z = key <= tq ? z : -INFINITY;
-          }
-          s[i][r] = z;
-          mx = fmaxf(mx, z);
-        }
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[i][r]);
       if (pass == 0 && it == 0) m = fmaxf(mx, xor32(mx));  // key 0 is visible to every query
       m_all = fmaxf(m_all, mx);
       const float mc = m * cabs;
@@ -230,20 +251,7 @@ void prefill_attn_kernel(AttnArgs a) {
                                            pack_bf16x2(p[8 * hf + 4], p[8 * hf + 5]), pack_bf16x2(p[8 * hf + 6], p[8 * hf + 7])});
       }
       // ---- O^T (D x 32 queries) += V^T . P^T ----
-      // k-step ks: P^T operand = accumulator registers 8 (ks % 2) .. + 7 of
-      // key block ks / 2, i.e. keys 16 ks + 8 (lane / 32) + e; the V^T
-      // operand of lane l is feature row 32 d + l % 32 at those same keys,
-      // chunk 2 ks + l / 32 of the row.
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int c = 2 * ks + (lane >> 5);
-#pragma unroll
-        for (int d = 0; d < C::DB; ++d) {
-          const int row = 32 * d + (lane & 31);
-          const bf16x8 vf = as_bf16x8(lds_read16(vt_l + row * 128 + ((c ^ swz_vt(row)) << 4)));
-          o[d] = mfma32(vf, pb[ks], o[d]);
-        }
-      }
+      pv(it % C::NST, pb);
     }
     const float mall = fmaxf(m_all, xor32(m_all));
     const bool redo = (m != -INFINITY) && ((mall - m) * cabs > 32.0f);
