@@ -13,8 +13,9 @@
 //    32 queries. With O^T (D x 32) and the scores (64 keys x 32) per wave the
 //    registers fit two waves per SIMD, so one wave's softmax arithmetic runs
 //    while the other wave's MFMAs do.
-//  * K and V tiles of 64 keys stream through a 3-stage LDS ring with 1 KiB
-//    direct-to-LDS loads (two tiles in flight), one barrier per tile.
+//  * K and V tiles of 64 keys stream through a 4-stage LDS ring with 1 KiB
+//    direct-to-LDS loads: one barrier per two tiles, after which the next
+//    two tiles are loaded into the stages of the previous two.
 //  * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16: each lane owns one query and
 //    16 keys per 32-key block, so the first-tile max needs one exchange with
 //    lane ^ 32. The K rows enter the MFMA in an order (bits 2 and 3 of the
@@ -42,9 +43,15 @@ namespace gmla {
 
 namespace {
 
+// LDS operand fragments read ahead of their MFMA (scheduling barriers keep
+// the order): one LDS latency then hides behind several MFMAs
+constexpr int kPFS = 4;  // k-steps of K fragments (two each) in flight in S^T
+constexpr int kPFV = 4;  // V^T fragments in flight in P.V
+constexpr int kSync = 2;  // key tiles per barrier; the ring holds 2 kSync tiles
+
 template <int D>
 struct FaCfg {
-  static constexpr int BQ = 256, BK = 64, NW = 8, NST = 3;
+  static constexpr int BQ = 256, BK = 64, NW = 8, NST = 2 * kSync;
   static constexpr int CH = D / 8;             // 16-byte chunks per row
   static constexpr int ROWB = 2 * D;           // bytes per row
   static constexpr int TILE = BK * ROWB;       // one K tile (64 rows of D), or one V^T tile (D rows of 64)
@@ -67,12 +74,6 @@ __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (((r & 3) << 2) 
 // V^T tiles have 128-byte rows (64 keys) read 32 rows x one chunk per
 // half-wave, the pattern of the D = 64 K tile, so they take its swizzle
 __device__ __forceinline__ int swz_vt(int r) { return (r >> 1) & 7; }
-
-template <int PER>
-__device__ __forceinline__ void fa_wait(int pending) {
-  if (pending >= 1) { wait_vmcnt<PER>(); return; }
-  wait_vmcnt<0>();
-}
 
 }  // namespace
 
@@ -171,15 +172,22 @@ void prefill_attn_kernel(AttnArgs a) {
   // 2 ks + l / 32 of the row.
   auto pv = [&](int st, const bf16x8* pw) {
     const LDS_AS char* vt_l = smem + st * C::STAGE + C::TILE;
+    constexpr int NF = 4 * C::DB;  // fragment f: k-step f / DB, row block f % DB
+    auto readV = [&](int f) -> bf16x8 {
+      const int c = 2 * (f / C::DB) + (lane >> 5);
+      const int row = 32 * (f % C::DB) + (lane & 31);
+      return as_bf16x8(lds_read16(vt_l + row * 128 + ((c ^ swz_vt(row)) << 4)));
+    };
+    bf16x8 vf[kPFV];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int c = 2 * ks + (lane >> 5);
+    for (int x = 0; x < kPFV; ++x) vf[x] = readV(x);
 #pragma unroll
-      for (int d = 0; d < C::DB; ++d) {
-        const int row = 32 * d + (lane & 31);
-        const bf16x8 vf = as_bf16x8(lds_read16(vt_l + row * 128 + ((c ^ swz_vt(row)) << 4)));
-        o[d] = mfma32(vf, pw[ks], o[d]);
-      }
+    for (int f = 0; f < NF; ++f) {
+      o[f % C::DB] = mfma32(vf[f % kPFV], pw[f / C::DB], o[f % C::DB]);
+      if (f + kPFV < NF) vf[f % kPFV] = readV(f + kPFV);
+      // LDS reads and MFMAs keep their order; the softmax arithmetic (VALU,
+      // transcendental, SALU) may still move in between
+      __builtin_amdgcn_sched_barrier(0x406);
     }
   };
 
@@ -190,27 +198,44 @@ void prefill_attn_kernel(AttnArgs a) {
     m_all = -INFINITY;
     lds_barrier();
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kSync; ++j)
       if (j < ntiles) load_tile(j, j);
     for (int it = 0; it < ntiles; ++it) {
-      // tile it has landed; tile it + 1 may still be in flight. Stage
-      // (it + 2) % 3 last held tile it - 1, which every wave is done with.
-      fa_wait<2 * C::RND>(ntiles - 1 - it);
-      lds_barrier();
-      if (it + 2 < ntiles) load_tile((it + 2) % C::NST, it + 2);
+      if (it % kSync == 0) {
+        // tiles it .. it + kSync - 1 have landed; their successors go into
+        // the stages of the previous kSync tiles, which every wave is done with
+        wait_vmcnt<0>();
+        lds_barrier();
+#pragma unroll
+        for (int j = kSync; j < 2 * kSync; ++j)
+          if (it + j < ntiles) load_tile((it + j) % C::NST, it + j);
+      }
       if (it >= my_tiles) continue;
       const LDS_AS char* kt_l = smem + (it % C::NST) * C::STAGE;
 
       // ---- S^T: 64 keys (2 blocks of 32) x 32 queries ----
       floatx16 s[2] = {floatx16{}, floatx16{}};
-#pragma unroll
-      for (int kk = 0; kk < C::KS; ++kk) {
+      auto readK = [&](int kk, int i) -> bf16x8 {
         const int c = 2 * kk + (lane >> 5);
+        const int row = 32 * i + krow;
+        return as_bf16x8(lds_read16(kt_l + row * C::ROWB + ((c ^ swz_k<D>(row)) << 4)));
+      };
+      {
+        constexpr int PF = kPFS < C::KS ? kPFS : C::KS;
+        bf16x8 kf[PF][2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int row = 32 * i + krow;
-          const bf16x8 kf = as_bf16x8(lds_read16(kt_l + row * C::ROWB + ((c ^ swz_k<D>(row)) << 4)));
-          s[i] = mfma32(kf, qf[kk], s[i]);
+        for (int x = 0; x < PF; ++x)
+#pragma unroll
+          for (int i = 0; i < 2; ++i) kf[x][i] = readK(x, i);
+#pragma unroll
+        for (int kk = 0; kk < C::KS; ++kk) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) s[i] = mfma32(kf[kk % PF][i], qf[kk], s[i]);
+          if (kk + PF < C::KS) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) kf[kk % PF][i] = readK(kk + PF, i);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       // ---- softmax weights (lane owns query tq and keys

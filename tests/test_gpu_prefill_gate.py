@@ -69,6 +69,28 @@ def test_gate_out_with_value_up_projection(T, D, H, d_c, d_v):
     assert e <= BF16_TOL
 
 
+@pytest.mark.parametrize("T,D,HV", [(4133, 4224, 4096), (2144, 4160, 8192)])
+def test_gate_out_large_tiles_sampled_rows(T, D, HV):
+    """gate_out at sizes whose GEMMs take the 256 x 256 tile kernels (at least
+    256 output tiles), with ragged row and column edges and both even and odd
+    counts of 64-wide k-steps; the oracle checks a seeded sample of rows that
+    always holds the first, last and tile-boundary rows."""
+    say(f"[gate_out large tiles] T={T} D={D} H*d_v={HV}")
+    g = torch.Generator().manual_seed(9)
+    x = torch.randn(T, D, generator=g).to(torch.bfloat16)
+    o = torch.randn(T, HV, generator=g).to(torch.bfloat16)
+    W_g = (torch.randn(HV, D, generator=g) / D ** 0.5).to(torch.bfloat16)
+    W_o = (torch.randn(D, HV, generator=g) / HV ** 0.5).to(torch.bfloat16)
+    y = ops.gate_out(dev(x), dev(o), dev(W_g), dev(W_o))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    rows = sorted({0, 1, 255, 256, T // 256 * 256 - 1, T - 2, T - 1} | set(rng.choice(T, 24, replace=False).tolist()))
+    ry = O.gate_out_reference(_np(x)[rows], _np(o)[rows], _np(W_g), _np(W_o))
+    e = rel_err(y[rows].float(), ry)
+    say(f"  rel err y {e:.2e}")
+    assert e <= BF16_TOL
+
+
 def test_gate_out_fp32_with_value_up_projection():
     say("[gate_out fp32]")
     g = torch.Generator().manual_seed(6)
