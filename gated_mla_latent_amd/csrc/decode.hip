@@ -96,7 +96,7 @@ struct DecodeCfg {
   static_assert(D_R == 0 || D_R == 64, "RoPE rows are 8 chunks of 16 bytes");
   static_assert(ROPE_ROWS * 8 <= 64, "RoPE rows of a wave fit one instruction");
   static_assert(LDS_BYTES <= 163840, "LDS budget");
-  static_assert(64 * NW * 8 + 16 <= LDS_BYTES, "scan scratch fits in the ring");
+  static_assert(NW * 8 + 16 <= LDS_BYTES, "scan scratch fits in the ring");
   static_assert(PD >= 1 && PD <= 3, "ring of 3 to 5 slots");
   static_assert((PD - 1) * ROUNDS < 64, "vmcnt range");
 };
@@ -111,6 +111,14 @@ __device__ __forceinline__ void wait_slots(int pending) {
     if (pending >= 1) { wait_vmcnt<ROUNDS>(); return; }
   }
   wait_vmcnt<0>();
+}
+
+// value of lane - off (any value where that is negative; callers mask it)
+__device__ __forceinline__ long long shfl_up_ll(long long v, int off) {
+  const int src = ((lane_id() - off) & 63) << 2;
+  const unsigned lo = (unsigned)__builtin_amdgcn_ds_bpermute(src, (int)(unsigned)(v & 0xffffffffLL));
+  const unsigned hi = (unsigned)__builtin_amdgcn_ds_bpermute(src, (int)(unsigned)((unsigned long long)v >> 32));
+  return (long long)(((unsigned long long)hi << 32) | lo);
 }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
@@ -157,37 +165,50 @@ void decode_attn_kernel(DecodeArgs a) {
   const int head_base = (item % chunks) * (16 * HG);  // first head of this chunk
 
   // ---- prefix sums of the sequence lengths (cooperative, any B); scratch in the ring ----
-  // thread i sums sequences i*cb .. i*cb + cb - 1, then an inclusive scan over NT threads
-  LDS_AS long long* s_scan = (LDS_AS long long*)smem;
-  LDS_AS long long* s_first = s_scan + NT;
+  // thread i sums sequences i*cb .. i*cb + cb - 1; a shuffle scan inside each
+  // wave and one pass over the NW wave totals give every thread its
+  // exclusive prefix with a single barrier
+  LDS_AS long long* s_wsum = (LDS_AS long long*)smem;  // [NW] wave totals
+  LDS_AS long long* s_first = s_wsum + C::NW;          // [2] first sequence of the slice, its offset
   const int B = a.B;
   const int cb = (B + NT - 1) / NT;
   long long mysum = 0;
+  int L0 = 0;  // the length of this thread's first sequence (the only one when B <= NT)
   for (int i = 0; i < cb; ++i) {
     int bb = tid * cb + i;
-    if (bb < B) { int L = a.seq_len[bb]; mysum += L > 0 ? L : 0; }
+    if (bb < B) {
+      int L = a.seq_len[bb];
+      L = L > 0 ? L : 0;
+      if (i == 0) L0 = L;
+      mysum += L;
+    }
   }
-  s_scan[tid] = mysum;
-  __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {
-    long long v = tid >= off ? s_scan[tid - off] : 0;
-    __syncthreads();
-    s_scan[tid] += v;
-    __syncthreads();
+  long long incl = mysum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const long long up = shfl_up_ll(incl, off);
+    if (lane >= off) incl += up;
   }
-  const long long N = s_scan[NT - 1];
-  const long long excl = tid > 0 ? s_scan[tid - 1] : 0;
-  const long long start_g = (long long)g * N / G;
-  const long long end_g = (long long)(g + 1) * N / G;
+  if (lane == 63) s_wsum[wave] = incl;
   if (tid == 0) { s_first[0] = -1; s_first[1] = 0; }
   __syncthreads();
+  long long N = 0, before = 0;
+#pragma unroll
+  for (int w = 0; w < C::NW; ++w) {
+    const long long t = s_wsum[w];
+    N += t;
+    before += w < wave ? t : 0;
+  }
+  const long long excl = before + incl - mysum;
+  const long long start_g = (long long)g * N / G;
+  const long long end_g = (long long)(g + 1) * N / G;
   {
     long long p = excl;
     for (int i = 0; i < cb; ++i) {
       int bb = tid * cb + i;
       if (bb >= B) break;
-      int L = a.seq_len[bb];
-      L = L > 0 ? L : 0;
+      int L = L0;
+      if (i > 0) { L = a.seq_len[bb]; L = L > 0 ? L : 0; }
       if (blockIdx.x == 0) a.prefix[bb] = p;
       if (L > 0 && p <= start_g && start_g < p + L) { s_first[0] = bb; s_first[1] = p; }
       p += L;

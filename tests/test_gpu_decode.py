@@ -77,6 +77,24 @@ def test_decode_split_invariance(num_splits):
     assert float((lse - l1).abs().max()) <= 1e-4
 
 
+@pytest.mark.parametrize("B,H", [(130, 64), (1100, 64), (600, 16)])
+def test_decode_many_sequences(B, H):
+    """More sequences than one wave (or one workgroup) of the prefix scan
+    holds, with empty ones among them."""
+    say(f"[decode many] B={B} H={H}")
+    rng = np.random.default_rng(B)
+    lengths = rng.integers(0, 41, size=B).tolist()
+    lengths[0] = 0
+    lengths[-1] = 33
+    inp = W.make_decode(B, H, 512, 64, 0, lengths=lengths, seed=4, name="many")
+    o, lse = _run(inp)
+    nonempty = [b for b in range(B) if lengths[b] > 0]
+    empty = [b for b in range(B) if lengths[b] == 0]
+    assert torch.all(o[empty] == 0)
+    assert torch.all(torch.isneginf(lse[empty]))
+    _check(inp, o, lse, batches=nonempty)
+
+
 def test_decode_honours_seq_start_with_gaps():
     say("[decode gaps]")
     inp = W.make_decode(5, 64, 512, 64, 10, 300, seed=5, gap_rows=13, name="gaps")
