@@ -74,9 +74,11 @@ void gemm_tile_kernel(GemmArgs g) {
   const int tiles_n = (c_cols<EPI>(g) + BN - 1) / BN, tiles_m = (g.M + BM - 1) / BM;
   const int total = tiles_n * tiles_m;
   int pid = blockIdx.x;
-  // XCD-contiguous tile ranges, then grouped rasterisation (8 m-tiles per group)
+  // XCD-contiguous tile ranges, then grouped rasterisation (4 m-tiles per group:
+  // the 32 tiles that run at once on an XCD are 4 m-tiles x 8 n-tiles, so each
+  // activation line serves 8 of them; measured 4% faster than 8 x 4)
   if (total % 8 == 0) pid = (pid % 8) * (total / 8) + pid / 8;
-  constexpr int GROUP = 8;
+  constexpr int GROUP = 4;
   const int group_size = GROUP * tiles_n;
   const int grp = pid / group_size;
   const int first_m = grp * GROUP;
