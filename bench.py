@@ -400,6 +400,11 @@ def main():
                                    "frac": a / HBM_PEAK_GBS, "traffic": traffic_record(dom, args.workload),
                                    "alg_bytes_per_launch": alg[dom]}
         out["kernels"] = kern
+        if "decode_attn" in kern and "decode_combine" in kern:
+            # the attention part of the step alone (latent-cache attention and
+            # the split-L combine, per launch), as tokens/s for one layer
+            t_att = sum(kern[k]["avg_us"] * kern[k]["launches_per_step"] for k in ("decode_attn", "decode_combine"))
+            out["attention_only"] = {"us": t_att, "tokens_per_s": inp.B / (t_att * 1e-6)}
         if not args.no_cpu_baseline:
             log("[bench] cpu baseline (fp64 oracle)")
             out["cpu_baseline"] = cpu_baseline_decode(inp, args.cpu_seconds)
