@@ -44,6 +44,7 @@ __all__ = [
     "causal_attention",
     "rope_rotate",
     "decode_reference",
+    "decode_prepare_reference",
     "lse_merge",
     "value_up_projection",
     "sigmoid",
@@ -208,6 +209,40 @@ def decode_reference(q_abs, cache, seq_start, seq_len, d_c: int, d_r: int,
         o_lat[b] = o[0]
         lse[b] = l[0]
     return o_lat, lse
+
+
+def decode_prepare_reference(x, W_c, W_kr, W_q, W_qr, W_uk, pos, rope_base: float):
+    """The projections of one decode step around the cached-latent attention
+    ([N03] §5.1 low-rank KV compression, absorption and 题4; §5.2 decoupled
+    RoPE), for the new token x_b of every sequence b at position pos[b]:
+
+        c     = W_c x                       the latent, appended to the cache
+        k^R   = RoPE(W^KR x, pos)           the shared RoPE key, stored rotated
+        q^(h) = W_q^(h) x                   per-head query (d_k wide)
+        q~^(h) = (W_UK^(h))^T q^(h)         absorbed query (d_c wide)
+        q^R(h) = W^QR(h) x                  per-head RoPE query, not rotated here
+                                            (the decode step rotates it)
+
+    x: [B, d_model]; W_c: [d_c, d_model]; W_kr: [d_r, d_model] or None;
+    W_q: [H*d_k, d_model]; W_qr: [H*d_r, d_model] or None;
+    W_uk: [H, d_k, d_c]; pos: [B].
+    Returns (cache_row [B, d_c + d_r], q_abs [B, H, d_c + d_r]).
+    """
+    x = _f64(x)
+    B = x.shape[0]
+    W_uk = _f64(W_uk)
+    H = W_uk.shape[0]
+    c = latent_projection(x, W_c)  # [B, d_c]
+    q = query_projection(x, W_q, H)  # [B, H, d_k]
+    q_t = np.einsum("bhk,hkc->bhc", q, W_uk)  # (W_UK^(h))^T q^(h)
+    if W_kr is None or np.asarray(W_kr).shape[0] == 0:
+        return c, q_t
+    k_r = x @ _f64(W_kr).T  # [B, d_r]
+    if rope_base != 0.0:
+        k_r = rope_rotate(k_r, np.asarray(pos, dtype=np.float64), rope_base)
+    d_r = k_r.shape[-1]
+    q_r = (x @ _f64(W_qr).T).reshape(B, H, d_r)
+    return np.concatenate([c, k_r], axis=1), np.concatenate([q_t, q_r], axis=2)
 
 
 def lse_merge(parts):

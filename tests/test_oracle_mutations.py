@@ -54,8 +54,28 @@ def _reconstruct_swapped(c, W_uk, W_uv):
     return k, np.einsum("...c,hdc->...hd", np.asarray(c, float), np.asarray(W_uv, float)[:, :, ::-1])
 
 
+def _prepare_heads_swapped(x, W_c, W_kr, W_q, W_qr, W_uk, pos, base):
+    # each head's query absorbed with another head's W_UK
+    return _orig_prepare(x, W_c, W_kr, W_q, W_qr, np.asarray(W_uk, float)[::-1], pos, base)
+
+
+def _prepare_pos_off_by_one(x, W_c, W_kr, W_q, W_qr, W_uk, pos, base):
+    # the new RoPE key rotated to the previous position
+    return _orig_prepare(x, W_c, W_kr, W_q, W_qr, W_uk, np.asarray(pos) - 1, base)
+
+
+def _prepare_rotates_query(x, W_c, W_kr, W_q, W_qr, W_uk, pos, base):
+    # the RoPE query rotated here as well as in the decode step
+    row, q = _orig_prepare(x, W_c, W_kr, W_q, W_qr, W_uk, pos, base)
+    d_c = row.shape[1] - (0 if W_kr is None else np.asarray(W_kr).shape[0])
+    q = q.copy()
+    q[..., d_c:] = G.rope_rotate(q[..., d_c:], np.asarray(pos, float)[:, None], base)
+    return row, q
+
+
 _orig_attend = G.attend_rows
 _orig_reconstruct = G.reconstruct_kv
+_orig_prepare = G.decode_prepare_reference
 
 MUTATIONS = [
     ("rope_rotate", _rope_wrong_sign, [P.test_rope_matches_complex_rotation_and_is_relative,
@@ -72,6 +92,14 @@ MUTATIONS = [
      [P.test_decode_equals_last_prefill_row, P.test_value_up_projection_moves_wuv_past_the_weighted_sum]),
     ("reconstruct_kv", _reconstruct_swapped, [P.test_prefill_explicit_equals_absorbed_route,
                                               P.test_whole_layer_matches_scalar_brute_force]),
+    ("decode_prepare_reference", _prepare_heads_swapped,
+     [lambda: P.test_decode_prepare_then_decode_equals_explicit_attention(0),
+      lambda: P.test_decode_prepare_then_decode_equals_explicit_attention(4),
+      P.test_decode_prepare_absorbed_query_matches_scalar_loops]),
+    ("decode_prepare_reference", _prepare_pos_off_by_one,
+     [lambda: P.test_decode_prepare_then_decode_equals_explicit_attention(4)]),
+    ("decode_prepare_reference", _prepare_rotates_query,
+     [lambda: P.test_decode_prepare_then_decode_equals_explicit_attention(4)]),
 ]
 
 

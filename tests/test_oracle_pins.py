@@ -298,6 +298,82 @@ def test_value_up_projection_moves_wuv_past_the_weighted_sum():
     np.testing.assert_allclose(O.value_up_projection(o_lat, W_uv), explicit, atol=1e-12)
 
 
+# ---------------------------------------------------------------- decode-step projections
+def _explicit_rope_decode(x_all, W_c, W_kr, W_q, W_qr, W_uk, W_uv, scale, base):
+    """The newest token of one sequence attending over all of it, with every
+    head's keys [W_UK^(h) c_j ; RoPE(W^KR x_j, j)] and values W_UV^(h) c_j
+    built explicitly (no absorption), the query [W_q^(h) x ; RoPE(W^QR(h) x, t)]
+    at the last position t. Written with plain numpy, not the oracle."""
+    T = x_all.shape[0]
+    H, dk, dc = W_uk.shape
+    dr = W_kr.shape[0]
+    c = x_all @ W_c.T
+    kr = _rope_complex(x_all @ W_kr.T, np.arange(T), base)
+    x = x_all[-1]
+    out = []
+    for h in range(H):
+        q = np.concatenate([W_q[h * dk:(h + 1) * dk] @ x, _rope_complex(W_qr[h * dr:(h + 1) * dr] @ x, T - 1, base)])
+        k = np.concatenate([c @ W_uk[h].T, kr], axis=1)  # [T, dk + dr]
+        z = scale * (k @ q)
+        a = np.exp(z - z.max())
+        a /= a.sum()
+        out.append(a @ (c @ W_uv[h].T))
+    return np.concatenate(out)
+
+
+@pytest.mark.parametrize("dr", [0, 4])
+def test_decode_prepare_then_decode_equals_explicit_attention(dr):
+    """Appending the new token's latent (and rotated RoPE key) and absorbing
+    W_UK into its query, then the latent-cache decode and the value
+    up-projection, give what explicit per-head K/V attention gives."""
+    D, H, dc, dk, dv, Lp, base, scale = 12, 3, 8, 5, 6, 7, 100.0, 0.4
+    x_all = rng.standard_normal((Lp + 1, D))
+    W_c, W_q = rng.standard_normal((dc, D)), rng.standard_normal((H * dk, D))
+    W_uk, W_uv = rng.standard_normal((H, dk, dc)), rng.standard_normal((H, dv, dc))
+    W_kr = rng.standard_normal((dr, D)) if dr else None
+    W_qr = rng.standard_normal((H * dr, D)) if dr else None
+    # earlier tokens' cache rows, written directly from the definition
+    prev = x_all[:Lp] @ W_c.T
+    if dr:
+        prev = np.concatenate([prev, _rope_complex(x_all[:Lp] @ W_kr.T, np.arange(Lp), base)], axis=1)
+    row, q_abs = O.decode_prepare_reference(x_all[Lp:], W_c, W_kr, W_q, W_qr, W_uk, [Lp], base)
+    assert row.shape == (1, dc + dr) and q_abs.shape == (1, H, dc + dr)
+    cache = np.concatenate([prev, row])
+    o_lat, _ = O.decode_reference(q_abs, cache, [0], [Lp + 1], dc, dr, base, scale)
+    o = O.value_up_projection(o_lat, W_uv).reshape(-1)
+    if dr:
+        ref = _explicit_rope_decode(x_all, W_c, W_kr, W_q, W_qr, W_uk, W_uv, scale, base)
+    else:
+        c = x_all @ W_c.T
+        x = x_all[-1]
+        ref = []
+        for h in range(H):
+            z = scale * ((c @ W_uk[h].T) @ (W_q[h * dk:(h + 1) * dk] @ x))
+            a = np.exp(z - z.max())
+            ref.append((a / a.sum()) @ (c @ W_uv[h].T))
+        ref = np.concatenate(ref)
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-11)
+
+
+def test_decode_prepare_absorbed_query_matches_scalar_loops():
+    D, H, dc, dk, dr = 4, 2, 3, 2, 2
+    x = rng.standard_normal((2, D))
+    W_c, W_q = rng.standard_normal((dc, D)), rng.standard_normal((H * dk, D))
+    W_uk, W_kr, W_qr = rng.standard_normal((H, dk, dc)), rng.standard_normal((dr, D)), rng.standard_normal((H * dr, D))
+    row, q_abs = O.decode_prepare_reference(x, W_c, W_kr, W_q, W_qr, W_uk, [3, 9], 0.0)  # base 0: no rotation
+    for b in range(2):
+        for c in range(dc):
+            assert abs(row[b][c] - sum(W_c[c][j] * x[b][j] for j in range(D))) < 1e-12
+        for i in range(dr):
+            assert abs(row[b][dc + i] - sum(W_kr[i][j] * x[b][j] for j in range(D))) < 1e-12
+        for h in range(H):
+            q = [sum(W_q[h * dk + k][j] * x[b][j] for j in range(D)) for k in range(dk)]
+            for c in range(dc):
+                assert abs(q_abs[b][h][c] - sum(W_uk[h][k][c] * q[k] for k in range(dk))) < 1e-12
+            for i in range(dr):
+                assert abs(q_abs[b][h][dc + i] - sum(W_qr[h * dr + i][j] * x[b][j] for j in range(D))) < 1e-12
+
+
 # ---------------------------------------------------------------- brute force
 def _brute_layer(x, W_c, W_q, W_uk, W_uv, W_g, W_o, scale):
     """Scalar loops over every index, math.exp only: one sequence."""
