@@ -6,7 +6,10 @@
 A step is one pass of the hot path over one batch of synthetic input:
   decode_*  : gmla_decode (attention over the latent cache + split combine)
               followed by gmla_gate_out (value up-projection, sigmoid gate,
-              W_o) for the B query tokens;
+              W_o) for the B query tokens; the step's input side,
+              gmla_decode_prepare (latent, RoPE key and query projections,
+              cache append, query absorption, d_k = 128), is timed in a
+              region of its own and reported as decode_prepare;
   prefill   : gmla_prefill (latent, query, K/V reconstruction, causal
               attention) followed by gmla_gate_out over all B*L tokens;
   tiny_fp32 : the same as prefill for the tiny fp32 workload.
@@ -94,6 +97,18 @@ def gate_out_bytes(inp):
     }
 
 
+DECODE_D_K = 128  # per-head query width of the decode workloads' input side
+
+
+def prepare_bytes(inp, d_k=DECODE_D_K):
+    """Algorithmic HBM bytes of gmla_decode_prepare: x and every weight read
+    once, the new cache rows and the absorbed queries written once."""
+    B, D, H, dc, dr = inp.B, inp.d_model, inp.H, inp.d_c, inp.d_r
+    W = dc + dr
+    weights = (dc + dr + H * d_k + H * dr) * D * 2 + H * d_k * dc * 2
+    return B * D * 2 + weights + B * W * 2 + B * H * W * 2
+
+
 def gate_out_flops(inp):
     T, D, H, dv, dc = inp.B, inp.d_model, inp.H, inp.d_v, inp.d_c
     return {"gemm_value_up": 2 * T * H * dv * dc, "gemm_gate": 2 * T * D * H * dv, "gemm_out": 2 * T * D * H * dv}
@@ -126,10 +141,24 @@ def build_decode(args, inp, torch, ops):
     q = inp.q_abs.to(dev)
     seq_start, seq_len = inp.seq_start.to(dev), inp.seq_len.to(dev)
     x = inp.x.to(dev)
+    from gated_mla_latent_amd import workloads
+    stp = workloads.make_decode_step(inp, inp.d_model, DECODE_D_K)
     copies = []
     for i in range(args.copies):
-        copies.append(dict(cache=inp.cache.to(dev), W_uv=inp.W_uv.to(dev), W_g=inp.W_g.to(dev), W_o=inp.W_o.to(dev)))
+        copies.append(dict(cache=inp.cache.to(dev), W_uv=inp.W_uv.to(dev), W_g=inp.W_g.to(dev), W_o=inp.W_o.to(dev),
+                           W_c=stp.W_c.to(dev), W_q=stp.W_q.to(dev), W_uk=stp.W_uk.to(dev),
+                           W_kr=None if stp.W_kr is None else stp.W_kr.to(dev),
+                           W_qr=None if stp.W_qr is None else stp.W_qr.to(dev)))
         log(f"  copy {i} resident")
+    # the input side appends each new row to a [B, d_c + d_r] buffer of its
+    # own (row b, at the sequence's true position seq_len[b]) so that the
+    # timed caches stay as generated
+    x_new = stp.x.to(dev)
+    rows_new = torch.empty((inp.B, inp.d_c + inp.d_r), dtype=torch.bfloat16, device=dev)
+    start_new = (torch.arange(inp.B, dtype=torch.int64) - inp.seq_len.to(torch.int64)).to(dev)
+    q_new = torch.empty((inp.B, inp.H, inp.d_c + inp.d_r), dtype=torch.bfloat16, device=dev)
+    wsp_n = L.gmla_decode_prepare_workspace_size(inp.B, inp.H, inp.d_c, DECODE_D_K, inp.d_r, 1)
+    wsp = torch.empty(wsp_n, dtype=torch.uint8, device=dev)
     o_lat = torch.empty((inp.B, inp.H, inp.d_c), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((inp.B, inp.H), dtype=torch.float32, device=dev)
     y = torch.empty((inp.B, inp.d_model), dtype=torch.bfloat16, device=dev)
@@ -144,11 +173,14 @@ def build_decode(args, inp, torch, ops):
                stream)
         go = (_vp(x), _vp(o_lat), _vp(c["W_uv"]), _vp(c["W_g"]), _vp(c["W_o"]), _vp(y), _vp(wsg), C.c_size_t(wsg_n),
               inp.B, inp.d_model, inp.H, inp.d_c, inp.d_v, 1, stream)
-        calls.append((dec, go))
-    keep = (q, seq_start, seq_len, x, copies, o_lat, lse, y, wsd, wsg)
+        pre = (_vp(x_new), _vp(c["W_c"]), _vp(c["W_kr"]), _vp(c["W_q"]), _vp(c["W_qr"]), _vp(c["W_uk"]),
+               _vp(rows_new), _vp(start_new), _vp(seq_len), _vp(q_new), _vp(wsp), C.c_size_t(wsp_n), inp.B,
+               inp.d_model, inp.H, inp.d_c, DECODE_D_K, inp.d_r, C.c_float(inp.rope_base), 1, stream)
+        calls.append((dec, go, pre))
+    keep = (q, seq_start, seq_len, x, copies, o_lat, lse, y, wsd, wsg, x_new, rows_new, start_new, q_new, wsp)
 
     def step(i):
-        dec, go = calls[i % len(calls)]
+        dec, go, _ = calls[i % len(calls)]
         s = L.gmla_decode(*dec)
         if s:
             raise RuntimeError(L.gmla_last_error().decode())
@@ -156,7 +188,12 @@ def build_decode(args, inp, torch, ops):
         if s:
             raise RuntimeError(L.gmla_last_error().decode())
 
-    return step, keep
+    def prepare(i):
+        s = L.gmla_decode_prepare(*calls[i % len(calls)][2])
+        if s:
+            raise RuntimeError(L.gmla_last_error().decode())
+
+    return step, (keep, prepare)
 
 
 def build_prefill(args, p, torch, ops):
@@ -368,6 +405,31 @@ def main():
             kern[k] = {"launches_per_step": n / args.steps, "avg_us": ms * 1e3}
         ops.trace_reset()
 
+    # timed region 3 (decode): the step's input side alone, then its kernels
+    prep_us, prep_kern = None, {}
+    if is_decode:
+        prepare = keep[1]
+        for i in range(args.warmup):
+            prepare(i)
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(args.steps):
+            prepare(args.warmup + i)
+        ev1.record()
+        torch.cuda.synchronize()
+        prep_us = ev0.elapsed_time(ev1) * 1e3 / args.steps
+        log(f"[bench] decode_prepare {prep_us:.1f} us")
+        if trace:
+            ops.trace_begin(16 * args.steps + 64)
+            for i in range(args.steps):
+                prepare(i)
+            torch.cuda.synchronize()
+            ops.trace_end()
+            for k in ops.trace_kernels():
+                n, ms = ops.trace_summary(k)
+                prep_kern[k] = {"launches_per_step": n / args.steps, "avg_us": ms * 1e3}
+            ops.trace_reset()
+
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "f32" if args.workload == "tiny_fp32" else "bf16",
@@ -405,6 +467,12 @@ def main():
             # the split-L combine, per launch), as tokens/s for one layer
             t_att = sum(kern[k]["avg_us"] * kern[k]["launches_per_step"] for k in ("decode_attn", "decode_combine"))
             out["attention_only"] = {"us": t_att, "tokens_per_s": inp.B / (t_att * 1e-6)}
+        pb = prepare_bytes(inp)
+        out["decode_prepare"] = {"us": prep_us, "alg_bytes": pb, "hbm_gbs": pb / (prep_us * 1e-6) / 1e9,
+                                 "hbm_frac": pb / (prep_us * 1e-6) / 1e9 / HBM_PEAK_GBS, "d_k": DECODE_D_K,
+                                 "kernels": prep_kern,
+                                 "layer_us": ms_step * 1e3 + prep_us,
+                                 "layer_tokens_per_s": inp.B / ((ms_step * 1e3 + prep_us) * 1e-6)}
         if not args.no_cpu_baseline:
             log("[bench] cpu baseline (fp64 oracle)")
             out["cpu_baseline"] = cpu_baseline_decode(inp, args.cpu_seconds)

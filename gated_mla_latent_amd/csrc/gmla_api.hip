@@ -268,6 +268,59 @@ gmla_status_t gmla_decode(const void* q_abs, const void* cache, const int64_t* s
   return ok();
 }
 
+// ============================================================ decode-step projections
+size_t gmla_decode_prepare_workspace_size(int B, int H, int d_c, int d_k, int d_r, gmla_dtype_t dtype) {
+  if (B <= 0 || H <= 0 || d_c <= 0 || d_k <= 0 || d_r < 0 || dtype != GMLA_BF16) return 0;
+  return up256((size_t)B * (d_c + d_r) * 2) + up256((size_t)B * H * d_k * 2) + up256((size_t)B * H * d_r * 2);
+}
+
+gmla_status_t gmla_decode_prepare(const void* x, const void* W_c, const void* W_kr, const void* W_q, const void* W_qr,
+                                  const void* W_uk, void* cache, const int64_t* seq_start, const int32_t* seq_len,
+                                  void* q_abs, void* workspace, size_t workspace_bytes, int B, int d_model, int H,
+                                  int d_c, int d_k, int d_r, float rope_base, gmla_dtype_t dtype, void* stream) {
+  REQUIRE(dtype == GMLA_F32 || dtype == GMLA_BF16, GMLA_ERR_INVALID_ARG, "dtype must be GMLA_F32 or GMLA_BF16");
+  REQUIRE(x && W_c && W_q && W_uk && cache && seq_start && seq_len && q_abs, GMLA_ERR_INVALID_ARG,
+          "null tensor pointer");
+  REQUIRE(B > 0 && d_model > 0 && H > 0 && d_c > 0 && d_k > 0 && d_r >= 0, GMLA_ERR_INVALID_ARG,
+          "sizes must be positive (d_r >= 0)");
+  REQUIRE(d_r == 0 || (W_kr && W_qr), GMLA_ERR_INVALID_ARG, "d_r > 0 needs W_kr and W_qr");
+  REQUIRE(d_r % 2 == 0, GMLA_ERR_INVALID_ARG, "d_r must be even (RoPE pairs)");
+  REQUIRE(std::isfinite(rope_base) && rope_base >= 0.f, GMLA_ERR_INVALID_ARG, "rope_base must be finite and >= 0");
+  REQUIRE(al16(x) && al16(W_c) && (!d_r || (al16(W_kr) && al16(W_qr))) && al16(W_q) && al16(W_uk) && al16(cache) &&
+              al16(seq_start) && al16(seq_len) && al16(q_abs),
+          GMLA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  REQUIRE(dtype == GMLA_BF16, GMLA_ERR_UNSUPPORTED, "decode_prepare is bf16 only");
+  REQUIRE(d_model % 64 == 0 && d_c % 64 == 0 && d_k <= 128 && d_k % 16 == 0 && d_r % 4 == 0, GMLA_ERR_UNSUPPORTED,
+          "bf16 decode_prepare needs d_model % 64 == 0, d_c % 64 == 0, d_k % 16 == 0, d_k <= 128, d_r % 4 == 0");
+  const size_t need = gmla_decode_prepare_workspace_size(B, H, d_c, d_k, d_r, dtype);
+  REQUIRE(workspace && workspace_bytes >= need, GMLA_ERR_WORKSPACE,
+          "decode_prepare workspace needs " + std::to_string(need) + " bytes");
+  REQUIRE(((uintptr_t)workspace & 255u) == 0, GMLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  const int W = d_c + d_r;
+  char* ws = (char*)workspace;
+  bf16* row = (bf16*)ws;
+  bf16* q = (bf16*)(ws + up256((size_t)B * W * 2));
+  bf16* qr = (bf16*)(ws + up256((size_t)B * W * 2) + up256((size_t)B * H * d_k * 2));
+  gmla_status_t s;
+  if ((s = run("gemm_latent", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_c, d_model, row, W, B, d_c, d_model), st); }))) return s;
+  if (d_r > 0 &&
+      (s = run("gemm_rope_key", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_kr, d_model, row + d_c, W, B, d_r, d_model), st); })))
+    return s;
+  if ((s = run("gemm_query", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_q, d_model, q, H * d_k, B, H * d_k, d_model), st); }))) return s;
+  if (d_r > 0 &&
+      (s = run("gemm_rope_query", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_qr, d_model, qr, H * d_r, B, H * d_r, d_model), st); })))
+    return s;
+  PrepareArgs a{};
+  a.row = row; a.q = q; a.q_r = qr; a.W_uk = (const bf16*)W_uk; a.cache = (bf16*)cache;
+  a.seq_start = seq_start; a.seq_len = seq_len; a.q_abs = (bf16*)q_abs;
+  a.B = B; a.H = H; a.d_c = d_c; a.d_k = d_k; a.d_r = d_r;
+  a.rope_base = d_r > 0 ? rope_base : 0.f;
+  if ((s = run("decode_append", st, [&] { return launch_decode_append(a, st); }))) return s;
+  if ((s = run("decode_absorb", st, [&] { return launch_decode_absorb(a, st); }))) return s;
+  return ok();
+}
+
 // ============================================================ gate + output
 size_t gmla_gate_out_workspace_size(int T, int H, int d_v, int with_value_up, gmla_dtype_t dtype) {
   if (T <= 0 || H <= 0 || d_v <= 0) return 0;

@@ -44,6 +44,22 @@ struct DecodeArgs {
   float scale_log2;         // sm_scale * log2(e)
   float rope_base;          // 0 = no rotation of the query's RoPE part
 };
+// decode-step projections after the input GEMMs: cache append, query absorb
+struct PrepareArgs {
+  const bf16* row;          // [B, d_c + d_r] latent and unrotated k^R of the new tokens
+  const bf16* q;            // [B, H, d_k] per-head queries
+  const bf16* q_r;          // [B, H, d_r] per-head RoPE queries (unrotated)
+  const bf16* W_uk;         // [H, d_k, d_c]
+  bf16* cache;              // [rows, d_c + d_r], row seq_start[b] + seq_len[b] is written
+  const int64_t* seq_start; // [B]
+  const int32_t* seq_len;   // [B] (the new token's position)
+  bf16* q_abs;              // [B, H, d_c + d_r] out
+  int B, H, d_c, d_k, d_r;
+  float rope_base;          // 0: no rotation
+};
+hipError_t launch_decode_append(const PrepareArgs& a, hipStream_t st);
+hipError_t launch_decode_absorb(const PrepareArgs& a, hipStream_t st);
+
 hipError_t launch_decode_attn(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st);
 bool decode_bf16_supported(int d_c, int d_r);

@@ -51,6 +51,10 @@ def lib():
     L.gmla_decode_workspace_size.restype = sz
     L.gmla_decode.argtypes = [vp] * 6 + [vp, sz] + [i32] * 4 + [f32, f32, i32, i32, vp]
     L.gmla_decode.restype = i32
+    L.gmla_decode_prepare_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.gmla_decode_prepare_workspace_size.restype = sz
+    L.gmla_decode_prepare.argtypes = [vp] * 10 + [vp, sz] + [i32] * 6 + [f32, i32, vp]
+    L.gmla_decode_prepare.restype = i32
     L.gmla_gate_out_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     L.gmla_gate_out_workspace_size.restype = sz
     L.gmla_gate_out.argtypes = [vp] * 6 + [vp, sz] + [i32] * 5 + [i32, vp]
@@ -151,6 +155,30 @@ def decode(q_abs, cache, seq_start, seq_len, d_c: int, d_r: int, rope_base: floa
                              _vp(workspace), wsb, B, H, d_c, d_r, float(rope_base), float(sm_scale), int(num_splits),
                              dt, _stream()))
     return o_lat, lse
+
+
+def decode_prepare(x, W_c, W_kr, W_q, W_qr, W_uk, cache, seq_start, seq_len, rope_base: float, q_abs=None,
+                   workspace=None):
+    """x [B, d_model] -> q_abs [B, H, d_c+d_r]; writes the new cache row
+    [W_c x ; RoPE(W_kr x, seq_len[b])] at cache[seq_start[b] + seq_len[b]].
+    W_kr and W_qr are None when d_r == 0. seq_len is not changed."""
+    _dev(x, W_c, W_kr, W_q, W_qr, W_uk, cache, seq_start, seq_len, q_abs, workspace)
+    if seq_start.dtype != torch.int64 or seq_len.dtype != torch.int32:
+        raise TypeError("seq_start must be int64 and seq_len int32")
+    B, D = x.shape
+    H, d_k, d_c = W_uk.shape
+    d_r = 0 if W_kr is None else W_kr.shape[0]
+    if cache.shape[-1] != d_c + d_r:
+        raise ValueError("cache width must be d_c + d_r")
+    dt = _dtype_code(x)
+    if q_abs is None:
+        q_abs = torch.empty((B, H, d_c + d_r), dtype=x.dtype, device=x.device)
+    need = lib().gmla_decode_prepare_workspace_size(B, H, d_c, d_k, d_r, dt)
+    workspace, wsb = _workspace(need, x.device, workspace)
+    _check(lib().gmla_decode_prepare(_vp(x), _vp(W_c), _vp(W_kr), _vp(W_q), _vp(W_qr), _vp(W_uk), _vp(cache),
+                                     _vp(seq_start), _vp(seq_len), _vp(q_abs), _vp(workspace), wsb, B, D, H, d_c,
+                                     d_k, d_r, float(rope_base), dt, _stream()))
+    return q_abs
 
 
 # ------------------------------------------------------------------ gate + output

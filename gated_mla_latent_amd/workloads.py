@@ -172,3 +172,36 @@ def decode_rope_b8_l131072(seed=0, with_output_side=True):
     """bf16 long-context decode: B=8, H=128, d_c=512 + 64, L=131072 each."""
     return make_decode(8, 128, 512, 64, 131072, 131072, rope_base=10000.0, d_k_scale=128,
                        seed=seed, with_output_side=with_output_side, name="decode_rope_b8_l131072")
+
+
+@dataclass
+class DecodeStepInputs:
+    """The new token of every sequence and the projections that feed one
+    decode step: x [B, d_model], W_c [d_c, d_model], W_kr [d_r, d_model],
+    W_q [H*d_k, d_model], W_qr [H*d_r, d_model], W_uk [H, d_k, d_c]
+    (W_kr and W_qr are None when d_r == 0)."""
+    d_model: int
+    d_k: int
+    x: torch.Tensor
+    W_c: torch.Tensor
+    W_kr: torch.Tensor | None
+    W_q: torch.Tensor
+    W_qr: torch.Tensor | None
+    W_uk: torch.Tensor
+
+
+def make_decode_step(dec: DecodeInputs, d_model: int, d_k: int, *, seed=0) -> DecodeStepInputs:
+    """Inputs of the decode-step projections for the sequences of `dec`.
+    Drawn from their own generator (seed + 7919) in the order x, W_c, W_kr,
+    W_q, W_qr, W_uk, so that `dec` is the same tensor set with or without
+    them. Build `dec` with gap_rows >= 1 so that row seq_start + seq_len, the
+    one the step appends, is free."""
+    gen = torch.Generator("cpu").manual_seed(seed + 7919)
+    B, H, d_c, d_r, dt = dec.B, dec.H, dec.d_c, dec.d_r, dec.dtype
+    x = _randn(gen, (B, d_model), 1.0, dt)
+    W_c = _weight(gen, d_c, d_model, dt)
+    W_kr = _weight(gen, d_r, d_model, dt) if d_r else None
+    W_q = _weight(gen, H * d_k, d_model, dt)
+    W_qr = _weight(gen, H * d_r, d_model, dt) if d_r else None
+    W_uk = _weight(gen, d_k, d_c, dt, lead=(H,))
+    return DecodeStepInputs(d_model=d_model, d_k=d_k, x=x, W_c=W_c, W_kr=W_kr, W_q=W_q, W_qr=W_qr, W_uk=W_uk)

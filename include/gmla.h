@@ -109,6 +109,40 @@ gmla_status_t gmla_decode(const void* q_abs, const void* cache, const int64_t* s
                           int d_r, float rope_base, float sm_scale, int num_splits, gmla_dtype_t dtype, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Decode-step projections: the new token's cache row and its absorbed query,
+ * the inputs of gmla_decode ([N03] §5.1 and exercise 4 answer for the
+ * absorbed query, §5.2 for the decoupled RoPE key that is rotated once and
+ * cached, the query's RoPE part being rotated by the attention).
+ *
+ *   x         [B, d_model]          hidden state of each sequence's new token
+ *   W_c       [d_c, d_model]        latent (down) projection
+ *   W_kr      [d_r, d_model]        shared RoPE key projection (NULL if d_r == 0)
+ *   W_q       [H*d_k, d_model]      query projection, head-major rows
+ *   W_qr      [H*d_r, d_model]      per-head RoPE query projection (NULL if d_r == 0)
+ *   W_uk      [H, d_k, d_c]         per-head key up-projection
+ *   cache     [rows, d_c + d_r]     in/out: row seq_start[b] + seq_len[b] is
+ *                                   set to [W_c x_b ; RoPE(W_kr x_b, seq_len[b])];
+ *                                   no other row is touched
+ *   seq_start [B] int64 (device), seq_len [B] int32 (device): cached tokens
+ *                                   before this step; not modified (the caller
+ *                                   adds 1 before gmla_decode, which then
+ *                                   rotates the query to position seq_len[b])
+ *   q_abs     [B, H, d_c + d_r]     out: [(W_UK^(h))^T q_h ; W_qr^(h) x_b],
+ *                                   q_h = W_q^(h) x_b, the RoPE part unrotated
+ * RoPE pairs are interleaved (2i, 2i+1), theta_i = rope_base^(-2i/d_r);
+ * rope_base == 0 leaves the key unrotated. The target rows must lie inside
+ * `cache` and differ between sequences (trusted, read on the device).
+ * Only GMLA_BF16 is supported (GMLA_ERR_UNSUPPORTED otherwise); it needs
+ * d_model % 64 == 0, d_c % 64 == 0, d_k % 16 == 0, d_k <= 128 and
+ * d_r % 4 == 0.
+ * ---------------------------------------------------------------------- */
+size_t gmla_decode_prepare_workspace_size(int B, int H, int d_c, int d_k, int d_r, gmla_dtype_t dtype);
+gmla_status_t gmla_decode_prepare(const void* x, const void* W_c, const void* W_kr, const void* W_q, const void* W_qr,
+                                  const void* W_uk, void* cache, const int64_t* seq_start, const int32_t* seq_len,
+                                  void* q_abs, void* workspace, size_t workspace_bytes, int B, int d_model, int H,
+                                  int d_c, int d_k, int d_r, float rope_base, gmla_dtype_t dtype, void* stream);
+
+/* ------------------------------------------------------------------------
  * Gate and output projection ([GF] §二 boxed equation):
  *   y_t = W_o [ Sigmoid(W_g x_t) (.) o~_t ]
  * With W_uv == NULL, `o` is o~ [T, H*d_v] (prefill output). With W_uv given,

@@ -109,6 +109,43 @@ def test_prefill_argument_checks(L):
     assert need == 2 * 16 * 2 * 128 * 2 + 2 * 128 * 64 * 2  # q, K, and V^T padded to 64 keys
 
 
+def _prep(L, **kw):
+    a = dict(x=A, Wc=A, Wkr=A, Wq=A, Wqr=A, Wuk=A, cache=A, start=A, len_=A, q=A, ws=A, wsb=1 << 40, B=4, D=256,
+             H=16, d_c=512, d_k=128, d_r=64, base=10000.0, dt=1)
+    a.update(kw)
+    return L.gmla_decode_prepare(a["x"], a["Wc"], a["Wkr"], a["Wq"], a["Wqr"], a["Wuk"], a["cache"], a["start"],
+                                 a["len_"], a["q"], a["ws"], a["wsb"], a["B"], a["D"], a["H"], a["d_c"], a["d_k"],
+                                 a["d_r"], a["base"], a["dt"], None)
+
+
+def test_decode_prepare_argument_checks(L):
+    assert _prep(L, Wq=0) == INVALID
+    assert _prep(L, Wkr=0) == INVALID               # d_r > 0 needs the RoPE projections
+    assert _prep(L, Wkr=0, Wqr=0, d_r=0, wsb=0) == WORKSPACE  # ... d_r == 0 does not
+    assert _prep(L, cache=A + 4) == INVALID
+    assert _prep(L, B=0) == INVALID
+    assert _prep(L, d_r=3) == INVALID
+    assert _prep(L, base=float("inf")) == INVALID
+    assert _prep(L, dt=0) == UNSUPPORTED            # bf16 only
+    assert _prep(L, D=200) == UNSUPPORTED
+    assert _prep(L, d_c=96) == UNSUPPORTED
+    assert _prep(L, d_k=256) == UNSUPPORTED
+    assert _prep(L, d_k=24) == UNSUPPORTED
+    assert _prep(L, d_r=2) == UNSUPPORTED
+    assert _prep(L, wsb=100) == WORKSPACE
+    assert _prep(L, ws=A + 16) == INVALID           # workspace must be 256-byte aligned
+
+
+def test_decode_prepare_workspace_size_formula(L):
+    up = lambda n: (n + 255) // 256 * 256
+    for B, H, d_c, d_k, d_r in [(4, 16, 512, 128, 64), (37, 128, 512, 128, 0), (1, 3, 64, 32, 4)]:
+        # new cache rows [B, d_c + d_r], queries [B, H d_k], RoPE queries [B, H d_r]
+        want = up(B * (d_c + d_r) * 2) + up(B * H * d_k * 2) + up(B * H * d_r * 2)
+        assert L.gmla_decode_prepare_workspace_size(B, H, d_c, d_k, d_r, 1) == want
+    assert L.gmla_decode_prepare_workspace_size(4, 16, 512, 128, 64, 0) == 0
+    assert L.gmla_decode_prepare_workspace_size(0, 16, 512, 128, 64, 1) == 0
+
+
 def _gate(L, **kw):
     a = dict(x=A, o=A, Wuv=0, Wg=A, Wo=A, y=A, ws=A, wsb=1 << 40, T=4, D=256, H=2, d_c=0, d_v=64, dt=1)
     a.update(kw)
