@@ -17,8 +17,12 @@ Sources (page title, section):
         §一 latent and per-head reconstruction; §二 causal softmax, head
         concat and the boxed gated output equation; §四 data flow; NoPE note.
   [N03] "LLM 注意力与计算内核精读笔记 · 03 注意力头变体：MQA / GQA / MLA"
-        §5.1 low-rank KV compression and absorption; §5.2 decoupled RoPE;
-        题4 answer (absorbed query (W^UK)^T q).
+        §5.1 low-rank KV compression and absorption, and the low-rank query
+        c^Q = W^DQ h, q = W^UQ c^Q; §5.2 decoupled RoPE (q^R from c^Q, k^R
+        from h); 题4 answer (absorbed query (W^UK)^T q).
+  [CD]  "Gated Multi-head Latent Attention (Gated MLA)" (concept page)
+        Gating Mechanism / Mathematical Formulation: the per-head scalar
+        gate g_h = sigmoid(W_g x + b_g) scaling head h's output.
 
 Readings where the pages leave a step open (each one is listed with its
 reason in the design notes of the repository):
@@ -28,7 +32,10 @@ reason in the design notes of the repository):
     already rotated ([N03] §5.2 applies RoPE to k^R before it is cached);
   * V in absorbed decode is the latent part c[:d_c] only;
   * the gate is per channel (H*d_v wide), without bias, fed by x_t ([GF] §二);
-  * head concat is head-major: channel h*d_v + j.
+  * head concat is head-major: channel h*d_v + j;
+  * in prefill the RoPE parts sit after each head's content part: score
+    q^C.k^C + RoPE(q^R, t).RoPE(k^R, s), with k^R shared by all heads;
+  * without query compression c^Q is x itself (W^DQ = identity).
 """
 from __future__ import annotations
 
@@ -39,6 +46,7 @@ import numpy as np
 __all__ = [
     "latent_projection",
     "query_projection",
+    "query_compression",
     "reconstruct_kv",
     "attend_rows",
     "causal_attention",
@@ -49,6 +57,7 @@ __all__ = [
     "value_up_projection",
     "sigmoid",
     "gate_out_reference",
+    "head_gate_out_reference",
     "prefill_reference",
     "gated_mla_layer",
 ]
@@ -77,6 +86,16 @@ def query_projection(x, W_q, H: int) -> np.ndarray:
     """
     q = _f64(x) @ _f64(W_q).T
     return q.reshape(q.shape[:-1] + (H, q.shape[-1] // H))
+
+
+def query_compression(x, W_dq) -> np.ndarray:
+    """c_t^Q = W^DQ h_t, the low-rank query latent ([N03] §5.1, last
+    paragraph); the per-head queries are then q_t = W^UQ c_t^Q and the RoPE
+    queries W^QR c_t^Q ([N03] §5.2).
+
+    x: [..., d_model]; W_dq: [d_cq, d_model]. Returns [..., d_cq].
+    """
+    return _f64(x) @ _f64(W_dq).T
 
 
 def reconstruct_kv(c, W_uk, W_uv):
@@ -211,7 +230,7 @@ def decode_reference(q_abs, cache, seq_start, seq_len, d_c: int, d_r: int,
     return o_lat, lse
 
 
-def decode_prepare_reference(x, W_c, W_kr, W_q, W_qr, W_uk, pos, rope_base: float):
+def decode_prepare_reference(x, W_c, W_kr, W_q, W_qr, W_uk, pos, rope_base: float, W_dq=None):
     """The projections of one decode step around the cached-latent attention
     ([N03] §5.1 low-rank KV compression, absorption and 题4; §5.2 decoupled
     RoPE), for the new token x_b of every sequence b at position pos[b]:
@@ -224,8 +243,10 @@ def decode_prepare_reference(x, W_c, W_kr, W_q, W_qr, W_uk, pos, rope_base: floa
                                             (the decode step rotates it)
 
     x: [B, d_model]; W_c: [d_c, d_model]; W_kr: [d_r, d_model] or None;
-    W_q: [H*d_k, d_model]; W_qr: [H*d_r, d_model] or None;
-    W_uk: [H, d_k, d_c]; pos: [B].
+    W_q: [H*d_k, d_in]; W_qr: [H*d_r, d_in] or None; W_uk: [H, d_k, d_c];
+    pos: [B]. With W_dq ([d_cq, d_model]) the query side starts from the
+    low-rank query c^Q = W^DQ x (d_in = d_cq: W_q is W^UQ, and the RoPE
+    query is W^QR c^Q); without it d_in = d_model and the query side reads x.
     Returns (cache_row [B, d_c + d_r], q_abs [B, H, d_c + d_r]).
     """
     x = _f64(x)
@@ -233,7 +254,8 @@ def decode_prepare_reference(x, W_c, W_kr, W_q, W_qr, W_uk, pos, rope_base: floa
     W_uk = _f64(W_uk)
     H = W_uk.shape[0]
     c = latent_projection(x, W_c)  # [B, d_c]
-    q = query_projection(x, W_q, H)  # [B, H, d_k]
+    xq = x if W_dq is None else query_compression(x, W_dq)
+    q = query_projection(xq, W_q, H)  # [B, H, d_k]
     q_t = np.einsum("bhk,hkc->bhc", q, W_uk)  # (W_UK^(h))^T q^(h)
     if W_kr is None or np.asarray(W_kr).shape[0] == 0:
         return c, q_t
@@ -241,7 +263,7 @@ def decode_prepare_reference(x, W_c, W_kr, W_q, W_qr, W_uk, pos, rope_base: floa
     if rope_base != 0.0:
         k_r = rope_rotate(k_r, np.asarray(pos, dtype=np.float64), rope_base)
     d_r = k_r.shape[-1]
-    q_r = (x @ _f64(W_qr).T).reshape(B, H, d_r)
+    q_r = (xq @ _f64(W_qr).T).reshape(B, H, d_r)
     return np.concatenate([c, k_r], axis=1), np.concatenate([q_t, q_r], axis=2)
 
 
@@ -296,26 +318,66 @@ def gate_out_reference(x, o_tilde, W_g, W_o, return_gated: bool = False):
     return (y, gated) if return_gated else y
 
 
+def head_gate_out_reference(x, o_tilde, W_g, b_g, W_o, return_gated: bool = False):
+    """Per-head scalar gate ([CD] Gating Mechanism and Mathematical
+    Formulation): g_t = Sigmoid(W_g x_t + b_g) in R^H, head h's output block
+    o~_t^(h) (channels h*d_v .. h*d_v + d_v - 1) scaled by g_t[h], then the
+    heads merged and projected: y_t = W_o [ g_t[h] o~_t^(h) ]_h.
+
+    x: [T, d_model]; o_tilde: [T, H*d_v]; W_g: [H, d_model]; b_g: [H] or
+    None (zero); W_o: [d_model, H*d_v].
+    """
+    z = _f64(x) @ _f64(W_g).T
+    if b_g is not None:
+        z = z + _f64(b_g)
+    g = sigmoid(z)  # [T, H]
+    o = _f64(o_tilde)
+    T, HV = o.shape
+    H = g.shape[1]
+    gated = (o.reshape(T, H, HV // H) * g[:, :, None]).reshape(T, HV)
+    y = gated @ _f64(W_o).T
+    return (y, gated) if return_gated else y
+
+
 # --------------------------------------------------------------------------
 # Prefill and the whole layer
 # --------------------------------------------------------------------------
-def prefill_reference(x, W_c, W_q, W_uk, W_uv, sm_scale: float, rows=None):
+def prefill_reference(x, W_c, W_q, W_uk, W_uv, sm_scale: float, rows=None, *, W_dq=None, W_kr=None, W_qr=None,
+                      rope_base: float = 0.0):
     """Causal prefill of a batch of sequences, explicit K/V per head.
 
     x: [B, L, d_model]. Returns (c [B, L, d_c], o_tilde, lse) where o_tilde is
     [B, L, H*d_v] (head-major concat, [GF] §二 second equation) and lse is
     [B, L, H]. With `rows` (a list of query positions) only those positions
     are attended (o_tilde/lse are then [B, R, ...]); c is always complete.
+
+    Optional parts:
+      * W_dq [d_cq, d_model]: low-rank query ([N03] §5.1): the queries come
+        from c^Q = W^DQ x, and W_q ([H*d_k, d_cq]) is W^UQ;
+      * W_kr [d_r, d_model], W_qr [H*d_r, d_in]: decoupled RoPE ([N03] §5.2):
+        every head's key is [W_UK^(h) c_s ; RoPE(W^KR x_s, s)] (the RoPE part
+        shared by the heads) and its query [q^C ; RoPE(W^QR(h) c^Q_t, t)]
+        (c^Q = x without W_dq); rope_base 0 leaves both unrotated.
     """
     x = _f64(x)
     B, L, _ = x.shape
     H = np.asarray(W_uk).shape[0]
     c = latent_projection(x, W_c)
     t_rows = np.arange(L) if rows is None else np.asarray(rows)
+    d_r = 0 if W_kr is None else np.asarray(W_kr).shape[0]
     outs, lses = [], []
     for b in range(B):
         k, v = reconstruct_kv(c[b], W_uk, W_uv)  # [L, H, d]
-        q = query_projection(x[b, t_rows], W_q, H)  # [R, H, d_k]
+        xq = x[b, t_rows] if W_dq is None else query_compression(x[b, t_rows], W_dq)
+        q = query_projection(xq, W_q, H)  # [R, H, d_k]
+        if d_r > 0:
+            k_r = x[b] @ _f64(W_kr).T  # [L, d_r], position s = row index
+            q_r = (xq @ _f64(W_qr).T).reshape(len(t_rows), H, d_r)
+            if rope_base != 0.0:
+                k_r = rope_rotate(k_r, np.arange(L, dtype=np.float64), rope_base)
+                q_r = rope_rotate(q_r, t_rows.astype(np.float64)[:, None], rope_base)
+            k = np.concatenate([k, np.broadcast_to(k_r[:, None, :], (L, H, d_r))], axis=2)
+            q = np.concatenate([q, q_r], axis=2)
         o, l = attend_rows(q, k, v, t_rows, sm_scale)
         outs.append(o.reshape(len(t_rows), -1))
         lses.append(l)

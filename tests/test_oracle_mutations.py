@@ -54,28 +54,57 @@ def _reconstruct_swapped(c, W_uk, W_uv):
     return k, np.einsum("...c,hdc->...hd", np.asarray(c, float), np.asarray(W_uv, float)[:, :, ::-1])
 
 
-def _prepare_heads_swapped(x, W_c, W_kr, W_q, W_qr, W_uk, pos, base):
+def _prepare_heads_swapped(x, W_c, W_kr, W_q, W_qr, W_uk, pos, base, **kw):
     # each head's query absorbed with another head's W_UK
-    return _orig_prepare(x, W_c, W_kr, W_q, W_qr, np.asarray(W_uk, float)[::-1], pos, base)
+    return _orig_prepare(x, W_c, W_kr, W_q, W_qr, np.asarray(W_uk, float)[::-1], pos, base, **kw)
 
 
-def _prepare_pos_off_by_one(x, W_c, W_kr, W_q, W_qr, W_uk, pos, base):
+def _prepare_pos_off_by_one(x, W_c, W_kr, W_q, W_qr, W_uk, pos, base, **kw):
     # the new RoPE key rotated to the previous position
-    return _orig_prepare(x, W_c, W_kr, W_q, W_qr, W_uk, np.asarray(pos) - 1, base)
+    return _orig_prepare(x, W_c, W_kr, W_q, W_qr, W_uk, np.asarray(pos) - 1, base, **kw)
 
 
-def _prepare_rotates_query(x, W_c, W_kr, W_q, W_qr, W_uk, pos, base):
+def _prepare_rotates_query(x, W_c, W_kr, W_q, W_qr, W_uk, pos, base, **kw):
     # the RoPE query rotated here as well as in the decode step
-    row, q = _orig_prepare(x, W_c, W_kr, W_q, W_qr, W_uk, pos, base)
+    row, q = _orig_prepare(x, W_c, W_kr, W_q, W_qr, W_uk, pos, base, **kw)
     d_c = row.shape[1] - (0 if W_kr is None else np.asarray(W_kr).shape[0])
     q = q.copy()
     q[..., d_c:] = G.rope_rotate(q[..., d_c:], np.asarray(pos, float)[:, None], base)
     return row, q
 
 
+def _query_compression_permuted(x, W_dq):
+    # the latent query's components in the wrong order
+    return np.asarray(x, float) @ np.asarray(W_dq, float)[::-1].T
+
+
+def _head_gate_tiled(x, o_tilde, W_g, b_g, W_o, return_gated=False):
+    # channel n gated by head n % H instead of head n // d_v
+    z = np.asarray(x, float) @ np.asarray(W_g, float).T + (0.0 if b_g is None else np.asarray(b_g, float))
+    g = 1.0 / (1.0 + np.exp(-z))
+    o = np.asarray(o_tilde, float)
+    gated = o * np.tile(g, (1, o.shape[1] // g.shape[1]))
+    y = gated @ np.asarray(W_o, float).T
+    return (y, gated) if return_gated else y
+
+
+def _prefill_no_rope_term(x, W_c, W_q, W_uk, W_uv, sm_scale, rows=None, **kw):
+    # the RoPE query dropped from the score (the key part then adds nothing)
+    if kw.get("W_qr") is not None:
+        kw["W_qr"] = 0.0 * np.asarray(kw["W_qr"], float)
+    return _orig_prefill(x, W_c, W_q, W_uk, W_uv, sm_scale, rows, **kw)
+
+
+def _prefill_unrotated(x, W_c, W_q, W_uk, W_uv, sm_scale, rows=None, **kw):
+    # decoupled RoPE parts used without rotating them
+    kw["rope_base"] = 0.0
+    return _orig_prefill(x, W_c, W_q, W_uk, W_uv, sm_scale, rows, **kw)
+
+
 _orig_attend = G.attend_rows
 _orig_reconstruct = G.reconstruct_kv
 _orig_prepare = G.decode_prepare_reference
+_orig_prefill = G.prefill_reference
 
 MUTATIONS = [
     ("rope_rotate", _rope_wrong_sign, [P.test_rope_matches_complex_rotation_and_is_relative,
@@ -100,6 +129,16 @@ MUTATIONS = [
      [lambda: P.test_decode_prepare_then_decode_equals_explicit_attention(4)]),
     ("decode_prepare_reference", _prepare_rotates_query,
      [lambda: P.test_decode_prepare_then_decode_equals_explicit_attention(4)]),
+    ("query_compression", _query_compression_permuted,
+     [P.test_low_rank_query_equals_composed_projection, P.test_low_rank_query_decode_prepare_scalar_loops]),
+    ("head_gate_out_reference", _head_gate_tiled,
+     [P.test_head_gate_matches_scalar_loops, P.test_head_gate_equals_channel_gate_with_repeated_rows,
+      P.test_head_gate_allows_folding_wo_wuv_in_decode]),
+    ("prefill_reference", _prefill_no_rope_term,
+     [P.test_rope_prefill_matches_scalar_brute_force, P.test_rope_prefill_rows_equal_absorbed_decode_steps]),
+    ("prefill_reference", _prefill_unrotated,
+     [P.test_rope_prefill_matches_scalar_brute_force, P.test_rope_prefill_rows_equal_absorbed_decode_steps]),
+    ("rope_rotate", _rope_wrong_sign, [P.test_rope_prefill_matches_scalar_brute_force]),
 ]
 
 

@@ -374,6 +374,140 @@ def test_decode_prepare_absorbed_query_matches_scalar_loops():
                 assert abs(q_abs[b][h][dc + i] - sum(W_qr[h * dr + i][j] * x[b][j] for j in range(D))) < 1e-12
 
 
+# ---------------------------------------------------------------- low-rank query
+def test_low_rank_query_equals_composed_projection():
+    """q = W^UQ (W^DQ x) and q^R = W^QR (W^DQ x) are the full-rank
+    projections W^UQ W^DQ and W^QR W^DQ applied to x (matrix product
+    associativity), in prefill and in the decode-step projections."""
+    B, L, D, H, dc, dk, dv, dr, dcq = 2, 5, 9, 3, 6, 4, 5, 4, 7
+    x = rng.standard_normal((B, L, D))
+    W_c, W_uk, W_uv = rng.standard_normal((dc, D)), rng.standard_normal((H, dk, dc)), rng.standard_normal((H, dv, dc))
+    W_dq, W_uq, W_qr = rng.standard_normal((dcq, D)), rng.standard_normal((H * dk, dcq)), rng.standard_normal((H * dr, dcq))
+    W_kr = rng.standard_normal((dr, D))
+    a = O.prefill_reference(x, W_c, W_uq, W_uk, W_uv, 0.3, W_dq=W_dq, W_kr=W_kr, W_qr=W_qr, rope_base=50.0)
+    b = O.prefill_reference(x, W_c, W_uq @ W_dq, W_uk, W_uv, 0.3, W_kr=W_kr, W_qr=W_qr @ W_dq, rope_base=50.0)
+    for u, v in zip(a, b):
+        np.testing.assert_allclose(u, v, rtol=0, atol=1e-11)
+    xs = x[:, -1]
+    r1, q1 = O.decode_prepare_reference(xs, W_c, W_kr, W_uq, W_qr, W_uk, [3, 8], 50.0, W_dq=W_dq)
+    r2, q2 = O.decode_prepare_reference(xs, W_c, W_kr, W_uq @ W_dq, W_qr @ W_dq, W_uk, [3, 8], 50.0)
+    np.testing.assert_allclose(r1, r2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(q1, q2, rtol=0, atol=1e-11)
+
+
+def test_low_rank_query_decode_prepare_scalar_loops():
+    D, H, dc, dk, dr, dcq = 4, 2, 3, 2, 2, 3
+    x = rng.standard_normal((2, D))
+    W_c, W_dq = rng.standard_normal((dc, D)), rng.standard_normal((dcq, D))
+    W_uq, W_uk = rng.standard_normal((H * dk, dcq)), rng.standard_normal((H, dk, dc))
+    W_kr, W_qr = rng.standard_normal((dr, D)), rng.standard_normal((H * dr, dcq))
+    _, q_abs = O.decode_prepare_reference(x, W_c, W_kr, W_uq, W_qr, W_uk, [1, 2], 0.0, W_dq=W_dq)
+    for b in range(2):
+        cq = [sum(W_dq[i][j] * x[b][j] for j in range(D)) for i in range(dcq)]
+        for h in range(H):
+            q = [sum(W_uq[h * dk + k][i] * cq[i] for i in range(dcq)) for k in range(dk)]
+            for c in range(dc):
+                assert abs(q_abs[b][h][c] - sum(W_uk[h][k][c] * q[k] for k in range(dk))) < 1e-12
+            for i in range(dr):
+                assert abs(q_abs[b][h][dc + i] - sum(W_qr[h * dr + i][j] * cq[j] for j in range(dcq))) < 1e-12
+
+
+# ---------------------------------------------------------------- RoPE prefill
+def _brute_rope_prefill(x, W_c, W_q, W_uk, W_uv, W_kr, W_qr, scale, base):
+    """One sequence, scalar loops; the rotation is the complex-number form."""
+    L, D = x.shape
+    H, dk, dc = W_uk.shape
+    dv, dr = W_uv.shape[1], W_kr.shape[0]
+    c = [[sum(W_c[i][j] * x[s][j] for j in range(D)) for i in range(dc)] for s in range(L)]
+    kr = _rope_complex(np.array([[sum(W_kr[i][j] * x[s][j] for j in range(D)) for i in range(dr)] for s in range(L)]),
+                       np.arange(L), base)
+    out = np.zeros((L, H * dv))
+    for t in range(L):
+        for h in range(H):
+            q = [sum(W_q[h * dk + i][j] * x[t][j] for j in range(D)) for i in range(dk)]
+            qr = _rope_complex(np.array([sum(W_qr[h * dr + i][j] * x[t][j] for j in range(D)) for i in range(dr)]),
+                               t, base)
+            z = []
+            for s in range(t + 1):
+                k = [sum(W_uk[h][i][m] * c[s][m] for m in range(dc)) for i in range(dk)]
+                z.append(scale * (sum(q[i] * k[i] for i in range(dk)) + sum(qr[i] * kr[s][i] for i in range(dr))))
+            mx = max(z)
+            e = [math.exp(u - mx) for u in z]
+            den = sum(e)
+            for i in range(dv):
+                out[t][h * dv + i] = sum(e[s] / den * sum(W_uv[h][i][m] * c[s][m] for m in range(dc))
+                                         for s in range(t + 1))
+    return out
+
+
+def test_rope_prefill_matches_scalar_brute_force():
+    L, D, H, dc, dk, dv, dr = 6, 5, 2, 4, 3, 3, 4
+    x = rng.standard_normal((1, L, D))
+    W_c, W_q = rng.standard_normal((dc, D)), rng.standard_normal((H * dk, D))
+    W_uk, W_uv = rng.standard_normal((H, dk, dc)), rng.standard_normal((H, dv, dc))
+    W_kr, W_qr = rng.standard_normal((dr, D)), rng.standard_normal((H * dr, D))
+    _, o, _ = O.prefill_reference(x, W_c, W_q, W_uk, W_uv, 0.4, W_kr=W_kr, W_qr=W_qr, rope_base=7.0)
+    ref = _brute_rope_prefill(x[0], W_c, W_q, W_uk, W_uv, W_kr, W_qr, 0.4, 7.0)
+    np.testing.assert_allclose(o[0], ref, rtol=0, atol=1e-11)
+
+
+def test_rope_prefill_rows_equal_absorbed_decode_steps():
+    """Row t of the explicit RoPE prefill equals the absorbed route: the
+    cache rows of tokens 0..t from the decode-step projections, the latent
+    decode over them, then W_UV."""
+    L, D, H, dc, dk, dv, dr, base, scale = 7, 6, 3, 5, 4, 3, 4, 100.0, 0.35
+    x = rng.standard_normal((1, L, D))
+    W_c, W_q = rng.standard_normal((dc, D)), rng.standard_normal((H * dk, D))
+    W_uk, W_uv = rng.standard_normal((H, dk, dc)), rng.standard_normal((H, dv, dc))
+    W_kr, W_qr = rng.standard_normal((dr, D)), rng.standard_normal((H * dr, D))
+    _, o, lse = O.prefill_reference(x, W_c, W_q, W_uk, W_uv, scale, W_kr=W_kr, W_qr=W_qr, rope_base=base)
+    rows, q_abs = O.decode_prepare_reference(x[0], W_c, W_kr, W_q, W_qr, W_uk, np.arange(L), base)
+    for t in range(L):
+        o_lat, l = O.decode_reference(q_abs[t:t + 1], rows, [0], [t + 1], dc, dr, base, scale)
+        np.testing.assert_allclose(O.value_up_projection(o_lat, W_uv)[0], o[0, t], rtol=0, atol=1e-11)
+        np.testing.assert_allclose(l[0], lse[0, t], rtol=0, atol=1e-11)
+
+
+# ---------------------------------------------------------------- per-head gate
+def test_head_gate_matches_scalar_loops():
+    T, D, H, dv = 3, 4, 2, 3
+    x, o = rng.standard_normal((T, D)), rng.standard_normal((T, H * dv))
+    W_g, b_g, W_o = rng.standard_normal((H, D)), rng.standard_normal(H), rng.standard_normal((D, H * dv))
+    y = O.head_gate_out_reference(x, o, W_g, b_g, W_o)
+    for t in range(T):
+        g = [1.0 / (1.0 + math.exp(-(sum(W_g[h][j] * x[t][j] for j in range(D)) + b_g[h]))) for h in range(H)]
+        for i in range(D):
+            want = sum(W_o[i][h * dv + j] * g[h] * o[t][h * dv + j] for h in range(H) for j in range(dv))
+            assert abs(y[t][i] - want) < 1e-12
+
+
+def test_head_gate_equals_channel_gate_with_repeated_rows():
+    """A per-head gate is the per-channel gate whose rows repeat each head's
+    gate row over its d_v channels."""
+    T, D, H, dv = 4, 6, 3, 5
+    x, o = rng.standard_normal((T, D)), rng.standard_normal((T, H * dv))
+    W_g, W_o = rng.standard_normal((H, D)), rng.standard_normal((D, H * dv))
+    y = O.head_gate_out_reference(x, o, W_g, None, W_o)
+    y_ch = O.gate_out_reference(x, o, np.repeat(W_g, dv, axis=0), W_o)
+    np.testing.assert_allclose(y, y_ch, rtol=0, atol=1e-12)
+    # zero weights and bias: every gate is 1/2
+    np.testing.assert_allclose(O.head_gate_out_reference(x, o, 0 * W_g, np.zeros(H), W_o), 0.5 * (o @ W_o.T),
+                               rtol=0, atol=1e-12)
+
+
+def test_head_gate_allows_folding_wo_wuv_in_decode():
+    """With a scalar per head, W_o^(h) W_UV^(h) can be folded into one
+    [d_model, d_c] matrix per head: y = sum_h g_h (W_o^(h) W_UV^(h)) o_lat_h."""
+    T, D, H, dc, dv = 3, 7, 2, 5, 4
+    x, o_lat = rng.standard_normal((T, D)), rng.standard_normal((T, H, dc))
+    W_g, b_g = rng.standard_normal((H, D)), rng.standard_normal(H)
+    W_uv, W_o = rng.standard_normal((H, dv, dc)), rng.standard_normal((D, H * dv))
+    y = O.head_gate_out_reference(x, O.value_up_projection(o_lat, W_uv), W_g, b_g, W_o)
+    g = 1.0 / (1.0 + np.exp(-(x @ W_g.T + b_g)))
+    y_fold = sum(g[:, h:h + 1] * (o_lat[:, h] @ (W_o[:, h * dv:(h + 1) * dv] @ W_uv[h]).T) for h in range(H))
+    np.testing.assert_allclose(y, y_fold, rtol=0, atol=1e-11)
+
+
 # ---------------------------------------------------------------- brute force
 def _brute_layer(x, W_c, W_q, W_uk, W_uv, W_g, W_o, scale):
     """Scalar loops over every index, math.exp only: one sequence."""
