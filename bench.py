@@ -157,13 +157,13 @@ def build_decode(args, inp, torch, ops):
     rows_new = torch.empty((inp.B, inp.d_c + inp.d_r), dtype=torch.bfloat16, device=dev)
     start_new = (torch.arange(inp.B, dtype=torch.int64) - inp.seq_len.to(torch.int64)).to(dev)
     q_new = torch.empty((inp.B, inp.H, inp.d_c + inp.d_r), dtype=torch.bfloat16, device=dev)
-    wsp_n = L.gmla_decode_prepare_workspace_size(inp.B, inp.H, inp.d_c, DECODE_D_K, inp.d_r, 1)
+    wsp_n = L.gmla_decode_prepare_workspace_size(inp.B, inp.d_model, inp.H, inp.d_c, DECODE_D_K, inp.d_r, 1)
     wsp = torch.empty(wsp_n, dtype=torch.uint8, device=dev)
     o_lat = torch.empty((inp.B, inp.H, inp.d_c), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((inp.B, inp.H), dtype=torch.float32, device=dev)
     y = torch.empty((inp.B, inp.d_model), dtype=torch.bfloat16, device=dev)
     wsd_n = L.gmla_decode_workspace_size(inp.B, inp.H, inp.d_c, args.num_splits, 1)
-    wsg_n = L.gmla_gate_out_workspace_size(inp.B, inp.H, inp.d_v, 1, 1)
+    wsg_n = L.gmla_gate_out_workspace_size(inp.B, inp.d_model, inp.H, inp.d_c, inp.d_v, 1, 1)
     wsd = torch.empty(wsd_n, dtype=torch.uint8, device=dev)
     wsg = torch.empty(wsg_n, dtype=torch.uint8, device=dev)
     calls = []
@@ -210,7 +210,7 @@ def build_prefill(args, p, torch, ops):
     ot = torch.empty((p.B, p.L, p.H * p.d_v), dtype=p.dtype, device=dev)
     y = torch.empty((T, p.d_model), dtype=p.dtype, device=dev)
     wsp_n = L.gmla_prefill_workspace_size(p.B, p.L, p.H, p.d_k, p.d_v, dt)
-    wsg_n = L.gmla_gate_out_workspace_size(T, 1, p.H * p.d_v, 0, dt)
+    wsg_n = L.gmla_gate_out_workspace_size(T, p.d_model, 1, 0, p.H * p.d_v, 0, dt)
     wsp = torch.empty(wsp_n, dtype=torch.uint8, device=dev)
     wsg = torch.empty(wsg_n, dtype=torch.uint8, device=dev)
     calls = []

@@ -17,7 +17,9 @@
 //  * gemm_skinny: M <= 64 (decode-step projections). Weight-streaming bound:
 //    each workgroup owns 32 output columns, its 4 waves split K and stream
 //    their chunks through private LDS rings (several chunks in flight per
-//    wave, no barrier in the loop), partial sums meet in LDS.
+//    wave, no barrier in the loop), partial sums meet in LDS. A grid of
+//    fewer than 512 workgroups (narrow N) also splits K across workgroups:
+//    fp32 partial sums, then gemm_splitk_reduce applies the epilogue.
 #include "common.h"
 #include "kernels.h"
 
@@ -248,20 +250,24 @@ __device__ __forceinline__ void skinny_wait(int pending) {
   wait_vmcnt<0>();
 }
 
+// Columns n0 .. n0 + 31 of batch `batch`, K slice zi of nz.
 template <int MT, int EPI>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
+__device__ __forceinline__ void skinny_body(const GemmArgs& g, int n0, int batch, int zi, int nz) {
   using C = SkinnyCfg<MT>;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n0 = blockIdx.x * 32;
-  const int batch = blockIdx.y;
   const bf16* A = g.A + batch * g.sA;
   const bf16* W = g.W + batch * g.sW;
   bf16* Cp = g.C + batch * g.sC;
   const bf16* Op = (EPI == EPI_GATE) ? g.O + batch * g.sO : nullptr;
   LDS_AS char* ring = smem + wave * C::WAVE_BYTES;
+  // K slice of this workgroup: chunks c_lo .. c_hi - 1 (all of K without split)
+  const int all_chunks = g.K / 64;
+  const int per = (all_chunks + nz - 1) / nz;
+  const int c_lo = zi * per;
+  const int c_hi = (c_lo + per) < all_chunks ? (c_lo + per) : all_chunks;
   const unsigned ring_addr = (unsigned)(uintptr_t)ring;
 
   // DMA: instruction q of a 32-row tile moves rows 8q .. 8q + 7; lane l
@@ -269,7 +275,6 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
   // (l % 8) ^ ((row >> 2) & 7). Rows past the end re-read the last row.
   const int lr = lane >> 3;
   auto piece_off = [&](int row) { return ((lane & 7) ^ ((row >> 2) & 7)) * 16; };
-  const int chunks = g.K / 64;
   auto issue = [&](int b, int j) {
     const unsigned dst = ring_addr + b * C::BUF_BYTES;
 #pragma unroll
@@ -295,10 +300,11 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
   floatx16 acc[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = floatx16{};
-  const int nmy = (chunks - wave + 3) / 4;  // this wave's chunks: wave, wave + 4, ...
+  const int span = c_hi > c_lo ? c_hi - c_lo : 0;
+  const int nmy = span > wave ? (span - wave + 3) / 4 : 0;  // this wave's chunks: c_lo + wave, + 4, ...
 #pragma unroll
   for (int b = 0; b < C::NBUF; ++b)
-    if (b < nmy) issue(b, wave + 4 * b);
+    if (b < nmy) issue(b, c_lo + wave + 4 * b);
   const int r32 = lane & 31, hk = lane >> 5;
   for (int i = 0; i < nmy; ++i) {
     const int b = i % C::NBUF;
@@ -315,7 +321,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
     }
     if (i + C::NBUF < nmy) {
       wait_lgkm0();  // this buffer's fragments are in registers before it is refilled
-      issue(b, wave + 4 * (i + C::NBUF));
+      issue(b, c_lo + wave + 4 * (i + C::NBUF));
     }
   }
 
@@ -339,8 +345,58 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
     }
     const int m = 32 * t + (lane & 31);
     const int n = n0 + 8 * wave + 4 * (lane >> 5);
-    store4<EPI>(g, Cp, Op, m, n, v[0], v[1], v[2], v[3]);
+    if (nz > 1) {  // partial sums [slice][batch][M][N rounded up to 4]
+      const int ldp = (g.N + 3) & ~3;
+      if (m < g.M && n < g.N)
+        *(float4*)(g.part + (((int64_t)zi * g.batches + batch) * g.M + m) * ldp + n) =
+            make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+      store4<EPI>(g, Cp, Op, m, n, v[0], v[1], v[2], v[3]);
+    }
   }
+}
+
+template <int MT, int EPI>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
+  skinny_body<MT, EPI>(g, blockIdx.x * 32, blockIdx.y, blockIdx.z, gridDim.z);
+}
+
+// Several plain-store GEMMs that share A, M and K in one grid: segment s
+// owns workgroups first_wg[s] .. first_wg[s + 1] - 1.
+template <int MT>
+__global__ __launch_bounds__(256) void gemm_skinny_group_kernel(GemmGroup gg) {
+  const int x = blockIdx.x;
+  const int s = (x >= gg.first_wg[1]) + (x >= gg.first_wg[2]) + (x >= gg.first_wg[3]);
+  GemmArgs g = gg.base;
+  g.W = s == 0 ? gg.W[0] : s == 1 ? gg.W[1] : s == 2 ? gg.W[2] : gg.W[3];
+  g.C = s == 0 ? gg.C[0] : s == 1 ? gg.C[1] : s == 2 ? gg.C[2] : gg.C[3];
+  g.N = s == 0 ? gg.N[0] : s == 1 ? gg.N[1] : s == 2 ? gg.N[2] : gg.N[3];
+  g.ldw = s == 0 ? gg.ldw[0] : s == 1 ? gg.ldw[1] : s == 2 ? gg.ldw[2] : gg.ldw[3];
+  g.ldc = s == 0 ? gg.ldc[0] : s == 1 ? gg.ldc[1] : s == 2 ? gg.ldc[2] : gg.ldc[3];
+  const int first = s == 0 ? 0 : s == 1 ? gg.first_wg[1] : s == 2 ? gg.first_wg[2] : gg.first_wg[3];
+  skinny_body<MT, EPI_STORE>(g, (x - first) * 32, 0, 0, 1);
+}
+
+// Sum the split-K partial sums of 4 consecutive columns and apply the
+// epilogue; one thread per (batch, m, 4 columns).
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmArgs g) {
+  const int ldp = (g.N + 3) & ~3, q4 = ldp / 4;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)g.batches * g.M * q4) return;
+  const int n = (int)(i % q4) * 4;
+  const int64_t bm = i / q4;
+  const int m = (int)(bm % g.M), batch = (int)(bm / g.M);
+  const int64_t slice = (int64_t)g.batches * g.M * ldp;
+  const float* p = g.part + bm * ldp + n;
+  float4 acc = *(const float4*)p;
+  for (int z = 1; z < g.ksplit; ++z) {
+    const float4 v = *(const float4*)(p + z * slice);
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  bf16* Cp = g.C + batch * g.sC;
+  const bf16* Op = (EPI == EPI_GATE) ? g.O + batch * g.sO : nullptr;
+  store4<EPI>(g, Cp, Op, m, n, acc.x, acc.y, acc.z, acc.w);
 }
 
 template <int MT, int EPI>
@@ -353,8 +409,14 @@ static hipError_t launch_skinny(const GemmArgs& g, hipStream_t st) {
     if (e != hipSuccess) return e;
     attr = true;
   }
-  return launch(kern, dim3((g.N + 31) / 32, g.batches), dim3(256), C::LDS_BYTES, st, g);
+  const int z = g.ksplit > 1 ? g.ksplit : 1;
+  if (z > 1 && !g.part) return hipErrorInvalidValue;
+  hipError_t e = launch(kern, dim3((g.N + 31) / 32, g.batches, z), dim3(256), C::LDS_BYTES, st, g);
+  if (e != hipSuccess || z == 1) return e;
+  const int64_t n4 = (int64_t)g.batches * g.M * (((g.N + 3) & ~3) / 4);
+  return launch(gemm_splitk_reduce_kernel<EPI>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, g);
 }
+
 
 // ----------------------------------------------------------------------------
 template <int BN, int BM, int EPI>
@@ -373,9 +435,11 @@ static hipError_t launch_tile(const GemmArgs& g, hipStream_t st) {
   return launch(kern, dim3(tiles, g.batches), dim3(512), LDS, st, g);
 }
 
+static bool skinny_path(int M, int N, int npad) { return M <= 64 && !(npad > N); }
+
 template <int EPI>
 static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
-  if (g.M <= 64 && !(EPI == EPI_STORE && g.npad > g.N)) {
+  if (skinny_path(g.M, g.N, EPI == EPI_STORE ? g.npad : 0)) {
     // the DMA offsets are 32-bit: every row start must be below 4 GiB
     if ((long long)g.N * g.ldw * 2 >= (1LL << 32) || (long long)g.M * g.lda * 2 >= (1LL << 32))
       return hipErrorInvalidValue;
@@ -384,6 +448,63 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
   const long long big_tiles = (long long)((g.N + 255) / 256) * ((g.M + 255) / 256) * g.batches;
   if (big_tiles >= 256) return launch_tile<256, 256, EPI>(g, st);
   return launch_tile<128, 128, EPI>(g, st);
+}
+
+// Split K when the skinny grid has fewer than 64 workgroups (a quarter of
+// the compute units; a grid of a few hundred loses more to the extra pass
+// than it gains), up to 256 workgroups, keeping at least 4 chunks of 64 per
+// workgroup (one per wave).
+int gemm_ksplit(int M, int N, int K, int batches, int npad) {
+  if (M <= 0 || N <= 0 || K <= 0 || batches <= 0 || !skinny_path(M, N, npad)) return 1;
+  const long long wgs = (long long)((N + 31) / 32) * batches;
+  if (wgs >= 64) return 1;
+  const int want = (int)((256 + wgs - 1) / wgs);
+  const int most = K / 64 / 4;
+  const int z = want < most ? want : most;
+  if (z <= 1) return 1;
+  const int per = (K / 64 + z - 1) / z;  // no empty slice
+  return (K / 64 + per - 1) / per;
+}
+
+size_t gemm_part_bytes(int M, int N, int K, int batches, int npad) {
+  const int z = gemm_ksplit(M, N, K, batches, npad);
+  return z > 1 ? (size_t)z * batches * M * (size_t)((N + 3) & ~3) * 4 : 0;
+}
+
+hipError_t launch_gemm_group_bf16(GemmGroup gg, hipStream_t st) {
+  const GemmArgs& b = gg.base;
+  if (gg.count < 1 || gg.count > 4 || b.M <= 0 || b.M > 64 || b.K % 64 != 0) return hipErrorInvalidValue;
+  if ((long long)b.M * b.lda * 2 >= (1LL << 32)) return hipErrorInvalidValue;
+  int first = 0;
+  for (int s = 0; s < 4; ++s) {
+    if (s < gg.count) {
+      if (gg.N[s] <= 0 || gg.N[s] % 4 != 0 || (long long)gg.N[s] * gg.ldw[s] * 2 >= (1LL << 32))
+        return hipErrorInvalidValue;
+      if (s > 0) gg.first_wg[s] = first;
+      first += (gg.N[s] + 31) / 32;
+    } else {
+      gg.first_wg[s] = INT32_MAX;  // no workgroup reaches an unused segment
+    }
+  }
+  gg.first_wg[0] = 0;
+  gg.base.batches = 1;
+  gg.base.ksplit = 1;
+  gg.base.epi = EPI_STORE;
+  gg.base.npad = 0;
+  using C1 = SkinnyCfg<1>;
+  using C2 = SkinnyCfg<2>;
+  auto k1 = gemm_skinny_group_kernel<1>;
+  auto k2 = gemm_skinny_group_kernel<2>;
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)k1, hipFuncAttributeMaxDynamicSharedMemorySize, C1::LDS_BYTES);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)k2, hipFuncAttributeMaxDynamicSharedMemorySize, C2::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  return b.M <= 32 ? launch(k1, dim3(first), dim3(256), C1::LDS_BYTES, st, gg)
+                   : launch(k2, dim3(first), dim3(256), C2::LDS_BYTES, st, gg);
 }
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t st) {

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -97,6 +98,14 @@ GemmArgs gemm(const void* A, int64_t lda, const void* W, int64_t ldw, void* C, i
   g.epi = epi;
   return g;
 }
+// Give a bf16 GEMM its split-K plan and partial-sum space (shared by the
+// GEMMs of one call, which run one after another on its stream).
+GemmArgs with_split(GemmArgs g, void* part) {
+  g.ksplit = gemm_ksplit(g.M, g.N, g.K, g.batches, g.npad);
+  g.part = g.ksplit > 1 ? (float*)part : nullptr;
+  return g;
+}
+
 GemmF32Args gemm32(const void* A, int64_t lda, const void* W, int64_t ldw, void* C, int64_t ldc, int M, int N, int K,
                    int epi = EPI_STORE, const void* O = nullptr, int64_t ldo = 0) {
   GemmF32Args g{};
@@ -269,8 +278,8 @@ gmla_status_t gmla_decode(const void* q_abs, const void* cache, const int64_t* s
 }
 
 // ============================================================ decode-step projections
-size_t gmla_decode_prepare_workspace_size(int B, int H, int d_c, int d_k, int d_r, gmla_dtype_t dtype) {
-  if (B <= 0 || H <= 0 || d_c <= 0 || d_k <= 0 || d_r < 0 || dtype != GMLA_BF16) return 0;
+size_t gmla_decode_prepare_workspace_size(int B, int d_model, int H, int d_c, int d_k, int d_r, gmla_dtype_t dtype) {
+  if (B <= 0 || d_model <= 0 || H <= 0 || d_c <= 0 || d_k <= 0 || d_r < 0 || dtype != GMLA_BF16) return 0;
   return up256((size_t)B * (d_c + d_r) * 2) + up256((size_t)B * H * d_k * 2) + up256((size_t)B * H * d_r * 2);
 }
 
@@ -292,7 +301,7 @@ gmla_status_t gmla_decode_prepare(const void* x, const void* W_c, const void* W_
   REQUIRE(dtype == GMLA_BF16, GMLA_ERR_UNSUPPORTED, "decode_prepare is bf16 only");
   REQUIRE(d_model % 64 == 0 && d_c % 64 == 0 && d_k <= 128 && d_k % 16 == 0 && d_r % 4 == 0, GMLA_ERR_UNSUPPORTED,
           "bf16 decode_prepare needs d_model % 64 == 0, d_c % 64 == 0, d_k % 16 == 0, d_k <= 128, d_r % 4 == 0");
-  const size_t need = gmla_decode_prepare_workspace_size(B, H, d_c, d_k, d_r, dtype);
+  const size_t need = gmla_decode_prepare_workspace_size(B, d_model, H, d_c, d_k, d_r, dtype);
   REQUIRE(workspace && workspace_bytes >= need, GMLA_ERR_WORKSPACE,
           "decode_prepare workspace needs " + std::to_string(need) + " bytes");
   REQUIRE(((uintptr_t)workspace & 255u) == 0, GMLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
@@ -303,14 +312,29 @@ gmla_status_t gmla_decode_prepare(const void* x, const void* W_c, const void* W_
   bf16* q = (bf16*)(ws + up256((size_t)B * W * 2));
   bf16* qr = (bf16*)(ws + up256((size_t)B * W * 2) + up256((size_t)B * H * d_k * 2));
   gmla_status_t s;
-  if ((s = run("gemm_latent", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_c, d_model, row, W, B, d_c, d_model), st); }))) return s;
-  if (d_r > 0 &&
-      (s = run("gemm_rope_key", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_kr, d_model, row + d_c, W, B, d_r, d_model), st); })))
-    return s;
-  if ((s = run("gemm_query", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_q, d_model, q, H * d_k, B, H * d_k, d_model), st); }))) return s;
-  if (d_r > 0 &&
-      (s = run("gemm_rope_query", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_qr, d_model, qr, H * d_r, B, H * d_r, d_model), st); })))
-    return s;
+  if (B <= 64) {
+    // the four projections of x in one weight-streaming launch
+    GemmGroup gg{};
+    gg.base = gemm(x, d_model, nullptr, d_model, nullptr, 0, B, 0, d_model);
+    const void* Ws[4] = {W_c, W_q, W_kr, W_qr};
+    bf16* Cs[4] = {row, q, row + d_c, qr};
+    const int Ns[4] = {d_c, H * d_k, d_r, H * d_r};
+    const int64_t ldcs[4] = {W, (int64_t)H * d_k, W, (int64_t)H * d_r};
+    gg.count = d_r > 0 ? 4 : 2;
+    for (int i = 0; i < gg.count; ++i) {
+      gg.W[i] = (const bf16*)Ws[i]; gg.C[i] = Cs[i]; gg.N[i] = Ns[i]; gg.ldw[i] = d_model; gg.ldc[i] = ldcs[i];
+    }
+    if ((s = run("gemm_input", st, [&] { return launch_gemm_group_bf16(gg, st); }))) return s;
+  } else {
+    if ((s = run("gemm_latent", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_c, d_model, row, W, B, d_c, d_model), st); }))) return s;
+    if (d_r > 0 &&
+        (s = run("gemm_rope_key", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_kr, d_model, row + d_c, W, B, d_r, d_model), st); })))
+      return s;
+    if ((s = run("gemm_query", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_q, d_model, q, H * d_k, B, H * d_k, d_model), st); }))) return s;
+    if (d_r > 0 &&
+        (s = run("gemm_rope_query", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_qr, d_model, qr, H * d_r, B, H * d_r, d_model), st); })))
+      return s;
+  }
   PrepareArgs a{};
   a.row = row; a.q = q; a.q_r = qr; a.W_uk = (const bf16*)W_uk; a.cache = (bf16*)cache;
   a.seq_start = seq_start; a.seq_len = seq_len; a.q_abs = (bf16*)q_abs;
@@ -322,10 +346,21 @@ gmla_status_t gmla_decode_prepare(const void* x, const void* W_c, const void* W_
 }
 
 // ============================================================ gate + output
-size_t gmla_gate_out_workspace_size(int T, int H, int d_v, int with_value_up, gmla_dtype_t dtype) {
-  if (T <= 0 || H <= 0 || d_v <= 0) return 0;
+// Split-K partial sums of the gate_out GEMMs (bf16, T <= 64): the largest.
+static size_t gate_out_part_bytes(int T, int d_model, int H, int d_c, int d_v, int with_value_up) {
+  const int HV = H * d_v;
+  size_t p = std::max(gemm_part_bytes(T, HV, d_model, 1), gemm_part_bytes(T, d_model, HV, 1));
+  if (with_value_up) p = std::max(p, gemm_part_bytes(T, d_v, d_c, H));
+  return up256(p);
+}
+
+size_t gmla_gate_out_workspace_size(int T, int d_model, int H, int d_c, int d_v, int with_value_up,
+                                    gmla_dtype_t dtype) {
+  if (T <= 0 || d_model <= 0 || H <= 0 || d_v <= 0 || (with_value_up && d_c <= 0)) return 0;
   const size_t one = up256((size_t)T * H * d_v * esize(dtype));
-  return with_value_up ? 2 * one : one;
+  const size_t base = with_value_up ? 2 * one : one;
+  if (dtype != GMLA_BF16) return base;
+  return base + gate_out_part_bytes(T, d_model, H, d_c, d_v, with_value_up);
 }
 
 gmla_status_t gmla_gate_out(const void* x, const void* o, const void* W_uv, const void* W_g, const void* W_o, void* y,
@@ -343,7 +378,7 @@ gmla_status_t gmla_gate_out(const void* x, const void* o, const void* W_uv, cons
             "bf16 gate_out needs d_model % 64 == 0, H*d_v % 64 == 0, d_v % 4 == 0");
     REQUIRE(!W_uv || d_c % 64 == 0, GMLA_ERR_UNSUPPORTED, "bf16 value up-projection needs d_c % 64 == 0");
   }
-  const size_t need = gmla_gate_out_workspace_size(T, H, d_v, W_uv != nullptr, dtype);
+  const size_t need = gmla_gate_out_workspace_size(T, d_model, H, d_c, d_v, W_uv != nullptr, dtype);
   REQUIRE(workspace && workspace_bytes >= need, GMLA_ERR_WORKSPACE,
           "gate_out workspace needs " + std::to_string(need) + " bytes");
   REQUIRE(al16(workspace), GMLA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
@@ -354,15 +389,17 @@ gmla_status_t gmla_gate_out(const void* x, const void* o, const void* W_uv, cons
   const void* ot = o;
   gmla_status_t s;
   if (dtype == GMLA_BF16) {
+    void* part = ws + (W_uv ? 2 : 1) * up256((size_t)T * HV * es);
     if (W_uv) {
       void* otw = ws + up256((size_t)T * HV * es);
       GemmArgs g = gemm(o, (int64_t)H * d_c, W_uv, d_c, otw, HV, T, d_v, d_c);
       g.batches = H; g.sA = d_c; g.sW = (int64_t)d_v * d_c; g.sC = d_v;
+      g = with_split(g, part);
       if ((s = run("gemm_value_up", st, [&] { return launch_gemm_bf16(g, st); }))) return s;
       ot = otw;
     }
-    if ((s = run("gemm_gate", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_g, d_model, gated, HV, T, HV, d_model, EPI_GATE, ot, HV), st); }))) return s;
-    if ((s = run("gemm_out", st, [&] { return launch_gemm_bf16(gemm(gated, HV, W_o, HV, y, d_model, T, d_model, HV), st); }))) return s;
+    if ((s = run("gemm_gate", st, [&] { return launch_gemm_bf16(with_split(gemm(x, d_model, W_g, d_model, gated, HV, T, HV, d_model, EPI_GATE, ot, HV), part), st); }))) return s;
+    if ((s = run("gemm_out", st, [&] { return launch_gemm_bf16(with_split(gemm(gated, HV, W_o, HV, y, d_model, T, d_model, HV), part), st); }))) return s;
   } else {
     if (W_uv) {
       void* otw = ws + up256((size_t)T * HV * es);

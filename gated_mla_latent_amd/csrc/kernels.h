@@ -9,7 +9,9 @@ namespace gmla {
 // Every kernel goes out through launch(). While the C-ABI layer traces a
 // call it points g_launch_events at a pair of events, and launch() has the
 // kernel's own dispatch record them (hipExtLaunchKernelGGL), so the pair
-// brackets that kernel alone rather than also the queue work around it.
+// brackets that kernel alone rather than also the queue work around it. When
+// one traced call launches several kernels, the first records the start and
+// each records the stop: the pair spans all of them.
 struct LaunchEvents {
   hipEvent_t start, stop;
   int launched;
@@ -19,7 +21,8 @@ extern thread_local LaunchEvents* g_launch_events;
 template <typename K, typename... Args>
 inline hipError_t launch(K kern, dim3 grid, dim3 block, unsigned shmem, hipStream_t st, Args... args) {
   if (LaunchEvents* ev = g_launch_events) {
-    hipExtLaunchKernelGGL(kern, grid, block, shmem, st, ev->start, ev->stop, 0, args...);
+    hipExtLaunchKernelGGL(kern, grid, block, shmem, st, ev->launched == 0 ? ev->start : nullptr, ev->stop, 0,
+                          args...);
     ++ev->launched;
   } else {
     hipLaunchKernelGGL(kern, grid, block, shmem, st, args...);
@@ -81,8 +84,27 @@ struct GemmArgs {
   int64_t sA, sW, sC, sO;   // batch strides (elements)
   int epi;
   int npad;                 // EPI_STORE: columns N .. npad - 1 of C are written as zeros (<= N: none)
+  float* part;              // split-K partial sums (gemm_ksplit(...) > 1): gemm_part_bytes(...) bytes
+  int ksplit;               // K slices of the skinny kernel (<= 1: none)
 };
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t st);
+// Split-K plan of the skinny kernel (M <= 64) for an under-filled grid, and
+// the fp32 partial-sum space it needs (0 when it does not split).
+int gemm_ksplit(int M, int N, int K, int batches, int npad = 0);
+size_t gemm_part_bytes(int M, int N, int K, int batches, int npad = 0);
+// Up to four plain-store GEMMs C_s = A W_s^T sharing A, M <= 64 and K, in one
+// launch (base gives A, lda, M, K; segment s its W, ldw, C, ldc, N;
+// first_wg is filled by the launcher; count 1..4).
+struct GemmGroup {
+  GemmArgs base;
+  const bf16* W[4];
+  bf16* C[4];
+  int N[4];
+  int64_t ldw[4], ldc[4];
+  int first_wg[4];
+  int count;
+};
+hipError_t launch_gemm_group_bf16(GemmGroup gg, hipStream_t st);
 
 // ---------------------------------------------------------------- prefill attention
 // Causal flash attention, one head per (b, h): q,k,v rows of width D.

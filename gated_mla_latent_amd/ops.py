@@ -51,11 +51,11 @@ def lib():
     L.gmla_decode_workspace_size.restype = sz
     L.gmla_decode.argtypes = [vp] * 6 + [vp, sz] + [i32] * 4 + [f32, f32, i32, i32, vp]
     L.gmla_decode.restype = i32
-    L.gmla_decode_prepare_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.gmla_decode_prepare_workspace_size.argtypes = [i32] * 7
     L.gmla_decode_prepare_workspace_size.restype = sz
     L.gmla_decode_prepare.argtypes = [vp] * 10 + [vp, sz] + [i32] * 6 + [f32, i32, vp]
     L.gmla_decode_prepare.restype = i32
-    L.gmla_gate_out_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    L.gmla_gate_out_workspace_size.argtypes = [i32] * 7
     L.gmla_gate_out_workspace_size.restype = sz
     L.gmla_gate_out.argtypes = [vp] * 6 + [vp, sz] + [i32] * 5 + [i32, vp]
     L.gmla_gate_out.restype = i32
@@ -173,7 +173,7 @@ def decode_prepare(x, W_c, W_kr, W_q, W_qr, W_uk, cache, seq_start, seq_len, rop
     dt = _dtype_code(x)
     if q_abs is None:
         q_abs = torch.empty((B, H, d_c + d_r), dtype=x.dtype, device=x.device)
-    need = lib().gmla_decode_prepare_workspace_size(B, H, d_c, d_k, d_r, dt)
+    need = lib().gmla_decode_prepare_workspace_size(B, D, H, d_c, d_k, d_r, dt)
     workspace, wsb = _workspace(need, x.device, workspace)
     _check(lib().gmla_decode_prepare(_vp(x), _vp(W_c), _vp(W_kr), _vp(W_q), _vp(W_qr), _vp(W_uk), _vp(cache),
                                      _vp(seq_start), _vp(seq_len), _vp(q_abs), _vp(workspace), wsb, B, D, H, d_c,
@@ -196,7 +196,7 @@ def gate_out(x, o, W_g, W_o, W_uv=None, y=None, workspace=None):
     dt = _dtype_code(x)
     if y is None:
         y = torch.empty((T, D), dtype=x.dtype, device=x.device)
-    need = lib().gmla_gate_out_workspace_size(T, H, d_v, int(W_uv is not None), dt)
+    need = lib().gmla_gate_out_workspace_size(T, D, H, d_c, d_v, int(W_uv is not None), dt)
     workspace, wsb = _workspace(need, x.device, workspace)
     _check(lib().gmla_gate_out(_vp(x), _vp(o), _vp(W_uv), _vp(W_g), _vp(W_o), _vp(y), _vp(workspace), wsb,
                                T, D, H, d_c, d_v, dt, _stream()))

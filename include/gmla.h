@@ -132,11 +132,12 @@ gmla_status_t gmla_decode(const void* q_abs, const void* cache, const int64_t* s
  * RoPE pairs are interleaved (2i, 2i+1), theta_i = rope_base^(-2i/d_r);
  * rope_base == 0 leaves the key unrotated. The target rows must lie inside
  * `cache` and differ between sequences (trusted, read on the device).
+ * The workspace holds the projections of x before the append and the absorb.
  * Only GMLA_BF16 is supported (GMLA_ERR_UNSUPPORTED otherwise); it needs
  * d_model % 64 == 0, d_c % 64 == 0, d_k % 16 == 0, d_k <= 128 and
  * d_r % 4 == 0.
  * ---------------------------------------------------------------------- */
-size_t gmla_decode_prepare_workspace_size(int B, int H, int d_c, int d_k, int d_r, gmla_dtype_t dtype);
+size_t gmla_decode_prepare_workspace_size(int B, int d_model, int H, int d_c, int d_k, int d_r, gmla_dtype_t dtype);
 gmla_status_t gmla_decode_prepare(const void* x, const void* W_c, const void* W_kr, const void* W_q, const void* W_qr,
                                   const void* W_uk, void* cache, const int64_t* seq_start, const int32_t* seq_len,
                                   void* q_abs, void* workspace, size_t workspace_bytes, int B, int d_model, int H,
@@ -151,9 +152,13 @@ gmla_status_t gmla_decode_prepare(const void* x, const void* W_c, const void* W_
  * pre-multiplied into W_o because the gate between them is per channel).
  *   x [T, d_model], W_g [H*d_v, d_model], W_o [d_model, H*d_v], y [T, d_model]
  * BF16 needs d_model % 64 == 0, (H*d_v) % 64 == 0, d_c % 64 == 0 and
- * d_v % 4 == 0.
+ * d_v % 4 == 0. The workspace holds gated (and o~ when W_uv is given) and,
+ * for T <= 64 with bf16, the fp32 partial sums of GEMMs whose K is split
+ * across workgroups; its size depends on every argument of the size query
+ * (d_c is ignored without the value up-projection).
  * ---------------------------------------------------------------------- */
-size_t gmla_gate_out_workspace_size(int T, int H, int d_v, int with_value_up, gmla_dtype_t dtype);
+size_t gmla_gate_out_workspace_size(int T, int d_model, int H, int d_c, int d_v, int with_value_up,
+                                    gmla_dtype_t dtype);
 gmla_status_t gmla_gate_out(const void* x, const void* o, const void* W_uv, const void* W_g, const void* W_o,
                             void* y, void* workspace, size_t workspace_bytes, int T, int d_model, int H, int d_c,
                             int d_v, gmla_dtype_t dtype, void* stream);

@@ -136,14 +136,56 @@ def test_decode_prepare_argument_checks(L):
     assert _prep(L, ws=A + 16) == INVALID           # workspace must be 256-byte aligned
 
 
+def _ksplit(M, N, K, batches):
+    """The documented split-K rule of the skinny GEMM (M <= 64): split when the
+    grid has fewer than 64 workgroups of 32 columns, towards 256 workgroups,
+    keeping at least four 64-wide K chunks per workgroup and no empty slice."""
+    wgs = (N + 31) // 32 * batches
+    if M > 64 or wgs >= 64:
+        return 1
+    z = min(-(-256 // wgs), K // 64 // 4)
+    if z <= 1:
+        return 1
+    per = -(-(K // 64) // z)
+    return -(-(K // 64) // per)
+
+
+def _part(M, N, K, batches=1):
+    z = _ksplit(M, N, K, batches)
+    return z * batches * M * ((N + 3) // 4 * 4) * 4 if z > 1 else 0
+
+
+def test_split_k_rule_examples():
+    assert _ksplit(64, 512, 7168, 1) == 16      # 16 workgroups -> 256
+    assert _ksplit(64, 128, 7168, 1) == 28      # 4 workgroups, capped at 4 chunks each
+    assert _ksplit(64, 64, 7168, 1) == 28
+    assert _ksplit(64, 16384, 7168, 1) == 1     # 512 workgroups already
+    assert _ksplit(64, 7168, 16384, 1) == 1     # 224: not split
+    assert _ksplit(64, 128, 512, 128) == 1      # batched value up-projection: 512
+    assert _ksplit(65, 512, 7168, 1) == 1       # tile kernel, no split
+
+
 def test_decode_prepare_workspace_size_formula(L):
     up = lambda n: (n + 255) // 256 * 256
-    for B, H, d_c, d_k, d_r in [(4, 16, 512, 128, 64), (37, 128, 512, 128, 0), (1, 3, 64, 32, 4)]:
+    for B, D, H, d_c, d_k, d_r in [(4, 256, 16, 512, 128, 64), (37, 7168, 128, 512, 128, 0), (1, 192, 3, 64, 32, 4),
+                                   (64, 7168, 128, 512, 128, 64)]:
         # new cache rows [B, d_c + d_r], queries [B, H d_k], RoPE queries [B, H d_r]
         want = up(B * (d_c + d_r) * 2) + up(B * H * d_k * 2) + up(B * H * d_r * 2)
-        assert L.gmla_decode_prepare_workspace_size(B, H, d_c, d_k, d_r, 1) == want
-    assert L.gmla_decode_prepare_workspace_size(4, 16, 512, 128, 64, 0) == 0
-    assert L.gmla_decode_prepare_workspace_size(0, 16, 512, 128, 64, 1) == 0
+        assert L.gmla_decode_prepare_workspace_size(B, D, H, d_c, d_k, d_r, 1) == want
+    assert L.gmla_decode_prepare_workspace_size(4, 256, 16, 512, 128, 64, 0) == 0
+    assert L.gmla_decode_prepare_workspace_size(0, 256, 16, 512, 128, 64, 1) == 0
+
+
+def test_gate_out_workspace_size_formula(L):
+    up = lambda n: (n + 255) // 256 * 256
+    for T, D, H, d_c, d_v, vu in [(4, 256, 2, 512, 64, 1), (32, 7168, 64, 512, 128, 1), (64, 7168, 128, 512, 128, 1),
+                                  (8, 7168, 128, 512, 128, 1), (16384, 7168, 1, 0, 8192, 0)]:
+        HV = H * d_v
+        part = max(_part(T, HV, D), _part(T, D, HV), _part(T, d_v, d_c, H) if vu else 0)
+        want = (2 if vu else 1) * up(T * HV * 2) + up(part)
+        assert L.gmla_gate_out_workspace_size(T, D, H, d_c, d_v, vu, 1) == want
+    assert L.gmla_gate_out_workspace_size(4, 256, 2, 64, 64, 1, 0) == 2 * up(4 * 2 * 64 * 4)  # fp32: no split
+    assert L.gmla_gate_out_workspace_size(4, 256, 2, 0, 64, 1, 1) == 0  # value up-projection needs d_c
 
 
 def _gate(L, **kw):
@@ -160,7 +202,6 @@ def test_gate_out_argument_checks(L):
     assert _gate(L, D=200) == UNSUPPORTED
     assert _gate(L, Wuv=A, d_c=100) == UNSUPPORTED
     assert _gate(L, wsb=10) == WORKSPACE
-    assert L.gmla_gate_out_workspace_size(4, 2, 64, 1, 1) == 2 * 256 * ((4 * 2 * 64 * 2 + 255) // 256)
 
 
 def test_trace_api_without_launches(L):
