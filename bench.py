@@ -157,7 +157,7 @@ def build_decode(args, inp, torch, ops):
     rows_new = torch.empty((inp.B, inp.d_c + inp.d_r), dtype=torch.bfloat16, device=dev)
     start_new = (torch.arange(inp.B, dtype=torch.int64) - inp.seq_len.to(torch.int64)).to(dev)
     q_new = torch.empty((inp.B, inp.H, inp.d_c + inp.d_r), dtype=torch.bfloat16, device=dev)
-    wsp_n = L.gmla_decode_prepare_workspace_size(inp.B, inp.d_model, inp.H, inp.d_c, DECODE_D_K, inp.d_r, 1)
+    wsp_n = L.gmla_decode_prepare_workspace_size(inp.B, inp.d_model, inp.H, inp.d_c, 0, DECODE_D_K, inp.d_r, 1)
     wsp = torch.empty(wsp_n, dtype=torch.uint8, device=dev)
     o_lat = torch.empty((inp.B, inp.H, inp.d_c), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((inp.B, inp.H), dtype=torch.float32, device=dev)
@@ -173,9 +173,9 @@ def build_decode(args, inp, torch, ops):
                stream)
         go = (_vp(x), _vp(o_lat), _vp(c["W_uv"]), _vp(c["W_g"]), _vp(c["W_o"]), _vp(y), _vp(wsg), C.c_size_t(wsg_n),
               inp.B, inp.d_model, inp.H, inp.d_c, inp.d_v, 1, stream)
-        pre = (_vp(x_new), _vp(c["W_c"]), _vp(c["W_kr"]), _vp(c["W_q"]), _vp(c["W_qr"]), _vp(c["W_uk"]),
+        pre = (_vp(x_new), _vp(c["W_c"]), _vp(c["W_kr"]), C.c_void_p(0), _vp(c["W_q"]), _vp(c["W_qr"]), _vp(c["W_uk"]),
                _vp(rows_new), _vp(start_new), _vp(seq_len), _vp(q_new), _vp(wsp), C.c_size_t(wsp_n), inp.B,
-               inp.d_model, inp.H, inp.d_c, DECODE_D_K, inp.d_r, C.c_float(inp.rope_base), 1, stream)
+               inp.d_model, inp.H, inp.d_c, 0, DECODE_D_K, inp.d_r, C.c_float(inp.rope_base), 1, stream)
         calls.append((dec, go, pre))
     keep = (q, seq_start, seq_len, x, copies, o_lat, lse, y, wsd, wsg, x_new, rows_new, start_new, q_new, wsp)
 
@@ -209,14 +209,16 @@ def build_prefill(args, p, torch, ops):
     lat = torch.empty((p.B, p.L, p.d_c), dtype=p.dtype, device=dev)
     ot = torch.empty((p.B, p.L, p.H * p.d_v), dtype=p.dtype, device=dev)
     y = torch.empty((T, p.d_model), dtype=p.dtype, device=dev)
-    wsp_n = L.gmla_prefill_workspace_size(p.B, p.L, p.H, p.d_k, p.d_v, dt)
+    wsp_n = L.gmla_prefill_workspace_size(p.B, p.L, p.H, 0, p.d_k, 0, p.d_v, dt)
     wsg_n = L.gmla_gate_out_workspace_size(T, p.d_model, 1, 0, p.H * p.d_v, 0, dt)
     wsp = torch.empty(wsp_n, dtype=torch.uint8, device=dev)
     wsg = torch.empty(wsg_n, dtype=torch.uint8, device=dev)
     calls = []
     for c in copies:
-        pre = (_vp(c["x"]), _vp(c["W_c"]), _vp(c["W_q"]), _vp(c["W_uk"]), _vp(c["W_uv"]), _vp(lat), _vp(ot), _vp(wsp),
-               C.c_size_t(wsp_n), p.B, p.L, p.d_model, p.H, p.d_c, p.d_k, p.d_v, C.c_float(p.sm_scale), dt, stream)
+        nul = C.c_void_p(0)
+        pre = (_vp(c["x"]), _vp(c["W_c"]), nul, _vp(c["W_q"]), nul, nul, _vp(c["W_uk"]), _vp(c["W_uv"]), _vp(lat),
+               _vp(ot), _vp(wsp), C.c_size_t(wsp_n), p.B, p.L, p.d_model, p.H, p.d_c, 0, p.d_k, 0, p.d_v,
+               C.c_float(p.sm_scale), C.c_float(0.0), dt, stream)
         go = (_vp(c["x"]), _vp(ot), C.c_void_p(0), _vp(c["W_g"]), _vp(c["W_o"]), _vp(y), _vp(wsg), C.c_size_t(wsg_n),
               T, p.d_model, 1, 0, p.H * p.d_v, dt, stream)
         calls.append((pre, go))

@@ -140,36 +140,46 @@ int gmla_version(void) { return 10000; }
 // contiguous, rows padded with zeros to Lp = L rounded up to 64 (one key tile)
 static size_t prefill_vt_ld(int L) { return ((size_t)L + 63) / 64 * 64; }
 
-size_t gmla_prefill_workspace_size(int B, int L, int H, int d_k, int d_v, gmla_dtype_t dtype) {
-  if (B <= 0 || L <= 0 || H <= 0 || d_k <= 0 || d_v <= 0) return 0;
+size_t gmla_prefill_workspace_size(int B, int L, int H, int d_cq, int d_k, int d_r, int d_v, gmla_dtype_t dtype) {
+  if (B <= 0 || L <= 0 || H <= 0 || d_cq < 0 || d_k <= 0 || d_r < 0 || d_v <= 0) return 0;
   const size_t T = (size_t)B * L;
   const size_t es = esize(dtype);
   const size_t v_elems = dtype == GMLA_BF16 ? (size_t)B * H * d_v * prefill_vt_ld(L) : T * H * d_v;
-  return up256(T * H * d_k * es) * 2 + up256(v_elems * es);
+  // q and K ([T, H (d_k + d_r)]), V, then the low-rank query c^Q [T, d_cq]
+  return up256(T * H * (d_k + d_r) * es) * 2 + up256(v_elems * es) + up256(T * d_cq * es);
 }
 
-gmla_status_t gmla_prefill(const void* x, const void* W_c, const void* W_q, const void* W_uk, const void* W_uv,
-                           void* latent_out, void* o_tilde, void* workspace, size_t workspace_bytes, int B, int L,
-                           int d_model, int H, int d_c, int d_k, int d_v, float sm_scale, gmla_dtype_t dtype,
+gmla_status_t gmla_prefill(const void* x, const void* W_c, const void* W_dq, const void* W_q, const void* W_kr,
+                           const void* W_qr, const void* W_uk, const void* W_uv, void* latent_out, void* o_tilde,
+                           void* workspace, size_t workspace_bytes, int B, int L, int d_model, int H, int d_c,
+                           int d_cq, int d_k, int d_r, int d_v, float sm_scale, float rope_base, gmla_dtype_t dtype,
                            void* stream) {
   REQUIRE(dtype == GMLA_F32 || dtype == GMLA_BF16, GMLA_ERR_INVALID_ARG, "dtype must be GMLA_F32 or GMLA_BF16");
   REQUIRE(x && W_c && W_q && W_uk && W_uv && latent_out && o_tilde, GMLA_ERR_INVALID_ARG, "null tensor pointer");
-  REQUIRE(B > 0 && L > 0 && d_model > 0 && H > 0 && d_c > 0 && d_k > 0 && d_v > 0, GMLA_ERR_INVALID_ARG,
-          "sizes must be positive");
-  REQUIRE(std::isfinite(sm_scale), GMLA_ERR_INVALID_ARG, "sm_scale must be finite");
-  REQUIRE(al16(x) && al16(W_c) && al16(W_q) && al16(W_uk) && al16(W_uv) && al16(latent_out) && al16(o_tilde),
+  REQUIRE(B > 0 && L > 0 && d_model > 0 && H > 0 && d_c > 0 && d_k > 0 && d_v > 0 && d_cq >= 0 && d_r >= 0,
+          GMLA_ERR_INVALID_ARG, "sizes must be positive (d_cq, d_r >= 0)");
+  REQUIRE((W_dq != nullptr) == (d_cq > 0), GMLA_ERR_INVALID_ARG, "W_dq is given exactly when d_cq > 0");
+  REQUIRE((W_kr != nullptr && W_qr != nullptr) == (d_r > 0) && (W_kr != nullptr) == (W_qr != nullptr),
+          GMLA_ERR_INVALID_ARG, "W_kr and W_qr are given exactly when d_r > 0");
+  REQUIRE(d_r % 2 == 0, GMLA_ERR_INVALID_ARG, "d_r must be even (RoPE pairs)");
+  REQUIRE(std::isfinite(sm_scale) && std::isfinite(rope_base) && rope_base >= 0.f, GMLA_ERR_INVALID_ARG,
+          "sm_scale must be finite and rope_base finite and >= 0");
+  REQUIRE(al16(x) && al16(W_c) && (!W_dq || al16(W_dq)) && al16(W_q) && (!W_kr || al16(W_kr)) &&
+              (!W_qr || al16(W_qr)) && al16(W_uk) && al16(W_uv) && al16(latent_out) && al16(o_tilde),
           GMLA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
-  REQUIRE((long long)B * L * std::max(std::max(d_model, H * d_k), H * d_v) < (1LL << 40), GMLA_ERR_UNSUPPORTED,
+  REQUIRE((long long)B * L * std::max({d_model, H * (d_k + d_r), H * d_v, d_cq}) < (1LL << 40), GMLA_ERR_UNSUPPORTED,
           "problem too large");
+  REQUIRE(d_r == 0, GMLA_ERR_UNSUPPORTED, "decoupled RoPE in prefill is not built");
   if (dtype == GMLA_BF16) {
     REQUIRE(d_model % 64 == 0, GMLA_ERR_UNSUPPORTED, "bf16 prefill needs d_model % 64 == 0");
     REQUIRE(d_c % 64 == 0, GMLA_ERR_UNSUPPORTED, "bf16 prefill needs d_c % 64 == 0");
+    REQUIRE(d_cq % 64 == 0, GMLA_ERR_UNSUPPORTED, "bf16 prefill needs d_cq % 64 == 0");
     REQUIRE(d_k == d_v && (d_k == 64 || d_k == 128), GMLA_ERR_UNSUPPORTED,
             "bf16 prefill needs d_k == d_v in {64, 128}");
   } else {
     REQUIRE(d_k <= 1024 && d_v <= 512, GMLA_ERR_UNSUPPORTED, "fp32 prefill needs d_k <= 1024, d_v <= 512");
   }
-  const size_t need = gmla_prefill_workspace_size(B, L, H, d_k, d_v, dtype);
+  const size_t need = gmla_prefill_workspace_size(B, L, H, d_cq, d_k, d_r, d_v, dtype);
   REQUIRE(workspace && workspace_bytes >= need, GMLA_ERR_WORKSPACE,
           "prefill workspace needs " + std::to_string(need) + " bytes");
   REQUIRE(al16(workspace), GMLA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
@@ -181,12 +191,20 @@ gmla_status_t gmla_prefill(const void* x, const void* W_c, const void* W_q, cons
   void* q = ws;
   void* k = ws + up256((size_t)T * H * d_k * es);
   void* v = (char*)k + up256((size_t)T * H * d_k * es);
+  const size_t v_elems = dtype == GMLA_BF16 ? (size_t)B * H * d_v * prefill_vt_ld(L) : (size_t)T * H * d_v;
+  void* cq = (char*)v + up256(v_elems * es);
+  // the query side reads x, or the low-rank query c^Q = x W_dq^T
+  const void* xq = d_cq > 0 ? cq : x;
+  const int dq_in = d_cq > 0 ? d_cq : d_model;
   const int HK = H * d_k, HV = H * d_v;
   gmla_status_t s;
   if (dtype == GMLA_BF16) {
     // c = x W_c^T (cache rows), q = x W_q^T, K = c W_UK^T, V = c W_UV^T (W_UK as [H*d_k, d_c])
     if ((s = run("gemm_latent", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_c, d_model, latent_out, d_c, T, d_c, d_model), st); }))) return s;
-    if ((s = run("gemm_query", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_q, d_model, q, HK, T, HK, d_model), st); }))) return s;
+    if (d_cq > 0 &&
+        (s = run("gemm_query_down", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_dq, d_model, cq, d_cq, T, d_cq, d_model), st); })))
+      return s;
+    if ((s = run("gemm_query", st, [&] { return launch_gemm_bf16(gemm(xq, dq_in, W_q, dq_in, q, HK, T, HK, dq_in), st); }))) return s;
     if ((s = run("gemm_key_recon", st, [&] { return launch_gemm_bf16(gemm(latent_out, d_c, W_uk, d_c, k, HK, T, HK, d_c), st); }))) return s;
     // V^T per sequence: [H d_v, Lp] = W_UV c^T (the operands swapped), the
     // columns past L written as zeros
@@ -207,7 +225,10 @@ gmla_status_t gmla_prefill(const void* x, const void* W_c, const void* W_q, cons
     if ((s = run("prefill_attn", st, [&] { return launch_prefill_attn_bf16(a, st); }))) return s;
   } else {
     if ((s = run("gemm_f32", st, [&] { return launch_gemm_f32(gemm32(x, d_model, W_c, d_model, latent_out, d_c, T, d_c, d_model), st); }))) return s;
-    if ((s = run("gemm_f32", st, [&] { return launch_gemm_f32(gemm32(x, d_model, W_q, d_model, q, HK, T, HK, d_model), st); }))) return s;
+    if (d_cq > 0 &&
+        (s = run("gemm_f32", st, [&] { return launch_gemm_f32(gemm32(x, d_model, W_dq, d_model, cq, d_cq, T, d_cq, d_model), st); })))
+      return s;
+    if ((s = run("gemm_f32", st, [&] { return launch_gemm_f32(gemm32(xq, dq_in, W_q, dq_in, q, HK, T, HK, dq_in), st); }))) return s;
     if ((s = run("gemm_f32", st, [&] { return launch_gemm_f32(gemm32(latent_out, d_c, W_uk, d_c, k, HK, T, HK, d_c), st); }))) return s;
     if ((s = run("gemm_f32", st, [&] { return launch_gemm_f32(gemm32(latent_out, d_c, W_uv, d_c, v, HV, T, HV, d_c), st); }))) return s;
     AttnF32Args a{};
@@ -278,30 +299,35 @@ gmla_status_t gmla_decode(const void* q_abs, const void* cache, const int64_t* s
 }
 
 // ============================================================ decode-step projections
-size_t gmla_decode_prepare_workspace_size(int B, int d_model, int H, int d_c, int d_k, int d_r, gmla_dtype_t dtype) {
-  if (B <= 0 || d_model <= 0 || H <= 0 || d_c <= 0 || d_k <= 0 || d_r < 0 || dtype != GMLA_BF16) return 0;
-  return up256((size_t)B * (d_c + d_r) * 2) + up256((size_t)B * H * d_k * 2) + up256((size_t)B * H * d_r * 2);
+size_t gmla_decode_prepare_workspace_size(int B, int d_model, int H, int d_c, int d_cq, int d_k, int d_r,
+                                          gmla_dtype_t dtype) {
+  if (B <= 0 || d_model <= 0 || H <= 0 || d_c <= 0 || d_cq < 0 || d_k <= 0 || d_r < 0 || dtype != GMLA_BF16) return 0;
+  return up256((size_t)B * (d_c + d_r) * 2) + up256((size_t)B * H * d_k * 2) + up256((size_t)B * H * d_r * 2) +
+         up256((size_t)B * d_cq * 2);
 }
 
-gmla_status_t gmla_decode_prepare(const void* x, const void* W_c, const void* W_kr, const void* W_q, const void* W_qr,
-                                  const void* W_uk, void* cache, const int64_t* seq_start, const int32_t* seq_len,
-                                  void* q_abs, void* workspace, size_t workspace_bytes, int B, int d_model, int H,
-                                  int d_c, int d_k, int d_r, float rope_base, gmla_dtype_t dtype, void* stream) {
+gmla_status_t gmla_decode_prepare(const void* x, const void* W_c, const void* W_kr, const void* W_dq, const void* W_q,
+                                  const void* W_qr, const void* W_uk, void* cache, const int64_t* seq_start,
+                                  const int32_t* seq_len, void* q_abs, void* workspace, size_t workspace_bytes, int B,
+                                  int d_model, int H, int d_c, int d_cq, int d_k, int d_r, float rope_base,
+                                  gmla_dtype_t dtype, void* stream) {
   REQUIRE(dtype == GMLA_F32 || dtype == GMLA_BF16, GMLA_ERR_INVALID_ARG, "dtype must be GMLA_F32 or GMLA_BF16");
   REQUIRE(x && W_c && W_q && W_uk && cache && seq_start && seq_len && q_abs, GMLA_ERR_INVALID_ARG,
           "null tensor pointer");
-  REQUIRE(B > 0 && d_model > 0 && H > 0 && d_c > 0 && d_k > 0 && d_r >= 0, GMLA_ERR_INVALID_ARG,
-          "sizes must be positive (d_r >= 0)");
+  REQUIRE(B > 0 && d_model > 0 && H > 0 && d_c > 0 && d_k > 0 && d_r >= 0 && d_cq >= 0, GMLA_ERR_INVALID_ARG,
+          "sizes must be positive (d_cq, d_r >= 0)");
   REQUIRE(d_r == 0 || (W_kr && W_qr), GMLA_ERR_INVALID_ARG, "d_r > 0 needs W_kr and W_qr");
+  REQUIRE((W_dq != nullptr) == (d_cq > 0), GMLA_ERR_INVALID_ARG, "W_dq is given exactly when d_cq > 0");
   REQUIRE(d_r % 2 == 0, GMLA_ERR_INVALID_ARG, "d_r must be even (RoPE pairs)");
   REQUIRE(std::isfinite(rope_base) && rope_base >= 0.f, GMLA_ERR_INVALID_ARG, "rope_base must be finite and >= 0");
-  REQUIRE(al16(x) && al16(W_c) && (!d_r || (al16(W_kr) && al16(W_qr))) && al16(W_q) && al16(W_uk) && al16(cache) &&
-              al16(seq_start) && al16(seq_len) && al16(q_abs),
+  REQUIRE(al16(x) && al16(W_c) && (!d_r || (al16(W_kr) && al16(W_qr))) && (!W_dq || al16(W_dq)) && al16(W_q) &&
+              al16(W_uk) && al16(cache) && al16(seq_start) && al16(seq_len) && al16(q_abs),
           GMLA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   REQUIRE(dtype == GMLA_BF16, GMLA_ERR_UNSUPPORTED, "decode_prepare is bf16 only");
-  REQUIRE(d_model % 64 == 0 && d_c % 64 == 0 && d_k <= 128 && d_k % 16 == 0 && d_r % 4 == 0, GMLA_ERR_UNSUPPORTED,
-          "bf16 decode_prepare needs d_model % 64 == 0, d_c % 64 == 0, d_k % 16 == 0, d_k <= 128, d_r % 4 == 0");
-  const size_t need = gmla_decode_prepare_workspace_size(B, d_model, H, d_c, d_k, d_r, dtype);
+  REQUIRE(d_model % 64 == 0 && d_c % 64 == 0 && d_cq % 64 == 0 && d_k <= 128 && d_k % 16 == 0 && d_r % 4 == 0,
+          GMLA_ERR_UNSUPPORTED,
+          "bf16 decode_prepare needs d_model, d_c and d_cq % 64 == 0, d_k % 16 == 0, d_k <= 128, d_r % 4 == 0");
+  const size_t need = gmla_decode_prepare_workspace_size(B, d_model, H, d_c, d_cq, d_k, d_r, dtype);
   REQUIRE(workspace && workspace_bytes >= need, GMLA_ERR_WORKSPACE,
           "decode_prepare workspace needs " + std::to_string(need) + " bytes");
   REQUIRE(((uintptr_t)workspace & 255u) == 0, GMLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
@@ -311,28 +337,46 @@ gmla_status_t gmla_decode_prepare(const void* x, const void* W_c, const void* W_
   bf16* row = (bf16*)ws;
   bf16* q = (bf16*)(ws + up256((size_t)B * W * 2));
   bf16* qr = (bf16*)(ws + up256((size_t)B * W * 2) + up256((size_t)B * H * d_k * 2));
+  bf16* cq = (bf16*)(ws + up256((size_t)B * W * 2) + up256((size_t)B * H * d_k * 2) + up256((size_t)B * H * d_r * 2));
+  // the query side reads x, or the low-rank query c^Q = x W_dq^T
+  const void* xq = d_cq > 0 ? (const void*)cq : x;
+  const int dq_in = d_cq > 0 ? d_cq : d_model;
   gmla_status_t s;
   if (B <= 64) {
-    // the four projections of x in one weight-streaming launch
-    GemmGroup gg{};
-    gg.base = gemm(x, d_model, nullptr, d_model, nullptr, 0, B, 0, d_model);
-    const void* Ws[4] = {W_c, W_q, W_kr, W_qr};
-    bf16* Cs[4] = {row, q, row + d_c, qr};
-    const int Ns[4] = {d_c, H * d_k, d_r, H * d_r};
-    const int64_t ldcs[4] = {W, (int64_t)H * d_k, W, (int64_t)H * d_r};
-    gg.count = d_r > 0 ? 4 : 2;
-    for (int i = 0; i < gg.count; ++i) {
-      gg.W[i] = (const bf16*)Ws[i]; gg.C[i] = Cs[i]; gg.N[i] = Ns[i]; gg.ldw[i] = d_model; gg.ldc[i] = ldcs[i];
-    }
-    if ((s = run("gemm_input", st, [&] { return launch_gemm_group_bf16(gg, st); }))) return s;
+    // the projections of x in one weight-streaming launch, then (low-rank
+    // query) those of c^Q in a second
+    struct Seg { const void* w; bf16* c; int n; int64_t ldc; };
+    Seg from_x[4], from_q[2];
+    int nx = 0, nq = 0;
+    from_x[nx++] = {W_c, row, d_c, W};
+    if (d_r > 0) from_x[nx++] = {W_kr, row + d_c, d_r, W};
+    if (d_cq > 0) from_x[nx++] = {W_dq, cq, d_cq, d_cq};
+    Seg* qs = d_cq > 0 ? from_q : from_x;
+    int& nqs = d_cq > 0 ? nq : nx;
+    qs[nqs++] = {W_q, q, H * d_k, (int64_t)H * d_k};
+    if (d_r > 0) qs[nqs++] = {W_qr, qr, H * d_r, (int64_t)H * d_r};
+    auto group = [&](const void* A, int K, const Seg* sg, int n) {
+      GemmGroup gg{};
+      gg.base = gemm(A, K, nullptr, K, nullptr, 0, B, 0, K);
+      gg.count = n;
+      for (int i = 0; i < n; ++i) {
+        gg.W[i] = (const bf16*)sg[i].w; gg.C[i] = sg[i].c; gg.N[i] = sg[i].n; gg.ldw[i] = K; gg.ldc[i] = sg[i].ldc;
+      }
+      return launch_gemm_group_bf16(gg, st);
+    };
+    if ((s = run("gemm_input", st, [&] { return group(x, d_model, from_x, nx); }))) return s;
+    if (nq > 0 && (s = run("gemm_query_up", st, [&] { return group(cq, d_cq, from_q, nq); }))) return s;
   } else {
     if ((s = run("gemm_latent", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_c, d_model, row, W, B, d_c, d_model), st); }))) return s;
     if (d_r > 0 &&
         (s = run("gemm_rope_key", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_kr, d_model, row + d_c, W, B, d_r, d_model), st); })))
       return s;
-    if ((s = run("gemm_query", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_q, d_model, q, H * d_k, B, H * d_k, d_model), st); }))) return s;
+    if (d_cq > 0 &&
+        (s = run("gemm_query_down", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_dq, d_model, cq, d_cq, B, d_cq, d_model), st); })))
+      return s;
+    if ((s = run("gemm_query", st, [&] { return launch_gemm_bf16(gemm(xq, dq_in, W_q, dq_in, q, H * d_k, B, H * d_k, dq_in), st); }))) return s;
     if (d_r > 0 &&
-        (s = run("gemm_rope_query", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_qr, d_model, qr, H * d_r, B, H * d_r, d_model), st); })))
+        (s = run("gemm_rope_query", st, [&] { return launch_gemm_bf16(gemm(xq, dq_in, W_qr, dq_in, qr, H * d_r, B, H * d_r, dq_in), st); })))
       return s;
   }
   PrepareArgs a{};

@@ -43,17 +43,17 @@ def lib():
         raise RuntimeError(f"{LIB_PATH} not found: build it with `python -m gated_mla_latent_amd.build`")
     L = C.CDLL(LIB_PATH)
     vp, i32, f32, sz = C.c_void_p, C.c_int, C.c_float, C.c_size_t
-    L.gmla_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.gmla_prefill_workspace_size.argtypes = [i32] * 8
     L.gmla_prefill_workspace_size.restype = sz
-    L.gmla_prefill.argtypes = [vp] * 7 + [vp, sz] + [i32] * 7 + [f32, i32, vp]
+    L.gmla_prefill.argtypes = [vp] * 10 + [vp, sz] + [i32] * 9 + [f32, f32, i32, vp]
     L.gmla_prefill.restype = i32
     L.gmla_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     L.gmla_decode_workspace_size.restype = sz
     L.gmla_decode.argtypes = [vp] * 6 + [vp, sz] + [i32] * 4 + [f32, f32, i32, i32, vp]
     L.gmla_decode.restype = i32
-    L.gmla_decode_prepare_workspace_size.argtypes = [i32] * 7
+    L.gmla_decode_prepare_workspace_size.argtypes = [i32] * 8
     L.gmla_decode_prepare_workspace_size.restype = sz
-    L.gmla_decode_prepare.argtypes = [vp] * 10 + [vp, sz] + [i32] * 6 + [f32, i32, vp]
+    L.gmla_decode_prepare.argtypes = [vp] * 11 + [vp, sz] + [i32] * 7 + [f32, i32, vp]
     L.gmla_decode_prepare.restype = i32
     L.gmla_gate_out_workspace_size.argtypes = [i32] * 7
     L.gmla_gate_out_workspace_size.restype = sz
@@ -111,21 +111,27 @@ def _workspace(nbytes: int, device, ws):
 
 
 # ------------------------------------------------------------------ prefill
-def prefill(x, W_c, W_q, W_uk, W_uv, sm_scale: float, latent_out=None, o_tilde=None, workspace=None):
-    """x [B, L, d_model] -> (latent [B, L, d_c], o_tilde [B, L, H*d_v])."""
-    _dev(x, W_c, W_q, W_uk, W_uv, latent_out, o_tilde, workspace)
+def prefill(x, W_c, W_q, W_uk, W_uv, sm_scale: float, latent_out=None, o_tilde=None, workspace=None, *,
+            W_dq=None, W_kr=None, W_qr=None, rope_base: float = 0.0):
+    """x [B, L, d_model] -> (cache rows [B, L, d_c + d_r], o_tilde [B, L, H*d_v]).
+    W_dq [d_cq, d_model] makes the query low-rank (W_q is then W^UQ);
+    W_kr [d_r, d_model] and W_qr [H*d_r, d_in] add decoupled RoPE."""
+    _dev(x, W_c, W_dq, W_q, W_kr, W_qr, W_uk, W_uv, latent_out, o_tilde, workspace)
     B, L, D = x.shape
     H, d_k, d_c = W_uk.shape
     d_v = W_uv.shape[1]
+    d_cq = 0 if W_dq is None else W_dq.shape[0]
+    d_r = 0 if W_kr is None else W_kr.shape[0]
     dt = _dtype_code(x)
     if latent_out is None:
-        latent_out = torch.empty((B, L, d_c), dtype=x.dtype, device=x.device)
+        latent_out = torch.empty((B, L, d_c + d_r), dtype=x.dtype, device=x.device)
     if o_tilde is None:
         o_tilde = torch.empty((B, L, H * d_v), dtype=x.dtype, device=x.device)
-    need = lib().gmla_prefill_workspace_size(B, L, H, d_k, d_v, dt)
+    need = lib().gmla_prefill_workspace_size(B, L, H, d_cq, d_k, d_r, d_v, dt)
     workspace, wsb = _workspace(need, x.device, workspace)
-    _check(lib().gmla_prefill(_vp(x), _vp(W_c), _vp(W_q), _vp(W_uk), _vp(W_uv), _vp(latent_out), _vp(o_tilde),
-                              _vp(workspace), wsb, B, L, D, H, d_c, d_k, d_v, float(sm_scale), dt, _stream()))
+    _check(lib().gmla_prefill(_vp(x), _vp(W_c), _vp(W_dq), _vp(W_q), _vp(W_kr), _vp(W_qr), _vp(W_uk), _vp(W_uv),
+                              _vp(latent_out), _vp(o_tilde), _vp(workspace), wsb, B, L, D, H, d_c, d_cq, d_k, d_r,
+                              d_v, float(sm_scale), float(rope_base), dt, _stream()))
     return latent_out, o_tilde
 
 
@@ -158,11 +164,12 @@ def decode(q_abs, cache, seq_start, seq_len, d_c: int, d_r: int, rope_base: floa
 
 
 def decode_prepare(x, W_c, W_kr, W_q, W_qr, W_uk, cache, seq_start, seq_len, rope_base: float, q_abs=None,
-                   workspace=None):
+                   workspace=None, W_dq=None):
     """x [B, d_model] -> q_abs [B, H, d_c+d_r]; writes the new cache row
     [W_c x ; RoPE(W_kr x, seq_len[b])] at cache[seq_start[b] + seq_len[b]].
-    W_kr and W_qr are None when d_r == 0. seq_len is not changed."""
-    _dev(x, W_c, W_kr, W_q, W_qr, W_uk, cache, seq_start, seq_len, q_abs, workspace)
+    W_kr and W_qr are None when d_r == 0. seq_len is not changed. W_dq
+    [d_cq, d_model] makes the query low-rank (W_q and W_qr then read c^Q)."""
+    _dev(x, W_c, W_kr, W_dq, W_q, W_qr, W_uk, cache, seq_start, seq_len, q_abs, workspace)
     if seq_start.dtype != torch.int64 or seq_len.dtype != torch.int32:
         raise TypeError("seq_start must be int64 and seq_len int32")
     B, D = x.shape
@@ -173,11 +180,12 @@ def decode_prepare(x, W_c, W_kr, W_q, W_qr, W_uk, cache, seq_start, seq_len, rop
     dt = _dtype_code(x)
     if q_abs is None:
         q_abs = torch.empty((B, H, d_c + d_r), dtype=x.dtype, device=x.device)
-    need = lib().gmla_decode_prepare_workspace_size(B, D, H, d_c, d_k, d_r, dt)
+    d_cq = 0 if W_dq is None else W_dq.shape[0]
+    need = lib().gmla_decode_prepare_workspace_size(B, D, H, d_c, d_cq, d_k, d_r, dt)
     workspace, wsb = _workspace(need, x.device, workspace)
-    _check(lib().gmla_decode_prepare(_vp(x), _vp(W_c), _vp(W_kr), _vp(W_q), _vp(W_qr), _vp(W_uk), _vp(cache),
-                                     _vp(seq_start), _vp(seq_len), _vp(q_abs), _vp(workspace), wsb, B, D, H, d_c,
-                                     d_k, d_r, float(rope_base), dt, _stream()))
+    _check(lib().gmla_decode_prepare(_vp(x), _vp(W_c), _vp(W_kr), _vp(W_dq), _vp(W_q), _vp(W_qr), _vp(W_uk),
+                                     _vp(cache), _vp(seq_start), _vp(seq_len), _vp(q_abs), _vp(workspace), wsb, B, D,
+                                     H, d_c, d_cq, d_k, d_r, float(rope_base), dt, _stream()))
     return q_abs
 
 

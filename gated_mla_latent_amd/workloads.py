@@ -82,6 +82,9 @@ class PrefillInputs:
     W_g: torch.Tensor  # [H*d_v, d_model]
     W_o: torch.Tensor  # [d_model, H*d_v]
     name: str = ""
+    # low-rank query (d_cq > 0): W_dq [d_cq, d_model]; W_q is then W^UQ [H*d_k, d_cq]
+    d_cq: int = 0
+    W_dq: torch.Tensor | None = None
 
 
 def make_decode(B, H, d_c, d_r, len_lo, len_hi=None, *, rope_base=10000.0,
@@ -126,20 +129,26 @@ def make_decode(B, H, d_c, d_r, len_lo, len_hi=None, *, rope_base=10000.0,
 
 
 def make_prefill(B, L, d_model, H, d_c, d_k, d_v, *, dtype=BF16, seed=0,
-                 sm_scale=None, name="") -> PrefillInputs:
+                 sm_scale=None, name="", d_cq=0) -> PrefillInputs:
+    """Prefill inputs. With d_cq > 0 the query is low-rank: W_dq is drawn
+    from a generator of its own (seed + 4099) and W_q has fan-in d_cq; the
+    other tensors are drawn exactly as without it."""
     gen = torch.Generator("cpu").manual_seed(seed)
     x = _randn(gen, (B, L, d_model), 1.0, dtype)
     W_c = _weight(gen, d_c, d_model, dtype)
-    W_q = _weight(gen, H * d_k, d_model, dtype)
+    W_q = _weight(gen, H * d_k, d_cq if d_cq else d_model, dtype)
     W_uk = _weight(gen, d_k, d_c, dtype, lead=(H,))
     W_uv = _weight(gen, d_v, d_c, dtype, lead=(H,))
     W_g = _weight(gen, H * d_v, d_model, dtype)
     W_o = _weight(gen, d_model, H * d_v, dtype)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d_k)
+    W_dq = None
+    if d_cq:
+        W_dq = _weight(torch.Generator("cpu").manual_seed(seed + 4099), d_cq, d_model, dtype)
     return PrefillInputs(B=B, L=L, d_model=d_model, H=H, d_c=d_c, d_k=d_k, d_v=d_v,
                          sm_scale=sm_scale, dtype=dtype, x=x, W_c=W_c, W_q=W_q,
-                         W_uk=W_uk, W_uv=W_uv, W_g=W_g, W_o=W_o, name=name)
+                         W_uk=W_uk, W_uv=W_uv, W_g=W_g, W_o=W_o, name=name, d_cq=d_cq, W_dq=W_dq)
 
 
 # The five workloads, with their full sizes.
@@ -179,7 +188,8 @@ class DecodeStepInputs:
     """The new token of every sequence and the projections that feed one
     decode step: x [B, d_model], W_c [d_c, d_model], W_kr [d_r, d_model],
     W_q [H*d_k, d_model], W_qr [H*d_r, d_model], W_uk [H, d_k, d_c]
-    (W_kr and W_qr are None when d_r == 0)."""
+    (W_kr and W_qr are None when d_r == 0). With d_cq > 0 the query is
+    low-rank: W_dq [d_cq, d_model], and W_q, W_qr have fan-in d_cq."""
     d_model: int
     d_k: int
     x: torch.Tensor
@@ -188,20 +198,25 @@ class DecodeStepInputs:
     W_q: torch.Tensor
     W_qr: torch.Tensor | None
     W_uk: torch.Tensor
+    d_cq: int = 0
+    W_dq: torch.Tensor | None = None
 
 
-def make_decode_step(dec: DecodeInputs, d_model: int, d_k: int, *, seed=0) -> DecodeStepInputs:
+def make_decode_step(dec: DecodeInputs, d_model: int, d_k: int, *, seed=0, d_cq=0) -> DecodeStepInputs:
     """Inputs of the decode-step projections for the sequences of `dec`.
     Drawn from their own generator (seed + 7919) in the order x, W_c, W_kr,
-    W_q, W_qr, W_uk, so that `dec` is the same tensor set with or without
-    them. Build `dec` with gap_rows >= 1 so that row seq_start + seq_len, the
-    one the step appends, is free."""
+    W_q, W_qr, W_uk (then W_dq), so that `dec` is the same tensor set with or
+    without them. Build `dec` with gap_rows >= 1 so that row seq_start +
+    seq_len, the one the step appends, is free."""
     gen = torch.Generator("cpu").manual_seed(seed + 7919)
     B, H, d_c, d_r, dt = dec.B, dec.H, dec.d_c, dec.d_r, dec.dtype
+    d_in = d_cq if d_cq else d_model
     x = _randn(gen, (B, d_model), 1.0, dt)
     W_c = _weight(gen, d_c, d_model, dt)
     W_kr = _weight(gen, d_r, d_model, dt) if d_r else None
-    W_q = _weight(gen, H * d_k, d_model, dt)
-    W_qr = _weight(gen, H * d_r, d_model, dt) if d_r else None
+    W_q = _weight(gen, H * d_k, d_in, dt)
+    W_qr = _weight(gen, H * d_r, d_in, dt) if d_r else None
     W_uk = _weight(gen, d_k, d_c, dt, lead=(H,))
-    return DecodeStepInputs(d_model=d_model, d_k=d_k, x=x, W_c=W_c, W_kr=W_kr, W_q=W_q, W_qr=W_qr, W_uk=W_uk)
+    W_dq = _weight(gen, d_cq, d_model, dt) if d_cq else None
+    return DecodeStepInputs(d_model=d_model, d_k=d_k, x=x, W_c=W_c, W_kr=W_kr, W_q=W_q, W_qr=W_qr, W_uk=W_uk,
+                            d_cq=d_cq, W_dq=W_dq)

@@ -56,25 +56,37 @@ typedef enum { GMLA_F32 = 0, GMLA_BF16 = 1 } gmla_dtype_t;
 
 /* ------------------------------------------------------------------------
  * Prefill: latent projection, explicit per-head K/V reconstruction and
- * causal attention ([GF] §一 and §二 first two equations).
+ * causal attention ([GF] §一 and §二 first two equations), with an optional
+ * low-rank query ([N03] §5.1: c^Q = W^DQ x, q = W^UQ c^Q) and optional
+ * decoupled RoPE ([N03] §5.2).
  *
  *   x          [B, L, d_model]      input hidden states
  *   W_c        [d_c, d_model]       latent (down) projection
- *   W_q        [H*d_k, d_model]     query projection, head-major rows
+ *   W_dq       [d_cq, d_model]      low-rank query projection W^DQ, or NULL
+ *                                   (d_cq == 0: the query side reads x)
+ *   W_q        [H*d_k, d_in]        query projection (W^UQ with W_dq),
+ *                                   head-major rows; d_in = d_cq or d_model
+ *   W_kr       [d_r, d_model]       shared RoPE key projection, or NULL (d_r == 0)
+ *   W_qr       [H*d_r, d_in]        per-head RoPE query projection, or NULL
  *   W_uk       [H, d_k, d_c]        per-head key up-projection
  *   W_uv       [H, d_v, d_c]        per-head value up-projection
- *   latent_out [B, L, d_c]          out: c_s = W_c x_s (the cache rows)
+ *   latent_out [B, L, d_c + d_r]    out: the cache rows [c_s ; RoPE(W_kr x_s, s)],
+ *                                   c_s = W_c x_s
  *   o_tilde    [B, L, H*d_v]        out: o~_t = Concat_h o_t^(h), channel
  *                                   h*d_v + j; o_t^(h) = sum_{s<=t}
  *                                   softmax_s(sm_scale q_t^(h).k_s^(h)) v_s^(h)
+ * With RoPE the score is q^C.k^C + RoPE(q^R, t).RoPE(k^R, s) (pairs
+ * interleaved, theta_i = rope_base^(-2i/d_r); rope_base 0: unrotated).
  * The gate and output projection follow with gmla_gate_out(W_uv = NULL).
- * Sizes: all >= 1. BF16 needs d_model % 64 == 0, d_c % 64 == 0 and
- * d_k == d_v in {64, 128}; F32 needs d_k <= 1024 and d_v <= 512.
+ * Sizes: all >= 1 (d_cq, d_r >= 0). BF16 needs d_model, d_c and d_cq
+ * % 64 == 0 and d_k == d_v in {64, 128}; F32 needs d_k <= 1024 and
+ * d_v <= 512. Decoupled RoPE (d_r > 0) returns GMLA_ERR_UNSUPPORTED.
  * ---------------------------------------------------------------------- */
-size_t gmla_prefill_workspace_size(int B, int L, int H, int d_k, int d_v, gmla_dtype_t dtype);
-gmla_status_t gmla_prefill(const void* x, const void* W_c, const void* W_q, const void* W_uk, const void* W_uv,
-                           void* latent_out, void* o_tilde, void* workspace, size_t workspace_bytes, int B, int L,
-                           int d_model, int H, int d_c, int d_k, int d_v, float sm_scale, gmla_dtype_t dtype,
+size_t gmla_prefill_workspace_size(int B, int L, int H, int d_cq, int d_k, int d_r, int d_v, gmla_dtype_t dtype);
+gmla_status_t gmla_prefill(const void* x, const void* W_c, const void* W_dq, const void* W_q, const void* W_kr,
+                           const void* W_qr, const void* W_uk, const void* W_uv, void* latent_out, void* o_tilde,
+                           void* workspace, size_t workspace_bytes, int B, int L, int d_model, int H, int d_c,
+                           int d_cq, int d_k, int d_r, int d_v, float sm_scale, float rope_base, gmla_dtype_t dtype,
                            void* stream);
 
 /* ------------------------------------------------------------------------
@@ -117,8 +129,11 @@ gmla_status_t gmla_decode(const void* q_abs, const void* cache, const int64_t* s
  *   x         [B, d_model]          hidden state of each sequence's new token
  *   W_c       [d_c, d_model]        latent (down) projection
  *   W_kr      [d_r, d_model]        shared RoPE key projection (NULL if d_r == 0)
- *   W_q       [H*d_k, d_model]      query projection, head-major rows
- *   W_qr      [H*d_r, d_model]      per-head RoPE query projection (NULL if d_r == 0)
+ *   W_dq      [d_cq, d_model]       low-rank query projection W^DQ ([N03] §5.1),
+ *                                   or NULL (d_cq == 0: the query side reads x)
+ *   W_q       [H*d_k, d_in]         query projection (W^UQ with W_dq),
+ *                                   head-major rows; d_in = d_cq or d_model
+ *   W_qr      [H*d_r, d_in]         per-head RoPE query projection (NULL if d_r == 0)
  *   W_uk      [H, d_k, d_c]         per-head key up-projection
  *   cache     [rows, d_c + d_r]     in/out: row seq_start[b] + seq_len[b] is
  *                                   set to [W_c x_b ; RoPE(W_kr x_b, seq_len[b])];
@@ -127,21 +142,24 @@ gmla_status_t gmla_decode(const void* q_abs, const void* cache, const int64_t* s
  *                                   before this step; not modified (the caller
  *                                   adds 1 before gmla_decode, which then
  *                                   rotates the query to position seq_len[b])
- *   q_abs     [B, H, d_c + d_r]     out: [(W_UK^(h))^T q_h ; W_qr^(h) x_b],
- *                                   q_h = W_q^(h) x_b, the RoPE part unrotated
+ *   q_abs     [B, H, d_c + d_r]     out: [(W_UK^(h))^T q_h ; W_qr^(h) u_b],
+ *                                   q_h = W_q^(h) u_b with u_b = W_dq x_b (or
+ *                                   x_b), the RoPE part unrotated
  * RoPE pairs are interleaved (2i, 2i+1), theta_i = rope_base^(-2i/d_r);
  * rope_base == 0 leaves the key unrotated. The target rows must lie inside
  * `cache` and differ between sequences (trusted, read on the device).
  * The workspace holds the projections of x before the append and the absorb.
  * Only GMLA_BF16 is supported (GMLA_ERR_UNSUPPORTED otherwise); it needs
- * d_model % 64 == 0, d_c % 64 == 0, d_k % 16 == 0, d_k <= 128 and
+ * d_model, d_c and d_cq % 64 == 0, d_k % 16 == 0, d_k <= 128 and
  * d_r % 4 == 0.
  * ---------------------------------------------------------------------- */
-size_t gmla_decode_prepare_workspace_size(int B, int d_model, int H, int d_c, int d_k, int d_r, gmla_dtype_t dtype);
-gmla_status_t gmla_decode_prepare(const void* x, const void* W_c, const void* W_kr, const void* W_q, const void* W_qr,
-                                  const void* W_uk, void* cache, const int64_t* seq_start, const int32_t* seq_len,
-                                  void* q_abs, void* workspace, size_t workspace_bytes, int B, int d_model, int H,
-                                  int d_c, int d_k, int d_r, float rope_base, gmla_dtype_t dtype, void* stream);
+size_t gmla_decode_prepare_workspace_size(int B, int d_model, int H, int d_c, int d_cq, int d_k, int d_r,
+                                          gmla_dtype_t dtype);
+gmla_status_t gmla_decode_prepare(const void* x, const void* W_c, const void* W_kr, const void* W_dq, const void* W_q,
+                                  const void* W_qr, const void* W_uk, void* cache, const int64_t* seq_start,
+                                  const int32_t* seq_len, void* q_abs, void* workspace, size_t workspace_bytes, int B,
+                                  int d_model, int H, int d_c, int d_cq, int d_k, int d_r, float rope_base,
+                                  gmla_dtype_t dtype, void* stream);
 
 /* ------------------------------------------------------------------------
  * Gate and output projection ([GF] §二 boxed equation):

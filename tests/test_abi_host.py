@@ -82,17 +82,21 @@ def test_prefill_workspace_size_formula(L):
     for B, Lq, H, d in [(2, 100, 3, 64), (1, 8192, 64, 128), (3, 64, 1, 128)]:
         T, Lp = B * Lq, (Lq + 63) // 64 * 64
         # bf16: q and K as [T, H d], V transposed per sequence as [B, H d, Lp]
-        assert L.gmla_prefill_workspace_size(B, Lq, H, d, d, 1) == 2 * up(T * H * d * 2) + up(B * H * d * Lp * 2)
-        assert L.gmla_prefill_workspace_size(B, Lq, H, d, d, 0) == 3 * up(T * H * d * 4)
-    assert L.gmla_prefill_workspace_size(0, 16, 2, 64, 64, 1) == 0
+        assert L.gmla_prefill_workspace_size(B, Lq, H, 0, d, 0, d, 1) == 2 * up(T * H * d * 2) + up(B * H * d * Lp * 2)
+        assert L.gmla_prefill_workspace_size(B, Lq, H, 0, d, 0, d, 0) == 3 * up(T * H * d * 4)
+        # low-rank query: c^Q [T, d_cq] follows; decoupled RoPE widens q and K to d + d_r
+        assert (L.gmla_prefill_workspace_size(B, Lq, H, 192, d, 64, d, 1) ==
+                2 * up(T * H * (d + 64) * 2) + up(B * H * d * Lp * 2) + up(T * 192 * 2))
+    assert L.gmla_prefill_workspace_size(0, 16, 2, 0, 64, 0, 64, 1) == 0
 
 
 def _pre(L, **kw):
-    a = dict(x=A, Wc=A, Wq=A, Wuk=A, Wuv=A, lat=A, ot=A, ws=A, wsb=1 << 40, B=1, Lq=16, D=256, H=2, d_c=128, d_k=128,
-             d_v=128, scale=0.1, dt=1)
+    a = dict(x=A, Wc=A, Wdq=0, Wq=A, Wkr=0, Wqr=0, Wuk=A, Wuv=A, lat=A, ot=A, ws=A, wsb=1 << 40, B=1, Lq=16, D=256,
+             H=2, d_c=128, d_cq=0, d_k=128, d_r=0, d_v=128, scale=0.1, base=0.0, dt=1)
     a.update(kw)
-    return L.gmla_prefill(a["x"], a["Wc"], a["Wq"], a["Wuk"], a["Wuv"], a["lat"], a["ot"], a["ws"], a["wsb"], a["B"],
-                          a["Lq"], a["D"], a["H"], a["d_c"], a["d_k"], a["d_v"], a["scale"], a["dt"], None)
+    return L.gmla_prefill(a["x"], a["Wc"], a["Wdq"], a["Wq"], a["Wkr"], a["Wqr"], a["Wuk"], a["Wuv"], a["lat"], a["ot"],
+                          a["ws"], a["wsb"], a["B"], a["Lq"], a["D"], a["H"], a["d_c"], a["d_cq"], a["d_k"], a["d_r"],
+                          a["d_v"], a["scale"], a["base"], a["dt"], None)
 
 
 def test_prefill_argument_checks(L):
@@ -104,18 +108,26 @@ def test_prefill_argument_checks(L):
     assert _pre(L, d_k=96, d_v=96) == UNSUPPORTED
     assert _pre(L, d_k=128, d_v=64) == UNSUPPORTED
     assert _pre(L, d_v=2048, d_k=2048, dt=0) == UNSUPPORTED
+    assert _pre(L, Wdq=A) == INVALID                # W_dq without d_cq
+    assert _pre(L, d_cq=64) == INVALID              # d_cq without W_dq
+    assert _pre(L, Wdq=A, d_cq=96) == UNSUPPORTED   # bf16 needs d_cq % 64 == 0
+    assert _pre(L, d_r=64) == INVALID               # d_r without W_kr / W_qr
+    assert _pre(L, Wkr=A, d_r=64) == INVALID
+    assert _pre(L, Wkr=A, Wqr=A, d_r=63) == INVALID
+    assert _pre(L, base=-1.0) == INVALID
     assert _pre(L, wsb=100) == WORKSPACE
-    need = L.gmla_prefill_workspace_size(1, 16, 2, 128, 128, 1)
+    assert _pre(L, Wdq=A, d_cq=64, wsb=L.gmla_prefill_workspace_size(1, 16, 2, 0, 128, 0, 128, 1)) == WORKSPACE
+    need = L.gmla_prefill_workspace_size(1, 16, 2, 0, 128, 0, 128, 1)
     assert need == 2 * 16 * 2 * 128 * 2 + 2 * 128 * 64 * 2  # q, K, and V^T padded to 64 keys
 
 
 def _prep(L, **kw):
-    a = dict(x=A, Wc=A, Wkr=A, Wq=A, Wqr=A, Wuk=A, cache=A, start=A, len_=A, q=A, ws=A, wsb=1 << 40, B=4, D=256,
-             H=16, d_c=512, d_k=128, d_r=64, base=10000.0, dt=1)
+    a = dict(x=A, Wc=A, Wkr=A, Wdq=0, Wq=A, Wqr=A, Wuk=A, cache=A, start=A, len_=A, q=A, ws=A, wsb=1 << 40, B=4,
+             D=256, H=16, d_c=512, d_cq=0, d_k=128, d_r=64, base=10000.0, dt=1)
     a.update(kw)
-    return L.gmla_decode_prepare(a["x"], a["Wc"], a["Wkr"], a["Wq"], a["Wqr"], a["Wuk"], a["cache"], a["start"],
-                                 a["len_"], a["q"], a["ws"], a["wsb"], a["B"], a["D"], a["H"], a["d_c"], a["d_k"],
-                                 a["d_r"], a["base"], a["dt"], None)
+    return L.gmla_decode_prepare(a["x"], a["Wc"], a["Wkr"], a["Wdq"], a["Wq"], a["Wqr"], a["Wuk"], a["cache"],
+                                 a["start"], a["len_"], a["q"], a["ws"], a["wsb"], a["B"], a["D"], a["H"], a["d_c"],
+                                 a["d_cq"], a["d_k"], a["d_r"], a["base"], a["dt"], None)
 
 
 def test_decode_prepare_argument_checks(L):
@@ -134,6 +146,9 @@ def test_decode_prepare_argument_checks(L):
     assert _prep(L, d_r=2) == UNSUPPORTED
     assert _prep(L, wsb=100) == WORKSPACE
     assert _prep(L, ws=A + 16) == INVALID           # workspace must be 256-byte aligned
+    assert _prep(L, Wdq=A) == INVALID                # W_dq without d_cq
+    assert _prep(L, d_cq=128) == INVALID             # d_cq without W_dq
+    assert _prep(L, Wdq=A, d_cq=100) == UNSUPPORTED
 
 
 def _ksplit(M, N, K, batches):
@@ -167,13 +182,13 @@ def test_split_k_rule_examples():
 
 def test_decode_prepare_workspace_size_formula(L):
     up = lambda n: (n + 255) // 256 * 256
-    for B, D, H, d_c, d_k, d_r in [(4, 256, 16, 512, 128, 64), (37, 7168, 128, 512, 128, 0), (1, 192, 3, 64, 32, 4),
-                                   (64, 7168, 128, 512, 128, 64)]:
-        # new cache rows [B, d_c + d_r], queries [B, H d_k], RoPE queries [B, H d_r]
-        want = up(B * (d_c + d_r) * 2) + up(B * H * d_k * 2) + up(B * H * d_r * 2)
-        assert L.gmla_decode_prepare_workspace_size(B, D, H, d_c, d_k, d_r, 1) == want
-    assert L.gmla_decode_prepare_workspace_size(4, 256, 16, 512, 128, 64, 0) == 0
-    assert L.gmla_decode_prepare_workspace_size(0, 256, 16, 512, 128, 64, 1) == 0
+    for B, D, H, d_c, d_cq, d_k, d_r in [(4, 256, 16, 512, 0, 128, 64), (37, 7168, 128, 512, 0, 128, 0),
+                                         (1, 192, 3, 64, 0, 32, 4), (64, 7168, 128, 512, 1536, 128, 64)]:
+        # new cache rows [B, d_c + d_r], queries [B, H d_k], RoPE queries [B, H d_r], c^Q [B, d_cq]
+        want = up(B * (d_c + d_r) * 2) + up(B * H * d_k * 2) + up(B * H * d_r * 2) + up(B * d_cq * 2)
+        assert L.gmla_decode_prepare_workspace_size(B, D, H, d_c, d_cq, d_k, d_r, 1) == want
+    assert L.gmla_decode_prepare_workspace_size(4, 256, 16, 512, 0, 128, 64, 0) == 0
+    assert L.gmla_decode_prepare_workspace_size(0, 256, 16, 512, 0, 128, 64, 1) == 0
 
 
 def test_gate_out_workspace_size_formula(L):

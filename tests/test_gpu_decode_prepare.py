@@ -130,7 +130,7 @@ def test_prepare_rejects_fp32_and_short_workspace():
         ops.decode_prepare(dev(st.x).float(), dev(st.W_c).float(), dev(st.W_kr).float(), dev(st.W_q).float(),
                            dev(st.W_qr).float(), dev(st.W_uk).float(), dev(dec.cache).float(), dev(dec.seq_start),
                            dev(dec.seq_len), dec.rope_base)
-    need = ops.lib().gmla_decode_prepare_workspace_size(4, 256, 16, 512, 128, 64, ops.GMLA_BF16)
+    need = ops.lib().gmla_decode_prepare_workspace_size(4, 256, 16, 512, 0, 128, 64, ops.GMLA_BF16)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     with pytest.raises(ops.GmlaError):
         ops.decode_prepare(dev(st.x), dev(st.W_c), dev(st.W_kr), dev(st.W_q), dev(st.W_qr), dev(st.W_uk),
