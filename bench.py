@@ -12,6 +12,8 @@ A step is one pass of the hot path over one batch of synthetic input:
               region of its own and reported as decode_prepare;
   prefill   : gmla_prefill (latent, query, K/V reconstruction, causal
               attention) followed by gmla_gate_out over all B*L tokens;
+  prefill_rope: the same with decoupled RoPE (RoPE key and query
+              projections, their rotation, 192-wide scores);
   tiny_fp32 : the same as prefill for the tiny fp32 workload.
 Inputs are resident in HBM before timing starts; several copies of every
 input that is read in the step rotate so that the 256 MB Infinity Cache
@@ -48,6 +50,7 @@ WORKLOADS = {
     "decode_rope": ("decode_rope_b64_h128", "decode RoPE, B=64, H=128, d_c=512+d_r=64, L_b~U[1024,16384], bf16 + gate/W_o (d_model 7168, d_v 128)"),
     "decode_long": ("decode_rope_b8_l131072", "decode RoPE, B=8, H=128, d_c=512+64, L=131072 each, bf16 + gate/W_o (d_model 7168, d_v 128)"),
     "prefill": ("prefill_b2_l8192", "causal prefill B=2, L=8192, d_model=7168, H=64, d_c=512, d_k=d_v=128, bf16 + gate/W_o"),
+    "prefill_rope": ("prefill_rope_b2_l8192", "causal prefill with decoupled RoPE B=2, L=8192, d_model=7168, H=64, d_c=512, d_k=d_v=128, d_r=64, bf16 + gate/W_o"),
     "tiny_fp32": ("prefill_f32_tiny", "causal prefill B=1, L=128, d_model=256, H=4, d_c=64, d_k=d_v=32, fp32 + gate/W_o"),
 }
 
@@ -122,10 +125,13 @@ def prefill_flops(p):
         "gemm_query": 2 * T * p.d_model * p.H * p.d_k,
         "gemm_key_recon": 2 * T * p.d_c * p.H * p.d_k,
         "gemm_value_recon": 2 * T * p.d_c * p.H * p.d_v,
-        "prefill_attn": 2 * pairs * p.H * (p.d_k + p.d_v),
+        "prefill_attn": 2 * pairs * p.H * (p.d_k + p.d_r + p.d_v),
         "gemm_gate": 2 * T * p.d_model * p.H * p.d_v,
         "gemm_out": 2 * T * p.H * p.d_v * p.d_model,
     }
+    if p.d_r:
+        f["gemm_rope_key"] = 2 * T * p.d_model * p.d_r
+        f["gemm_rope_query"] = 2 * T * p.d_model * p.H * p.d_r
     return f
 
 
@@ -204,21 +210,22 @@ def build_prefill(args, p, torch, ops):
     T = p.B * p.L
     copies = []
     for i in range(args.copies):
-        copies.append({k: getattr(p, k).to(dev) for k in ("x", "W_c", "W_q", "W_uk", "W_uv", "W_g", "W_o")})
+        copies.append({k: (None if getattr(p, k) is None else getattr(p, k).to(dev))
+                       for k in ("x", "W_c", "W_q", "W_uk", "W_uv", "W_g", "W_o", "W_kr", "W_qr")})
         log(f"  copy {i} resident")
-    lat = torch.empty((p.B, p.L, p.d_c), dtype=p.dtype, device=dev)
+    lat = torch.empty((p.B, p.L, p.d_c + p.d_r), dtype=p.dtype, device=dev)
     ot = torch.empty((p.B, p.L, p.H * p.d_v), dtype=p.dtype, device=dev)
     y = torch.empty((T, p.d_model), dtype=p.dtype, device=dev)
-    wsp_n = L.gmla_prefill_workspace_size(p.B, p.L, p.H, 0, p.d_k, 0, p.d_v, dt)
+    wsp_n = L.gmla_prefill_workspace_size(p.B, p.L, p.H, 0, p.d_k, p.d_r, p.d_v, dt)
     wsg_n = L.gmla_gate_out_workspace_size(T, p.d_model, 1, 0, p.H * p.d_v, 0, dt)
     wsp = torch.empty(wsp_n, dtype=torch.uint8, device=dev)
     wsg = torch.empty(wsg_n, dtype=torch.uint8, device=dev)
     calls = []
     for c in copies:
         nul = C.c_void_p(0)
-        pre = (_vp(c["x"]), _vp(c["W_c"]), nul, _vp(c["W_q"]), nul, nul, _vp(c["W_uk"]), _vp(c["W_uv"]), _vp(lat),
-               _vp(ot), _vp(wsp), C.c_size_t(wsp_n), p.B, p.L, p.d_model, p.H, p.d_c, 0, p.d_k, 0, p.d_v,
-               C.c_float(p.sm_scale), C.c_float(0.0), dt, stream)
+        pre = (_vp(c["x"]), _vp(c["W_c"]), nul, _vp(c["W_q"]), _vp(c["W_kr"]), _vp(c["W_qr"]), _vp(c["W_uk"]),
+               _vp(c["W_uv"]), _vp(lat), _vp(ot), _vp(wsp), C.c_size_t(wsp_n), p.B, p.L, p.d_model, p.H, p.d_c, 0,
+               p.d_k, p.d_r, p.d_v, C.c_float(p.sm_scale), C.c_float(p.rope_base), dt, stream)
         go = (_vp(c["x"]), _vp(ot), C.c_void_p(0), _vp(c["W_g"]), _vp(c["W_o"]), _vp(y), _vp(wsg), C.c_size_t(wsg_n),
               T, p.d_model, 1, 0, p.H * p.d_v, dt, stream)
         calls.append((pre, go))
@@ -283,11 +290,14 @@ def cpu_baseline_prefill(p, budget_s):
     # sample: the first Ls positions of sequence 0; Ls doubles until the
     # oracle run takes about a third of the budget (or covers the sequence)
     Ls = min(p.L, 64)
-    W = [getattr(p, k).float().numpy() for k in ("W_c", "W_q", "W_uk", "W_uv", "W_g", "W_o")]
+    W = {k: (None if getattr(p, k) is None else getattr(p, k).float().numpy())
+         for k in ("W_c", "W_q", "W_uk", "W_uv", "W_g", "W_o", "W_kr", "W_qr")}
     while True:
         x = p.x[:1, :Ls].float().numpy()
         t0 = time.perf_counter()
-        O.gated_mla_layer(x, *W, p.sm_scale)
+        _, ot, _ = O.prefill_reference(x, W["W_c"], W["W_q"], W["W_uk"], W["W_uv"], p.sm_scale, W_kr=W["W_kr"],
+                                       W_qr=W["W_qr"], rope_base=p.rope_base)
+        O.gate_out_reference(x[0], ot[0], W["W_g"], W["W_o"])
         secs = time.perf_counter() - t0
         if secs >= budget_s / 3 or Ls >= p.L:
             break

@@ -36,6 +36,13 @@
 //    input).
 //  * Each workgroup takes two query tiles, the k-th longest and the k-th
 //    shortest, so all workgroups carry the same causal work.
+//  * Decoupled RoPE ([N03] "LLM 注意力与计算内核精读笔记 · 03" §5.2): the
+//    score gains q^R . k^R over DR more features, the rotated RoPE query of
+//    the head and the RoPE key shared by all heads. They are DR / 16 more
+//    k-steps of S^T: the query fragments from their own rows, the key
+//    fragments from a third tile of the stage (64 keys x DR). The larger
+//    stage leaves room for three stages only: one barrier per tile, two
+//    tiles in flight behind the one being read.
 #include "common.h"
 #include "kernels.h"
 
@@ -49,19 +56,26 @@ constexpr int kPFS = 4;  // k-steps of K fragments (two each) in flight in S^T
 constexpr int kPFV = 4;  // V^T fragments in flight in P.V
 constexpr int kSync = 2;  // key tiles per barrier; the ring holds 2 kSync tiles
 
-template <int D>
+template <int D, int DR>
 struct FaCfg {
-  static constexpr int BQ = 256, BK = 64, NW = 8, NST = 2 * kSync;
+  static constexpr int BQ = 256, BK = 64, NW = 8;
   static constexpr int CH = D / 8;             // 16-byte chunks per row
   static constexpr int ROWB = 2 * D;           // bytes per row
   static constexpr int TILE = BK * ROWB;       // one K tile (64 rows of D), or one V^T tile (D rows of 64)
-  static constexpr int STAGE = 2 * TILE;
+  static constexpr int RTILE = BK * DR * 2;    // the RoPE key tile (64 rows of DR)
+  static constexpr int STAGE = 2 * TILE + RTILE;
+  static constexpr int SYNC = DR ? 1 : kSync;  // key tiles per barrier
+  static constexpr int NST = DR ? 3 : 2 * kSync;  // ring stages
   static constexpr int LDS = NST * STAGE;
-  static constexpr int KS = D / 16;            // k-steps of S^T
+  static constexpr int KSC = D / 16;           // k-steps of S^T over the content features
+  static constexpr int KS = (D + DR) / 16;     // all k-steps of S^T
   static constexpr int DB = D / 32;            // 32-row blocks of O^T
   static constexpr int RND = BK * CH / (64 * NW);  // 1 KiB loads per wave per K (or V) tile
+  static constexpr int RNDR = BK * DR / 8 / (64 * NW);  // ... per RoPE key tile
+  static constexpr int LPT = 2 * RND + RNDR;   // loads per wave per tile
   static_assert(RND >= 1, "at least one load per wave");
-  static_assert(LDS <= 163840, "LDS budget");
+  static_assert(DR == 0 || (DR == 64 && RNDR == 1), "RoPE key tile: one load per wave");
+  static_assert(LDS <= 131072, "LDS budget");
 };
 
 // Chunk swizzles (physical chunk = logical chunk ^ f(row)). The K and V^T
@@ -77,10 +91,10 @@ __device__ __forceinline__ int swz_vt(int r) { return (r >> 1) & 7; }
 
 }  // namespace
 
-template <int D>
+template <int D, int DR>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void prefill_attn_kernel(AttnArgs a) {
-  using C = FaCfg<D>;
+  using C = FaCfg<D, DR>;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   const unsigned smem_base = (unsigned)(uintptr_t)smem;
@@ -99,6 +113,8 @@ void prefill_attn_kernel(AttnArgs a) {
   const bf16* kb = a.k + b * a.skb + h * a.skh;
   const bf16* vb = a.v + b * a.svb + h * a.svh;
   bf16* ob = a.o + b * a.sob + h * a.soh;
+  const bf16* qrb = DR ? a.qr + b * a.sqrb + h * a.sqrh : nullptr;
+  const bf16* krb = DR ? a.kr + b * a.skrb : nullptr;
 
   // softmax constant: |scale| log2 e; a negative scale negates the queries
   const float cabs = fabsf(a.scale_log2);
@@ -117,9 +133,17 @@ void prefill_attn_kernel(AttnArgs a) {
     t = t < a.L ? t : a.L - 1;
     const bf16* qp = qb + (int64_t)t * a.sqt + 8 * (lane >> 5);
 #pragma unroll
-    for (int kk = 0; kk < C::KS; ++kk) {
+    for (int kk = 0; kk < C::KSC; ++kk) {
       u32x4 v = *(const u32x4*)(qp + 16 * kk);
       qf[kk] = as_bf16x8(u32x4{v[0] ^ qsign, v[1] ^ qsign, v[2] ^ qsign, v[3] ^ qsign});
+    }
+    if constexpr (DR > 0) {
+      const bf16* qrp = qrb + (int64_t)t * a.sqrt_ + 8 * (lane >> 5);
+#pragma unroll
+      for (int kk = C::KSC; kk < C::KS; ++kk) {
+        u32x4 v = *(const u32x4*)(qrp + 16 * (kk - C::KSC));
+        qf[kk] = as_bf16x8(u32x4{v[0] ^ qsign, v[1] ^ qsign, v[2] ^ qsign, v[3] ^ qsign});
+      }
     }
   }
 
@@ -144,6 +168,15 @@ void prefill_attn_kernel(AttnArgs a) {
       g2lds16_s(kbase, (unsigned)((rr * a.skt + (pc ^ swz_k<D>(row)) * 8) * 2), kdst + n * 1024);
       const int vrow = 8 * n + (lane >> 3);
       g2lds16_s(vbase, (unsigned)((vrow * a.svj + ((lane & 7) ^ swz_vt(vrow)) * 8) * 2), vdst + n * 1024);
+    }
+    if constexpr (DR > 0) {
+      // RoPE key rows 8 wave .. 8 wave + 7 (128-byte rows, the V^T swizzle)
+      const unsigned rdst = kdst + 2 * C::TILE;
+      const unsigned long long rbase = (unsigned long long)(uintptr_t)(krb + (int64_t)t0 * a.skrt);
+      const int row = 8 * wave + (lane >> 3);
+      int rr = t0 + row;
+      rr = (rr < a.L ? rr : a.L - 1) - t0;
+      g2lds16_s(rbase, (unsigned)((rr * a.skrt + ((lane & 7) ^ swz_vt(row)) * 8) * 2), rdst + wave * 1024);
     }
   };
 
@@ -197,18 +230,28 @@ void prefill_attn_kernel(AttnArgs a) {
     lsum = 0.f;
     m_all = -INFINITY;
     lds_barrier();
+    constexpr int PRE = DR ? 2 : kSync;  // tiles issued before the loop
 #pragma unroll
-    for (int j = 0; j < kSync; ++j)
+    for (int j = 0; j < PRE; ++j)
       if (j < ntiles) load_tile(j, j);
     for (int it = 0; it < ntiles; ++it) {
-      if (it % kSync == 0) {
-        // tiles it .. it + kSync - 1 have landed; their successors go into
-        // the stages of the previous kSync tiles, which every wave is done with
-        wait_vmcnt<0>();
-        lds_barrier();
+      if constexpr (DR == 0) {
+        if (it % kSync == 0) {
+          // tiles it .. it + kSync - 1 have landed; their successors go into
+          // the stages of the previous kSync tiles, which every wave is done with
+          wait_vmcnt<0>();
+          lds_barrier();
 #pragma unroll
-        for (int j = kSync; j < 2 * kSync; ++j)
-          if (it + j < ntiles) load_tile((it + j) % C::NST, it + j);
+          for (int j = kSync; j < 2 * kSync; ++j)
+            if (it + j < ntiles) load_tile((it + j) % C::NST, it + j);
+        }
+      } else {
+        // tile it has landed (tile it + 1 may still be in flight); tile
+        // it + 2 goes into the stage of tile it - 1, which every wave is done with
+        if (it + 1 < ntiles) wait_vmcnt<C::LPT>();
+        else wait_vmcnt<0>();
+        lds_barrier();
+        if (it + 2 < ntiles) load_tile((it + 2) % C::NST, it + 2);
       }
       if (it >= my_tiles) continue;
       const LDS_AS char* kt_l = smem + (it % C::NST) * C::STAGE;
@@ -216,9 +259,13 @@ void prefill_attn_kernel(AttnArgs a) {
       // ---- S^T: 64 keys (2 blocks of 32) x 32 queries ----
       floatx16 s[2] = {floatx16{}, floatx16{}};
       auto readK = [&](int kk, int i) -> bf16x8 {
-        const int c = 2 * kk + (lane >> 5);
         const int row = 32 * i + krow;
-        return as_bf16x8(lds_read16(kt_l + row * C::ROWB + ((c ^ swz_k<D>(row)) << 4)));
+        if (kk < C::KSC) {
+          const int c = 2 * kk + (lane >> 5);
+          return as_bf16x8(lds_read16(kt_l + row * C::ROWB + ((c ^ swz_k<D>(row)) << 4)));
+        }
+        const int c = 2 * (kk - C::KSC) + (lane >> 5);
+        return as_bf16x8(lds_read16(kt_l + 2 * C::TILE + row * 128 + ((c ^ swz_vt(row)) << 4)));
       };
       {
         constexpr int PF = kPFS < C::KS ? kPFS : C::KS;
@@ -299,10 +346,10 @@ void prefill_attn_kernel(AttnArgs a) {
   }
 }
 
-template <int D>
+template <int D, int DR>
 static hipError_t launch_d(const AttnArgs& a, hipStream_t st) {
-  using C = FaCfg<D>;
-  auto kern = prefill_attn_kernel<D>;
+  using C = FaCfg<D, DR>;
+  auto kern = prefill_attn_kernel<D, DR>;
   static bool attr = false;
   if (!attr) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
@@ -310,15 +357,21 @@ static hipError_t launch_d(const AttnArgs& a, hipStream_t st) {
     attr = true;
   }
   // the loads use 32-bit offsets from a per-tile scalar base
-  if ((long long)C::BK * a.skt * 2 >= (1LL << 31) || (long long)D * a.svj * 2 >= (1LL << 31))
+  if ((long long)C::BK * a.skt * 2 >= (1LL << 31) || (long long)D * a.svj * 2 >= (1LL << 31) ||
+      (long long)C::BK * a.skrt * 2 >= (1LL << 31))
     return hipErrorInvalidValue;
   const int npair = ((a.L + C::BQ - 1) / C::BQ + 1) / 2;
   return launch(kern, dim3(npair * a.B * a.H), dim3(64 * C::NW), C::LDS, st, a);
 }
 
 hipError_t launch_prefill_attn_bf16(const AttnArgs& a, hipStream_t st) {
-  if (a.D == 128) return launch_d<128>(a, st);
-  if (a.D == 64) return launch_d<64>(a, st);
+  if (a.D_R == 0) {
+    if (a.D == 128) return launch_d<128, 0>(a, st);
+    if (a.D == 64) return launch_d<64, 0>(a, st);
+  } else if (a.D_R == 64 && a.qr && a.kr) {
+    if (a.D == 128) return launch_d<128, 64>(a, st);
+    if (a.D == 64) return launch_d<64, 64>(a, st);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -138,4 +138,19 @@ __device__ __forceinline__ float xor32(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Rotate the interleaved pair (x0, x1) with index i of a d_r-wide RoPE vector
+// to position pos, theta_i = base^(-2i / d_r) ([N03] "LLM 注意力与计算内核精读笔记
+// · 03" §5.2); the angle is formed and reduced modulo 2 pi in fp64 so that long
+// positions keep their accuracy, then fp32 sine and cosine.
+__device__ __forceinline__ void rope_pair(float& x0, float& x1, int i, int d_r, double log2_base, double pos) {
+  const double theta = exp2(-(2.0 * i / d_r) * log2_base);
+  double ang = pos * theta;
+  ang -= 6.283185307179586 * floor(ang * 0.15915494309189535);
+  float s, c;
+  sincosf((float)ang, &s, &c);
+  const float y0 = x0 * c - x1 * s, y1 = x0 * s + x1 * c;
+  x0 = y0;
+  x1 = y1;
+}
+
 }  // namespace gmla

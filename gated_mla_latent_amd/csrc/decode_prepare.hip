@@ -1,5 +1,8 @@
-// The projections around one decode step (bf16, gfx950), after the four
-// input GEMMs (x W_c^T, x W^KR^T, x W_q^T, x W^QR^T) have run:
+// RoPE rotation kernels (bf16, gfx950): the decode step's cache append and
+// query absorption, and the in-place rotation of prefill's RoPE rows.
+//
+// The projections around one decode step, after the input GEMMs (x W_c^T,
+// x W^KR^T, x W_q^T, x W^QR^T) have run:
 //
 //   * append: the new token's cache row [c ; RoPE(k^R, pos)] goes to row
 //     seq_start[b] + seq_len[b] of the cache, pos = seq_len[b]
@@ -17,20 +20,6 @@
 namespace gmla {
 
 namespace {
-
-// Rotate the interleaved pair (x0, x1) with index i of a d_r-wide RoPE vector
-// to position pos, theta_i = base^(-2i / d_r); the angle is formed and reduced
-// in fp64 so that long positions keep their accuracy.
-__device__ __forceinline__ void rope_pair(float& x0, float& x1, int i, int d_r, double log2_base, double pos) {
-  const double theta = exp2(-(2.0 * i / d_r) * log2_base);
-  double ang = pos * theta;
-  ang -= 6.283185307179586 * floor(ang * 0.15915494309189535);
-  float s, c;
-  sincosf((float)ang, &s, &c);
-  const float y0 = x0 * c - x1 * s, y1 = x0 * s + x1 * c;
-  x0 = y0;
-  x1 = y1;
-}
 
 // One workgroup per new row: the latent copied in 16-byte pieces (4-byte ones
 // when d_c + d_r is not a multiple of 8), then the RoPE part rotated pair by
@@ -121,7 +110,35 @@ __global__ __launch_bounds__(256) void decode_absorb_kernel(PrepareArgs a) {
   }
 }
 
+// Rotate in place every RoPE vector of a row-major buffer: row r holds nvec
+// vectors of d_r elements (vector v at p + r ld + v d_r), at position r % L
+// (rows are sequence-major, L tokens each). One thread per pair.
+__global__ __launch_bounds__(256) void rope_rows_kernel(RopeRowsArgs a) {
+  const int P = a.d_r / 2;
+  const int64_t n = (int64_t)a.rows * a.nvec * P;
+  const double lb = log2((double)a.base);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int pi = (int)(i % P);
+    const int64_t rv = i / P;
+    const int v = (int)(rv % a.nvec);
+    const int64_t r = rv / a.nvec;
+    unsigned* w = (unsigned*)(a.p + r * a.ld + (int64_t)v * a.d_r + 2 * pi);
+    const unsigned u = *w;
+    float x0 = bf16_bits_to_f32((unsigned short)(u & 0xffff)), x1 = bf16_bits_to_f32((unsigned short)(u >> 16));
+    rope_pair(x0, x1, pi, a.d_r, lb, (double)(r % a.L));
+    *w = pack_bf16x2(x0, x1);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_rope_rows(const RopeRowsArgs& a, hipStream_t st) {
+  if (a.rows <= 0 || a.nvec <= 0 || a.d_r <= 0 || a.base == 0.0f) return hipSuccess;
+  if (a.d_r % 2 != 0 || a.ld % 2 != 0 || a.L <= 0) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)a.rows * a.nvec * (a.d_r / 2);
+  const int64_t blocks = (n + 255) / 256;
+  return launch(rope_rows_kernel, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, st, a);
+}
 
 hipError_t launch_decode_append(const PrepareArgs& a, hipStream_t st) {
   if (a.B <= 0) return hipSuccess;

@@ -145,8 +145,9 @@ size_t gmla_prefill_workspace_size(int B, int L, int H, int d_cq, int d_k, int d
   const size_t T = (size_t)B * L;
   const size_t es = esize(dtype);
   const size_t v_elems = dtype == GMLA_BF16 ? (size_t)B * H * d_v * prefill_vt_ld(L) : T * H * d_v;
-  // q and K ([T, H (d_k + d_r)]), V, then the low-rank query c^Q [T, d_cq]
-  return up256(T * H * (d_k + d_r) * es) * 2 + up256(v_elems * es) + up256(T * d_cq * es);
+  // q and the RoPE queries ([T, H d_k], [T, H d_r]), K [T, H d_k], V, then
+  // the low-rank query c^Q [T, d_cq]
+  return up256(T * H * (d_k + d_r) * es) + up256(T * H * d_k * es) + up256(v_elems * es) + up256(T * d_cq * es);
 }
 
 gmla_status_t gmla_prefill(const void* x, const void* W_c, const void* W_dq, const void* W_q, const void* W_kr,
@@ -169,8 +170,9 @@ gmla_status_t gmla_prefill(const void* x, const void* W_c, const void* W_dq, con
           GMLA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   REQUIRE((long long)B * L * std::max({d_model, H * (d_k + d_r), H * d_v, d_cq}) < (1LL << 40), GMLA_ERR_UNSUPPORTED,
           "problem too large");
-  REQUIRE(d_r == 0, GMLA_ERR_UNSUPPORTED, "decoupled RoPE in prefill is not built");
+  REQUIRE(d_r == 0 || dtype == GMLA_BF16, GMLA_ERR_UNSUPPORTED, "decoupled RoPE in prefill is bf16 only");
   if (dtype == GMLA_BF16) {
+    REQUIRE(d_r == 0 || d_r == 64, GMLA_ERR_UNSUPPORTED, "bf16 prefill needs d_r in {0, 64}");
     REQUIRE(d_model % 64 == 0, GMLA_ERR_UNSUPPORTED, "bf16 prefill needs d_model % 64 == 0");
     REQUIRE(d_c % 64 == 0, GMLA_ERR_UNSUPPORTED, "bf16 prefill needs d_c % 64 == 0");
     REQUIRE(d_cq % 64 == 0, GMLA_ERR_UNSUPPORTED, "bf16 prefill needs d_cq % 64 == 0");
@@ -189,7 +191,8 @@ gmla_status_t gmla_prefill(const void* x, const void* W_c, const void* W_dq, con
   const size_t es = esize(dtype);
   char* ws = (char*)workspace;
   void* q = ws;
-  void* k = ws + up256((size_t)T * H * d_k * es);
+  void* qr = ws + (size_t)T * H * d_k * es;  // RoPE queries follow q
+  void* k = ws + up256((size_t)T * H * (d_k + d_r) * es);
   void* v = (char*)k + up256((size_t)T * H * d_k * es);
   const size_t v_elems = dtype == GMLA_BF16 ? (size_t)B * H * d_v * prefill_vt_ld(L) : (size_t)T * H * d_v;
   void* cq = (char*)v + up256(v_elems * es);
@@ -197,21 +200,33 @@ gmla_status_t gmla_prefill(const void* x, const void* W_c, const void* W_dq, con
   const void* xq = d_cq > 0 ? cq : x;
   const int dq_in = d_cq > 0 ? d_cq : d_model;
   const int HK = H * d_k, HV = H * d_v;
+  const int CW = d_c + d_r;  // cache row width: [c ; RoPE key]
   gmla_status_t s;
   if (dtype == GMLA_BF16) {
     // c = x W_c^T (cache rows), q = x W_q^T, K = c W_UK^T, V = c W_UV^T (W_UK as [H*d_k, d_c])
-    if ((s = run("gemm_latent", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_c, d_model, latent_out, d_c, T, d_c, d_model), st); }))) return s;
+    if ((s = run("gemm_latent", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_c, d_model, latent_out, CW, T, d_c, d_model), st); }))) return s;
     if (d_cq > 0 &&
         (s = run("gemm_query_down", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_dq, d_model, cq, d_cq, T, d_cq, d_model), st); })))
       return s;
     if ((s = run("gemm_query", st, [&] { return launch_gemm_bf16(gemm(xq, dq_in, W_q, dq_in, q, HK, T, HK, dq_in), st); }))) return s;
-    if ((s = run("gemm_key_recon", st, [&] { return launch_gemm_bf16(gemm(latent_out, d_c, W_uk, d_c, k, HK, T, HK, d_c), st); }))) return s;
+    if (d_r > 0) {
+      // k^R = RoPE(x W_kr^T, s) into the cache rows' tail; q^R = RoPE(u W_qr^T, t)
+      if ((s = run("gemm_rope_key", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_kr, d_model, (bf16*)latent_out + d_c, CW, T, d_r, d_model), st); })))
+        return s;
+      if ((s = run("gemm_rope_query", st, [&] { return launch_gemm_bf16(gemm(xq, dq_in, W_qr, dq_in, qr, (int64_t)H * d_r, T, H * d_r, dq_in), st); })))
+        return s;
+      RopeRowsArgs rk{(bf16*)latent_out + d_c, CW, T, 1, d_r, L, rope_base};
+      RopeRowsArgs rq{(bf16*)qr, (int64_t)H * d_r, T, H, d_r, L, rope_base};
+      if ((s = run("rope_rows", st, [&] { return launch_rope_rows(rk, st); }))) return s;
+      if ((s = run("rope_rows", st, [&] { return launch_rope_rows(rq, st); }))) return s;
+    }
+    if ((s = run("gemm_key_recon", st, [&] { return launch_gemm_bf16(gemm(latent_out, CW, W_uk, d_c, k, HK, T, HK, d_c), st); }))) return s;
     // V^T per sequence: [H d_v, Lp] = W_UV c^T (the operands swapped), the
     // columns past L written as zeros
     const int64_t Lp = (int64_t)prefill_vt_ld(L);
     if ((s = run("gemm_value_recon", st, [&] {
-           GemmArgs g = gemm(W_uv, d_c, latent_out, d_c, v, Lp, HV, L, d_c);
-           g.batches = B; g.sA = 0; g.sW = (int64_t)L * d_c; g.sC = (int64_t)HV * Lp; g.npad = (int)Lp;
+           GemmArgs g = gemm(W_uv, d_c, latent_out, CW, v, Lp, HV, L, d_c);
+           g.batches = B; g.sA = 0; g.sW = (int64_t)L * CW; g.sC = (int64_t)HV * Lp; g.npad = (int)Lp;
            return launch_gemm_bf16(g, st);
          }))) return s;
     AttnArgs a{};
@@ -222,6 +237,11 @@ gmla_status_t gmla_prefill(const void* x, const void* W_c, const void* W_dq, con
     a.svb = (int64_t)HV * Lp; a.svj = Lp; a.svh = (int64_t)d_v * Lp;
     a.sob = (int64_t)L * HV; a.sot = HV; a.soh = d_v;
     a.scale_log2 = sm_scale * 1.4426950408889634f;
+    if (d_r > 0) {
+      a.D_R = d_r;
+      a.qr = (const bf16*)qr; a.sqrb = (int64_t)L * H * d_r; a.sqrt_ = (int64_t)H * d_r; a.sqrh = d_r;
+      a.kr = (const bf16*)latent_out + d_c; a.skrb = (int64_t)L * CW; a.skrt = CW;
+    }
     if ((s = run("prefill_attn", st, [&] { return launch_prefill_attn_bf16(a, st); }))) return s;
   } else {
     if ((s = run("gemm_f32", st, [&] { return launch_gemm_f32(gemm32(x, d_model, W_c, d_model, latent_out, d_c, T, d_c, d_model), st); }))) return s;

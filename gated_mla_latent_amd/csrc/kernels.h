@@ -61,6 +61,15 @@ struct PrepareArgs {
   float rope_base;          // 0: no rotation
 };
 hipError_t launch_decode_append(const PrepareArgs& a, hipStream_t st);
+// in-place RoPE rotation of row-major rows (prefill): row r holds nvec
+// vectors of d_r elements at p + r ld + v d_r, position r % L; base 0: none
+struct RopeRowsArgs {
+  bf16* p;
+  int64_t ld;
+  int rows, nvec, d_r, L;
+  float base;
+};
+hipError_t launch_rope_rows(const RopeRowsArgs& a, hipStream_t st);
 hipError_t launch_decode_absorb(const PrepareArgs& a, hipStream_t st);
 
 hipError_t launch_decode_attn(const DecodeArgs& a, hipStream_t st);
@@ -111,11 +120,17 @@ hipError_t launch_gemm_group_bf16(GemmGroup gg, hipStream_t st);
 // Element (b, t, h, j) of q, k and o lives at X + b*sXb + t*sXt + h*sXh + j. V is transposed:
 // element (b, key t, h, j) at b svb + h svh + j svj + t, each row (b, h, j)
 // holding at least L rounded up to 64 keys, zeros past L.
+// Decoupled RoPE (D_R > 0): every head's score gains q^R_(b,t,h) . k^R_(b,s), both
+// already rotated; q^R at qr + b sqrb + t sqrt + h sqrh, the shared k^R at
+// kr + b skrb + s skrt (D_R elements each).
 struct AttnArgs {
   const bf16* q; const bf16* k; const bf16* v; bf16* o;
   int B, L, H, D;
   int64_t sqb, sqt, sqh, skb, skt, skh, svb, svj, svh, sob, sot, soh;
   float scale_log2;
+  const bf16* qr; const bf16* kr;
+  int D_R;
+  int64_t sqrb, sqrt_, sqrh, skrb, skrt;
 };
 hipError_t launch_prefill_attn_bf16(const AttnArgs& a, hipStream_t st);
 

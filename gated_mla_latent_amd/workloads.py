@@ -85,6 +85,11 @@ class PrefillInputs:
     # low-rank query (d_cq > 0): W_dq [d_cq, d_model]; W_q is then W^UQ [H*d_k, d_cq]
     d_cq: int = 0
     W_dq: torch.Tensor | None = None
+    # decoupled RoPE (d_r > 0): W_kr [d_r, d_model], W_qr [H*d_r, d_in]
+    d_r: int = 0
+    rope_base: float = 0.0
+    W_kr: torch.Tensor | None = None
+    W_qr: torch.Tensor | None = None
 
 
 def make_decode(B, H, d_c, d_r, len_lo, len_hi=None, *, rope_base=10000.0,
@@ -129,10 +134,12 @@ def make_decode(B, H, d_c, d_r, len_lo, len_hi=None, *, rope_base=10000.0,
 
 
 def make_prefill(B, L, d_model, H, d_c, d_k, d_v, *, dtype=BF16, seed=0,
-                 sm_scale=None, name="", d_cq=0) -> PrefillInputs:
+                 sm_scale=None, name="", d_cq=0, d_r=0, rope_base=10000.0) -> PrefillInputs:
     """Prefill inputs. With d_cq > 0 the query is low-rank: W_dq is drawn
-    from a generator of its own (seed + 4099) and W_q has fan-in d_cq; the
-    other tensors are drawn exactly as without it."""
+    from a generator of its own (seed + 4099) and W_q has fan-in d_cq. With
+    d_r > 0, W_kr and W_qr (fan-in d_model, and d_cq or d_model) come from
+    another (seed + 8191), and the default scale is 1/sqrt(d_k + d_r). The
+    other tensors are drawn exactly as without them."""
     gen = torch.Generator("cpu").manual_seed(seed)
     x = _randn(gen, (B, L, d_model), 1.0, dtype)
     W_c = _weight(gen, d_c, d_model, dtype)
@@ -142,13 +149,19 @@ def make_prefill(B, L, d_model, H, d_c, d_k, d_v, *, dtype=BF16, seed=0,
     W_g = _weight(gen, H * d_v, d_model, dtype)
     W_o = _weight(gen, d_model, H * d_v, dtype)
     if sm_scale is None:
-        sm_scale = 1.0 / math.sqrt(d_k)
+        sm_scale = 1.0 / math.sqrt(d_k + d_r)
     W_dq = None
     if d_cq:
         W_dq = _weight(torch.Generator("cpu").manual_seed(seed + 4099), d_cq, d_model, dtype)
+    W_kr = W_qr = None
+    if d_r:
+        g2 = torch.Generator("cpu").manual_seed(seed + 8191)
+        W_kr = _weight(g2, d_r, d_model, dtype)
+        W_qr = _weight(g2, H * d_r, d_cq if d_cq else d_model, dtype)
     return PrefillInputs(B=B, L=L, d_model=d_model, H=H, d_c=d_c, d_k=d_k, d_v=d_v,
                          sm_scale=sm_scale, dtype=dtype, x=x, W_c=W_c, W_q=W_q,
-                         W_uk=W_uk, W_uv=W_uv, W_g=W_g, W_o=W_o, name=name, d_cq=d_cq, W_dq=W_dq)
+                         W_uk=W_uk, W_uv=W_uv, W_g=W_g, W_o=W_o, name=name, d_cq=d_cq, W_dq=W_dq,
+                         d_r=d_r, rope_base=rope_base if d_r else 0.0, W_kr=W_kr, W_qr=W_qr)
 
 
 # The five workloads, with their full sizes.
@@ -175,6 +188,13 @@ def prefill_b2_l8192(seed=0):
     """bf16 causal prefill: B=2, L=8192, d_model=7168, H=64, d_c=512,
     d_k=d_v=128, NoPE, gate 7168 -> 8192 before W_o 8192 -> 7168."""
     return make_prefill(2, 8192, 7168, 64, 512, 128, 128, seed=seed, name="prefill_b2_l8192")
+
+
+def prefill_rope_b2_l8192(seed=0):
+    """bf16 causal prefill with decoupled RoPE: the prefill workload's shape
+    plus d_r = 64 (RoPE key shared by the heads, base 10000), scale
+    1/sqrt(128 + 64)."""
+    return make_prefill(2, 8192, 7168, 64, 512, 128, 128, seed=seed, d_r=64, name="prefill_rope_b2_l8192")
 
 
 def decode_rope_b8_l131072(seed=0, with_output_side=True):

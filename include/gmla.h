@@ -79,8 +79,8 @@ typedef enum { GMLA_F32 = 0, GMLA_BF16 = 1 } gmla_dtype_t;
  * interleaved, theta_i = rope_base^(-2i/d_r); rope_base 0: unrotated).
  * The gate and output projection follow with gmla_gate_out(W_uv = NULL).
  * Sizes: all >= 1 (d_cq, d_r >= 0). BF16 needs d_model, d_c and d_cq
- * % 64 == 0 and d_k == d_v in {64, 128}; F32 needs d_k <= 1024 and
- * d_v <= 512. Decoupled RoPE (d_r > 0) returns GMLA_ERR_UNSUPPORTED.
+ * % 64 == 0, d_k == d_v in {64, 128} and d_r in {0, 64}; F32 needs
+ * d_k <= 1024, d_v <= 512 and d_r == 0 (GMLA_ERR_UNSUPPORTED otherwise).
  * ---------------------------------------------------------------------- */
 size_t gmla_prefill_workspace_size(int B, int L, int H, int d_cq, int d_k, int d_r, int d_v, gmla_dtype_t dtype);
 gmla_status_t gmla_prefill(const void* x, const void* W_c, const void* W_dq, const void* W_q, const void* W_kr,

@@ -84,9 +84,9 @@ def test_prefill_workspace_size_formula(L):
         # bf16: q and K as [T, H d], V transposed per sequence as [B, H d, Lp]
         assert L.gmla_prefill_workspace_size(B, Lq, H, 0, d, 0, d, 1) == 2 * up(T * H * d * 2) + up(B * H * d * Lp * 2)
         assert L.gmla_prefill_workspace_size(B, Lq, H, 0, d, 0, d, 0) == 3 * up(T * H * d * 4)
-        # low-rank query: c^Q [T, d_cq] follows; decoupled RoPE widens q and K to d + d_r
+        # q then the RoPE queries [T, H (d + d_r)], K, V^T, then c^Q [T, d_cq]
         assert (L.gmla_prefill_workspace_size(B, Lq, H, 192, d, 64, d, 1) ==
-                2 * up(T * H * (d + 64) * 2) + up(B * H * d * Lp * 2) + up(T * 192 * 2))
+                up(T * H * (d + 64) * 2) + up(T * H * d * 2) + up(B * H * d * Lp * 2) + up(T * 192 * 2))
     assert L.gmla_prefill_workspace_size(0, 16, 2, 0, 64, 0, 64, 1) == 0
 
 
@@ -114,6 +114,8 @@ def test_prefill_argument_checks(L):
     assert _pre(L, d_r=64) == INVALID               # d_r without W_kr / W_qr
     assert _pre(L, Wkr=A, d_r=64) == INVALID
     assert _pre(L, Wkr=A, Wqr=A, d_r=63) == INVALID
+    assert _pre(L, Wkr=A, Wqr=A, d_r=32) == UNSUPPORTED      # bf16 RoPE prefill: d_r == 64
+    assert _pre(L, Wkr=A, Wqr=A, d_r=64, dt=0) == UNSUPPORTED  # ... and bf16 only
     assert _pre(L, base=-1.0) == INVALID
     assert _pre(L, wsb=100) == WORKSPACE
     assert _pre(L, Wdq=A, d_cq=64, wsb=L.gmla_prefill_workspace_size(1, 16, 2, 0, 128, 0, 128, 1)) == WORKSPACE
