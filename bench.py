@@ -112,6 +112,13 @@ def prepare_bytes(inp, d_k=DECODE_D_K):
     return B * D * 2 + weights + B * W * 2 + B * H * W * 2
 
 
+def head_gate_bytes(inp):
+    """Algorithmic HBM bytes of gmla_head_gate_out at decode: W_UV, W_g
+    [H, d_model], b_g, W_o and x read once, o_lat read once, y written once."""
+    T, D, H, dv, dc = inp.B, inp.d_model, inp.H, inp.d_v, inp.d_c
+    return (H * dv * dc + H * D + H + D * H * dv + T * D + T * H * dc + T * D) * 2
+
+
 def gate_out_flops(inp):
     T, D, H, dv, dc = inp.B, inp.d_model, inp.H, inp.d_v, inp.d_c
     return {"gemm_value_up": 2 * T * H * dv * dc, "gemm_gate": 2 * T * D * H * dv, "gemm_out": 2 * T * D * H * dv}
@@ -165,6 +172,11 @@ def build_decode(args, inp, torch, ops):
     q_new = torch.empty((inp.B, inp.H, inp.d_c + inp.d_r), dtype=torch.bfloat16, device=dev)
     wsp_n = L.gmla_decode_prepare_workspace_size(inp.B, inp.d_model, inp.H, inp.d_c, 0, DECODE_D_K, inp.d_r, 1)
     wsp = torch.empty(wsp_n, dtype=torch.uint8, device=dev)
+    # the per-head scalar gate variant of the output side (W_g [H, d_model], b_g [H])
+    hg = workloads.make_head_gate(1, inp.d_model, inp.H, inp.d_v, seed=3)
+    W_gh, b_gh = hg.W_g.to(dev), hg.b_g.to(dev)
+    wsh_n = L.gmla_head_gate_out_workspace_size(inp.B, inp.d_model, inp.H, inp.d_c, inp.d_v, 1, 1)
+    wsh = torch.empty(wsh_n, dtype=torch.uint8, device=dev)
     o_lat = torch.empty((inp.B, inp.H, inp.d_c), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((inp.B, inp.H), dtype=torch.float32, device=dev)
     y = torch.empty((inp.B, inp.d_model), dtype=torch.bfloat16, device=dev)
@@ -182,11 +194,14 @@ def build_decode(args, inp, torch, ops):
         pre = (_vp(x_new), _vp(c["W_c"]), _vp(c["W_kr"]), C.c_void_p(0), _vp(c["W_q"]), _vp(c["W_qr"]), _vp(c["W_uk"]),
                _vp(rows_new), _vp(start_new), _vp(seq_len), _vp(q_new), _vp(wsp), C.c_size_t(wsp_n), inp.B,
                inp.d_model, inp.H, inp.d_c, 0, DECODE_D_K, inp.d_r, C.c_float(inp.rope_base), 1, stream)
-        calls.append((dec, go, pre))
-    keep = (q, seq_start, seq_len, x, copies, o_lat, lse, y, wsd, wsg, x_new, rows_new, start_new, q_new, wsp)
+        hgo = (_vp(x), _vp(o_lat), _vp(c["W_uv"]), _vp(W_gh), _vp(b_gh), _vp(c["W_o"]), _vp(y), _vp(wsh),
+               C.c_size_t(wsh_n), inp.B, inp.d_model, inp.H, inp.d_c, inp.d_v, 1, stream)
+        calls.append((dec, go, pre, hgo))
+    keep = (q, seq_start, seq_len, x, copies, o_lat, lse, y, wsd, wsg, x_new, rows_new, start_new, q_new, wsp,
+            W_gh, b_gh, wsh)
 
     def step(i):
-        dec, go, _ = calls[i % len(calls)]
+        dec, go = calls[i % len(calls)][:2]
         s = L.gmla_decode(*dec)
         if s:
             raise RuntimeError(L.gmla_last_error().decode())
@@ -199,7 +214,12 @@ def build_decode(args, inp, torch, ops):
         if s:
             raise RuntimeError(L.gmla_last_error().decode())
 
-    return step, (keep, prepare)
+    def head_gate(i):
+        s = L.gmla_head_gate_out(*calls[i % len(calls)][3])
+        if s:
+            raise RuntimeError(L.gmla_last_error().decode())
+
+    return step, (keep, {"decode_prepare": prepare, "head_gate_out": head_gate})
 
 
 def build_prefill(args, p, torch, ops):
@@ -417,30 +437,33 @@ def main():
             kern[k] = {"launches_per_step": n / args.steps, "avg_us": ms * 1e3}
         ops.trace_reset()
 
-    # timed region 3 (decode): the step's input side alone, then its kernels
-    prep_us, prep_kern = None, {}
+    # timed regions 3, 4 (decode): the step's input side alone, and the
+    # per-head gate variant of its output side, each then with its kernels
+    extra = {}
     if is_decode:
-        prepare = keep[1]
-        for i in range(args.warmup):
-            prepare(i)
-        torch.cuda.synchronize()
-        ev0.record()
-        for i in range(args.steps):
-            prepare(args.warmup + i)
-        ev1.record()
-        torch.cuda.synchronize()
-        prep_us = ev0.elapsed_time(ev1) * 1e3 / args.steps
-        log(f"[bench] decode_prepare {prep_us:.1f} us")
-        if trace:
-            ops.trace_begin(16 * args.steps + 64)
-            for i in range(args.steps):
-                prepare(i)
+        for name, fn in keep[1].items():
+            for i in range(args.warmup):
+                fn(i)
             torch.cuda.synchronize()
-            ops.trace_end()
-            for k in ops.trace_kernels():
-                n, ms = ops.trace_summary(k)
-                prep_kern[k] = {"launches_per_step": n / args.steps, "avg_us": ms * 1e3}
-            ops.trace_reset()
+            ev0.record()
+            for i in range(args.steps):
+                fn(args.warmup + i)
+            ev1.record()
+            torch.cuda.synchronize()
+            us = ev0.elapsed_time(ev1) * 1e3 / args.steps
+            log(f"[bench] {name} {us:.1f} us")
+            kk = {}
+            if trace:
+                ops.trace_begin(16 * args.steps + 64)
+                for i in range(args.steps):
+                    fn(i)
+                torch.cuda.synchronize()
+                ops.trace_end()
+                for k in ops.trace_kernels():
+                    n, ms = ops.trace_summary(k)
+                    kk[k] = {"launches_per_step": n / args.steps, "avg_us": ms * 1e3}
+                ops.trace_reset()
+            extra[name] = (us, kk)
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -480,11 +503,17 @@ def main():
             t_att = sum(kern[k]["avg_us"] * kern[k]["launches_per_step"] for k in ("decode_attn", "decode_combine"))
             out["attention_only"] = {"us": t_att, "tokens_per_s": inp.B / (t_att * 1e-6)}
         pb = prepare_bytes(inp)
+        prep_us, prep_kern = extra["decode_prepare"]
         out["decode_prepare"] = {"us": prep_us, "alg_bytes": pb, "hbm_gbs": pb / (prep_us * 1e-6) / 1e9,
                                  "hbm_frac": pb / (prep_us * 1e-6) / 1e9 / HBM_PEAK_GBS, "d_k": DECODE_D_K,
                                  "kernels": prep_kern,
                                  "layer_us": ms_step * 1e3 + prep_us,
                                  "layer_tokens_per_s": inp.B / ((ms_step * 1e3 + prep_us) * 1e-6)}
+        hb = head_gate_bytes(inp)
+        hg_us, hg_kern = extra["head_gate_out"]
+        out["head_gate_out"] = {"us": hg_us, "alg_bytes": hb, "hbm_gbs": hb / (hg_us * 1e-6) / 1e9,
+                                "hbm_frac": hb / (hg_us * 1e-6) / 1e9 / HBM_PEAK_GBS, "kernels": hg_kern,
+                                "per_channel_gate_out_us": sum(kern[k]["avg_us"] for k in gb if k in kern)}
         if not args.no_cpu_baseline:
             log("[bench] cpu baseline (fp64 oracle)")
             out["cpu_baseline"] = cpu_baseline_decode(inp, args.cpu_seconds)

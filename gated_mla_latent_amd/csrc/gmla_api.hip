@@ -478,6 +478,58 @@ gmla_status_t gmla_gate_out(const void* x, const void* o, const void* W_uv, cons
   return ok();
 }
 
+// ============================================================ per-head gate + output
+size_t gmla_head_gate_out_workspace_size(int T, int d_model, int H, int d_c, int d_v, int with_value_up,
+                                         gmla_dtype_t dtype) {
+  if (T <= 0 || d_model <= 0 || H <= 0 || d_v <= 0 || (with_value_up && d_c <= 0) || dtype != GMLA_BF16) return 0;
+  const int HV = H * d_v;
+  size_t part = std::max(gemm_part_bytes(T, H, d_model, 1), gemm_part_bytes(T, d_model, HV, 1));
+  if (with_value_up) part = std::max(part, gemm_part_bytes(T, d_v, d_c, H));
+  const size_t one = up256((size_t)T * HV * 2);
+  return (with_value_up ? 2 : 1) * one + up256((size_t)T * H * 2) + up256(part);
+}
+
+gmla_status_t gmla_head_gate_out(const void* x, const void* o, const void* W_uv, const void* W_g, const void* b_g,
+                                 const void* W_o, void* y, void* workspace, size_t workspace_bytes, int T, int d_model,
+                                 int H, int d_c, int d_v, gmla_dtype_t dtype, void* stream) {
+  REQUIRE(dtype == GMLA_F32 || dtype == GMLA_BF16, GMLA_ERR_INVALID_ARG, "dtype must be GMLA_F32 or GMLA_BF16");
+  REQUIRE(x && o && W_g && W_o && y, GMLA_ERR_INVALID_ARG, "null tensor pointer");
+  REQUIRE(T > 0 && d_model > 0 && H > 0 && d_v > 0 && (!W_uv || d_c > 0), GMLA_ERR_INVALID_ARG,
+          "sizes must be positive");
+  REQUIRE(al16(x) && al16(o) && (!W_uv || al16(W_uv)) && al16(W_g) && (!b_g || al16(b_g)) && al16(W_o) && al16(y),
+          GMLA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  REQUIRE(dtype == GMLA_BF16, GMLA_ERR_UNSUPPORTED, "head_gate_out is bf16 only");
+  const int HV = H * d_v;
+  REQUIRE(d_model % 64 == 0 && HV % 64 == 0 && d_v % 8 == 0 && H % 4 == 0 && (!W_uv || d_c % 64 == 0),
+          GMLA_ERR_UNSUPPORTED,
+          "bf16 head_gate_out needs d_model % 64 == 0, H*d_v % 64 == 0, d_v % 8 == 0, H % 4 == 0, d_c % 64 == 0");
+  const size_t need = gmla_head_gate_out_workspace_size(T, d_model, H, d_c, d_v, W_uv != nullptr, dtype);
+  REQUIRE(workspace && workspace_bytes >= need, GMLA_ERR_WORKSPACE,
+          "head_gate_out workspace needs " + std::to_string(need) + " bytes");
+  REQUIRE(((uintptr_t)workspace & 255u) == 0, GMLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const size_t one = up256((size_t)T * HV * 2);
+  void* gated = ws;
+  void* otw = ws + one;
+  void* z = ws + (W_uv ? 2 : 1) * one;
+  void* part = (char*)z + up256((size_t)T * H * 2);
+  const void* ot = o;
+  gmla_status_t s;
+  if (W_uv) {
+    GemmArgs g = gemm(o, (int64_t)H * d_c, W_uv, d_c, otw, HV, T, d_v, d_c);
+    g.batches = H; g.sA = d_c; g.sW = (int64_t)d_v * d_c; g.sC = d_v;
+    g = with_split(g, part);
+    if ((s = run("gemm_value_up", st, [&] { return launch_gemm_bf16(g, st); }))) return s;
+    ot = otw;
+  }
+  if ((s = run("gemm_gate_logits", st, [&] { return launch_gemm_bf16(with_split(gemm(x, d_model, W_g, d_model, z, H, T, H, d_model), part), st); }))) return s;
+  HeadGateArgs hg{(const bf16*)z, (const bf16*)b_g, (const bf16*)ot, (bf16*)gated, T, H, d_v, H, HV, HV};
+  if ((s = run("head_gate", st, [&] { return launch_head_gate(hg, st); }))) return s;
+  if ((s = run("gemm_out", st, [&] { return launch_gemm_bf16(with_split(gemm(gated, HV, W_o, HV, y, d_model, T, d_model, HV), part), st); }))) return s;
+  return ok();
+}
+
 // ============================================================ trace
 gmla_status_t gmla_trace_begin(int max_launches) {
   REQUIRE(max_launches > 0 && max_launches <= (1 << 20), GMLA_ERR_INVALID_ARG, "max_launches out of range");

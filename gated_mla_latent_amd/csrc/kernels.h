@@ -72,6 +72,17 @@ struct RopeRowsArgs {
 hipError_t launch_rope_rows(const RopeRowsArgs& a, hipStream_t st);
 hipError_t launch_decode_absorb(const PrepareArgs& a, hipStream_t st);
 
+// per-head scalar gate: gated[t, h d_v + j] = sigmoid(z[t, h] + bias[h]) o[t, h d_v + j]
+struct HeadGateArgs {
+  const bf16* z;     // [T, ldz] gate logits x W_g^T
+  const bf16* bias;  // [H] or null
+  const bf16* o;     // [T, ldo] o~
+  bf16* gated;       // [T, ldg]
+  int T, H, d_v;
+  int64_t ldz, ldo, ldg;
+};
+hipError_t launch_head_gate(const HeadGateArgs& a, hipStream_t st);
+
 hipError_t launch_decode_attn(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st);
 bool decode_bf16_supported(int d_c, int d_r);

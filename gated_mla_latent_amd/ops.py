@@ -55,6 +55,10 @@ def lib():
     L.gmla_decode_prepare_workspace_size.restype = sz
     L.gmla_decode_prepare.argtypes = [vp] * 11 + [vp, sz] + [i32] * 7 + [f32, i32, vp]
     L.gmla_decode_prepare.restype = i32
+    L.gmla_head_gate_out_workspace_size.argtypes = [i32] * 7
+    L.gmla_head_gate_out_workspace_size.restype = sz
+    L.gmla_head_gate_out.argtypes = [vp] * 7 + [vp, sz] + [i32] * 5 + [i32, vp]
+    L.gmla_head_gate_out.restype = i32
     L.gmla_gate_out_workspace_size.argtypes = [i32] * 7
     L.gmla_gate_out_workspace_size.restype = sz
     L.gmla_gate_out.argtypes = [vp] * 6 + [vp, sz] + [i32] * 5 + [i32, vp]
@@ -208,6 +212,25 @@ def gate_out(x, o, W_g, W_o, W_uv=None, y=None, workspace=None):
     workspace, wsb = _workspace(need, x.device, workspace)
     _check(lib().gmla_gate_out(_vp(x), _vp(o), _vp(W_uv), _vp(W_g), _vp(W_o), _vp(y), _vp(workspace), wsb,
                                T, D, H, d_c, d_v, dt, _stream()))
+    return y
+
+
+def head_gate_out(x, o, W_g, W_o, b_g=None, W_uv=None, y=None, workspace=None):
+    """y = W_o [g_h * o~_h], g = Sigmoid(x W_g^T + b_g) per head (W_g [H, d_model]).
+    With W_uv given, `o` is o_lat [T, H, d_c]; else `o` is o~ [T, H*d_v]."""
+    _dev(x, o, W_g, W_o, b_g, W_uv, y, workspace)
+    T, D = x.shape[0], x.shape[-1]
+    H = W_g.shape[0]
+    HV = W_o.shape[1]
+    d_v = HV // H
+    d_c = W_uv.shape[2] if W_uv is not None else 0
+    dt = _dtype_code(x)
+    if y is None:
+        y = torch.empty((T, D), dtype=x.dtype, device=x.device)
+    need = lib().gmla_head_gate_out_workspace_size(T, D, H, d_c, d_v, int(W_uv is not None), dt)
+    workspace, wsb = _workspace(need, x.device, workspace)
+    _check(lib().gmla_head_gate_out(_vp(x), _vp(o), _vp(W_uv), _vp(W_g), _vp(b_g), _vp(W_o), _vp(y), _vp(workspace),
+                                    wsb, T, D, H, d_c, d_v, dt, _stream()))
     return y
 
 

@@ -240,3 +240,34 @@ def make_decode_step(dec: DecodeInputs, d_model: int, d_k: int, *, seed=0, d_cq=
     W_dq = _weight(gen, d_cq, d_model, dt) if d_cq else None
     return DecodeStepInputs(d_model=d_model, d_k=d_k, x=x, W_c=W_c, W_kr=W_kr, W_q=W_q, W_qr=W_qr, W_uk=W_uk,
                             d_cq=d_cq, W_dq=W_dq)
+
+
+@dataclass
+class HeadGateInputs:
+    """Inputs of the per-head scalar gate and output projection: x [T, d_model],
+    o (o~ [T, H*d_v], or o_lat [T, H, d_c] with W_uv [H, d_v, d_c]),
+    W_g [H, d_model], b_g [H] (or None), W_o [d_model, H*d_v]."""
+    T: int
+    d_model: int
+    H: int
+    d_v: int
+    d_c: int
+    x: torch.Tensor
+    o: torch.Tensor
+    W_uv: torch.Tensor | None
+    W_g: torch.Tensor
+    b_g: torch.Tensor | None
+    W_o: torch.Tensor
+
+
+def make_head_gate(T, d_model, H, d_v, d_c=0, *, with_bias=True, dtype=BF16, seed=0) -> HeadGateInputs:
+    """Drawn in the order x, o, W_uv (d_c > 0: the decode form), W_g, b_g,
+    W_o; o and the bias are N(0, 1), weights N(0, 1/fan_in)."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    x = _randn(gen, (T, d_model), 1.0, dtype)
+    o = _randn(gen, (T, H, d_c) if d_c else (T, H * d_v), 1.0, dtype)
+    W_uv = _weight(gen, d_v, d_c, dtype, lead=(H,)) if d_c else None
+    W_g = _weight(gen, H, d_model, dtype)
+    b_g = _randn(gen, (H,), 1.0, dtype) if with_bias else None
+    W_o = _weight(gen, d_model, H * d_v, dtype)
+    return HeadGateInputs(T=T, d_model=d_model, H=H, d_v=d_v, d_c=d_c, x=x, o=o, W_uv=W_uv, W_g=W_g, b_g=b_g, W_o=W_o)

@@ -182,6 +182,27 @@ gmla_status_t gmla_gate_out(const void* x, const void* o, const void* W_uv, cons
                             int d_v, gmla_dtype_t dtype, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Per-head scalar gate and output projection ("Gated Multi-head Latent
+ * Attention (Gated MLA)" concept page [CD], Gating Mechanism and
+ * Mathematical Formulation):
+ *   g_t = Sigmoid(W_g x_t + b_g) in R^H,  y_t = W_o [ g_t[h] o~_t^(h) ]_h
+ * head h's output block (channels h*d_v .. h*d_v + d_v - 1) scaled by one
+ * scalar. `o` and W_uv as in gmla_gate_out (W_uv given: `o` is o_lat
+ * [T, H, d_c] and o~_h = W_uv[h] o_lat_h first).
+ *   x [T, d_model], W_g [H, d_model], b_g [H] or NULL (zero),
+ *   W_o [d_model, H*d_v], y [T, d_model]
+ * The logits x W_g^T are rounded to bf16 before the bias and the sigmoid.
+ * Only GMLA_BF16 (GMLA_ERR_UNSUPPORTED otherwise); it needs
+ * d_model % 64 == 0, (H*d_v) % 64 == 0, d_v % 8 == 0, H % 4 == 0 and, with
+ * W_uv, d_c % 64 == 0. Workspace: 256-byte aligned, the size below.
+ * ---------------------------------------------------------------------- */
+size_t gmla_head_gate_out_workspace_size(int T, int d_model, int H, int d_c, int d_v, int with_value_up,
+                                         gmla_dtype_t dtype);
+gmla_status_t gmla_head_gate_out(const void* x, const void* o, const void* W_uv, const void* W_g, const void* b_g,
+                                 const void* W_o, void* y, void* workspace, size_t workspace_bytes, int T, int d_model,
+                                 int H, int d_c, int d_v, gmla_dtype_t dtype, void* stream);
+
+/* ------------------------------------------------------------------------
  * Diagnostics
  * ---------------------------------------------------------------------- */
 const char* gmla_status_string(gmla_status_t status);

@@ -221,6 +221,31 @@ def test_gate_out_argument_checks(L):
     assert _gate(L, wsb=10) == WORKSPACE
 
 
+def _hg(L, **kw):
+    a = dict(x=A, o=A, Wuv=0, Wg=A, bg=0, Wo=A, y=A, ws=A, wsb=1 << 40, T=4, D=256, H=4, d_c=0, d_v=64, dt=1)
+    a.update(kw)
+    return L.gmla_head_gate_out(a["x"], a["o"], a["Wuv"], a["Wg"], a["bg"], a["Wo"], a["y"], a["ws"], a["wsb"],
+                                a["T"], a["D"], a["H"], a["d_c"], a["d_v"], a["dt"], None)
+
+
+def test_head_gate_out_argument_checks_and_workspace(L):
+    assert _hg(L, Wg=0) == INVALID
+    assert _hg(L, bg=A + 2) == INVALID              # misaligned bias
+    assert _hg(L, Wuv=A, d_c=0) == INVALID
+    assert _hg(L, dt=0) == UNSUPPORTED              # bf16 only
+    assert _hg(L, H=3) == UNSUPPORTED               # H % 4
+    assert _hg(L, d_v=60, H=16) == UNSUPPORTED      # d_v % 8
+    assert _hg(L, wsb=10) == WORKSPACE
+    assert _hg(L, ws=A + 16) == INVALID             # workspace must be 256-byte aligned
+    up = lambda n: (n + 255) // 256 * 256
+    for T, D, H, d_c, d_v, vu in [(4, 256, 4, 0, 64, 0), (32, 1024, 64, 512, 128, 1), (300, 256, 4, 0, 128, 0)]:
+        HV = H * d_v
+        part = max(_part(T, H, D), _part(T, D, HV), _part(T, d_v, d_c, H) if vu else 0)
+        want = (2 if vu else 1) * up(T * HV * 2) + up(T * H * 2) + up(part)
+        assert L.gmla_head_gate_out_workspace_size(T, D, H, d_c, d_v, vu, 1) == want
+    assert L.gmla_head_gate_out_workspace_size(4, 256, 4, 0, 64, 0, 0) == 0
+
+
 def test_trace_api_without_launches(L):
     assert L.gmla_trace_begin(0) == INVALID
     n, ms = C.c_int(5), C.c_double(1.0)
