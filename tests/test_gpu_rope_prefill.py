@@ -93,3 +93,28 @@ def test_rope_prefill_cache_feeds_rope_decode():
     e = rel_err(torch.from_numpy(o[0]), rot[0, 0])
     say(f"  rel err {e:.2e}")
     assert e <= 2e-2
+
+
+@pytest.mark.slow
+def test_rope_prefill_full_size_sampled_rows():
+    """The RoPE prefill workload at full size (B=2, L=8192, d_model=7168,
+    H=64, d_k=d_v=128, d_r=64) as the benchmark launches it: the cache rows of
+    a seeded sample of tokens and o~ on a seeded sample of query rows."""
+    say("[rope prefill full] generating")
+    inp = W.prefill_rope_b2_l8192()
+    rows_gpu, ot = _run(inp)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    rows = sorted(set([0, 1, 4095, inp.L - 1] + rng.choice(inp.L, 8, replace=False).tolist()))
+    say(f"  oracle on rows {rows}")
+    _, rot, _ = O.prefill_reference(_np(inp.x), _np(inp.W_c), _np(inp.W_q), _np(inp.W_uk), _np(inp.W_uv),
+                                    inp.sm_scale, rows=rows, W_kr=_np(inp.W_kr), W_qr=_np(inp.W_qr),
+                                    rope_base=inp.rope_base)
+    e_rows = []
+    for b in range(inp.B):
+        ref_rows, _ = O.decode_prepare_reference(_np(inp.x[b, rows]), _np(inp.W_c), _np(inp.W_kr), _np(inp.W_q),
+                                                 _np(inp.W_qr), _np(inp.W_uk), np.asarray(rows), inp.rope_base)
+        e_rows.append(rel_err(rows_gpu[b, rows].float(), ref_rows))
+    e_o = rel_err(ot[:, rows].float(), rot)
+    say(f"  rel err cache rows {max(e_rows):.2e}  o~ {e_o:.2e}")
+    assert max(e_rows) <= BF16_TOL and e_o <= BF16_TOL
