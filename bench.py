@@ -70,6 +70,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
+    ap.add_argument("--no-measured-peak", action="store_true",
+                    help="skip the measured reference peaks (device copy, library GEMM)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (reference for HBM byte counters)")
     return ap.parse_args()
@@ -328,6 +330,43 @@ def cpu_baseline_prefill(p, budget_s):
                       f"({sum(fl.values()) / 1e9:.1f} GFLOP); {secs:.1f} s on the host"}
 
 
+def measured_peak(torch, bound):
+    """A measured reference beside the published peak, labelled separately:
+    HBM: a device-to-device copy of 1 GiB (bytes read + written per second);
+    MFMA: torch.matmul (the vendor GEMM library) on an 8192^3 bf16 product."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    if bound == "hbm":
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        v = 2 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del src, dst
+        return {"value": v, "unit": "GB/s", "how": "device-to-device copy of 1 GiB, read + write bytes"}
+    n = 8192
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    v = 2 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b
+    return {"value": v, "unit": "TFLOP/s", "how": "torch.matmul (vendor library) bf16 8192 x 8192 x 8192"}
+
+
 # ----------------------------------------------------------------------------- main
 
 # HBM traffic of a kernel, from a committed rocprofv3 counter summary
@@ -540,6 +579,11 @@ def main():
         if not args.no_cpu_baseline:
             log("[bench] cpu baseline (fp64 oracle)")
             out["cpu_baseline"] = cpu_baseline_prefill(inp, args.cpu_seconds)
+    roof = out.get("roofline")
+    if roof and not args.no_measured_peak and roof["bound"] in ("hbm", "mfma"):
+        mp = measured_peak(torch, roof["bound"])
+        roof["measured_peak"] = mp
+        roof["frac_of_measured"] = roof["achieved"] / mp["value"]
     print(json.dumps(out), flush=True)
 
 
