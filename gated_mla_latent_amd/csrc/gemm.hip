@@ -228,19 +228,25 @@ void gemm_tile_kernel(GemmArgs g) {
 // Rows are 128 bytes; the 16-byte piece p of row r is stored at piece
 // p ^ ((r >> 2) & 7), which makes the fragment reads (32 rows at one piece
 // per half-wave) hit 32 distinct bank groups.
-template <int MT>
+// NT = 2: a workgroup owns 64 columns, so each activation chunk in LDS
+// serves two weight tiles (half the activation bytes per weight byte) at the
+// price of one buffer less per wave.
+template <int MT, int NT>
 struct SkinnyCfg {
-  static constexpr int NBUF = MT == 1 ? 4 : 3;
-  static constexpr int W_BYTES = 32 * 128;           // 32 weight rows x 64 K
+  static constexpr int NBUF = (MT == 1 ? 4 : 3) - (NT - 1);
+  static constexpr int W_BYTES = NT * 32 * 128;      // 32 NT weight rows x 64 K
   static constexpr int A_BYTES = MT * 32 * 128;      // 32 MT rows of A x 64 K
   static constexpr int BUF_BYTES = W_BYTES + A_BYTES;
   static constexpr int WAVE_BYTES = NBUF * BUF_BYTES;
   static constexpr int RPC = (W_BYTES + A_BYTES) / 1024;  // DMA instructions per chunk
   static constexpr int LDS_BYTES = 4 * WAVE_BYTES;
+  static_assert(NT == 1 || NT == 2, "32 or 64 columns per workgroup");
   static_assert(LDS_BYTES <= 163840, "LDS budget");
-  static_assert(LDS_BYTES >= 4 * MT * 16 * 64 * 4, "reduction fits in the ring");
+  static_assert(LDS_BYTES >= 4 * NT * MT * 16 * 64 * 4, "reduction fits in the ring");
   static_assert((NBUF - 1) * RPC < 64, "vmcnt range");
 };
+// use 64-column workgroups when the grid still has a workgroup per CU
+constexpr bool kSkinnyNT2 = true;
 
 template <int RPC, int MAXP>
 __device__ __forceinline__ void skinny_wait(int pending) {
@@ -250,10 +256,10 @@ __device__ __forceinline__ void skinny_wait(int pending) {
   wait_vmcnt<0>();
 }
 
-// Columns n0 .. n0 + 31 of batch `batch`, K slice zi of nz.
-template <int MT, int EPI>
+// Columns n0 .. n0 + 32 NT - 1 of batch `batch`, K slice zi of nz.
+template <int MT, int NT, int EPI>
 __device__ __forceinline__ void skinny_body(const GemmArgs& g, int n0, int batch, int zi, int nz) {
-  using C = SkinnyCfg<MT>;
+  using C = SkinnyCfg<MT, NT>;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -278,7 +284,7 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& g, int n0, int batch
   auto issue = [&](int b, int j) {
     const unsigned dst = ring_addr + b * C::BUF_BYTES;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 4 * NT; ++q) {
       int row = n0 + 8 * q + lr;
       row = row < g.N ? row : g.N - 1;
       const unsigned long long base = (unsigned long long)(uintptr_t)(W + (int64_t)j * 64);
@@ -297,9 +303,11 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& g, int n0, int batch
     return as_bf16x8(lds_read16(tile + r * 128 + ((p ^ ((r >> 2) & 7)) << 4)));
   };
 
-  floatx16 acc[MT];
+  floatx16 acc[NT][MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = floatx16{};
+  for (int u = 0; u < NT; ++u)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[u][t] = floatx16{};
   const int span = c_hi > c_lo ? c_hi - c_lo : 0;
   const int nmy = span > wave ? (span - wave + 3) / 4 : 0;  // this wave's chunks: c_lo + wave, + 4, ...
 #pragma unroll
@@ -315,9 +323,15 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& g, int n0, int batch
     const LDS_AS char* at = wt + C::W_BYTES;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const bf16x8 wf = frag(wt, r32, 2 * kk + hk);
+      bf16x8 af[MT];
 #pragma unroll
-      for (int t = 0; t < MT; ++t) acc[t] = mfma32(wf, frag(at, 32 * t + r32, 2 * kk + hk), acc[t]);
+      for (int t = 0; t < MT; ++t) af[t] = frag(at, 32 * t + r32, 2 * kk + hk);
+#pragma unroll
+      for (int u = 0; u < NT; ++u) {
+        const bf16x8 wf = frag(wt + u * 4096, r32, 2 * kk + hk);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[u][t] = mfma32(wf, af[t], acc[u][t]);
+      }
     }
     if (i + C::NBUF < nmy) {
       wait_lgkm0();  // this buffer's fragments are in registers before it is refilled
@@ -326,25 +340,29 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& g, int n0, int batch
   }
 
   __syncthreads();  // every wave is done with its ring: reuse it for the reduction
-  LDS_AS float* red = (LDS_AS float*)smem;  // [4 waves][MT][16][64]
+  constexpr int NA = NT * MT;  // accumulators per wave
+  LDS_AS float* red = (LDS_AS float*)smem;  // [4 waves][NT MT][16][64]
 #pragma unroll
-  for (int t = 0; t < MT; ++t)
+  for (int u = 0; u < NT; ++u)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) red[((wave * MT + t) * 16 + r) * 64 + lane] = acc[t][r];
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[((wave * NA + u * MT + t) * 16 + r) * 64 + lane] = acc[u][t][r];
   __syncthreads();
   // wave w finishes register group r4 = w (4 consecutive columns per lane)
 #pragma unroll
-  for (int t = 0; t < MT; ++t) {
+  for (int ut = 0; ut < NA; ++ut) {
+    const int u = ut / MT, t = ut % MT;
     float v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * wave + e;
       v[e] = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) v[e] += red[((w * MT + t) * 16 + r) * 64 + lane];
+      for (int w = 0; w < 4; ++w) v[e] += red[((w * NA + ut) * 16 + r) * 64 + lane];
     }
     const int m = 32 * t + (lane & 31);
-    const int n = n0 + 8 * wave + 4 * (lane >> 5);
+    const int n = n0 + 32 * u + 8 * wave + 4 * (lane >> 5);
     if (nz > 1) {  // partial sums [slice][batch][M][N rounded up to 4]
       const int ldp = (g.N + 3) & ~3;
       if (m < g.M && n < g.N)
@@ -356,14 +374,14 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& g, int n0, int batch
   }
 }
 
-template <int MT, int EPI>
+template <int MT, int NT, int EPI>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
-  skinny_body<MT, EPI>(g, blockIdx.x * 32, blockIdx.y, blockIdx.z, gridDim.z);
+  skinny_body<MT, NT, EPI>(g, blockIdx.x * 32 * NT, blockIdx.y, blockIdx.z, gridDim.z);
 }
 
 // Several plain-store GEMMs that share A, M and K in one grid: segment s
 // owns workgroups first_wg[s] .. first_wg[s + 1] - 1.
-template <int MT>
+template <int MT, int NT>
 __global__ __launch_bounds__(256) void gemm_skinny_group_kernel(GemmGroup gg) {
   const int x = blockIdx.x;
   const int s = (x >= gg.first_wg[1]) + (x >= gg.first_wg[2]) + (x >= gg.first_wg[3]);
@@ -374,7 +392,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_group_kernel(GemmGroup gg) {
   g.ldw = s == 0 ? gg.ldw[0] : s == 1 ? gg.ldw[1] : s == 2 ? gg.ldw[2] : gg.ldw[3];
   g.ldc = s == 0 ? gg.ldc[0] : s == 1 ? gg.ldc[1] : s == 2 ? gg.ldc[2] : gg.ldc[3];
   const int first = s == 0 ? 0 : s == 1 ? gg.first_wg[1] : s == 2 ? gg.first_wg[2] : gg.first_wg[3];
-  skinny_body<MT, EPI_STORE>(g, (x - first) * 32, 0, 0, 1);
+  skinny_body<MT, NT, EPI_STORE>(g, (x - first) * 32 * NT, 0, 0, 1);
 }
 
 // Sum the split-K partial sums of 4 consecutive columns and apply the
@@ -399,10 +417,10 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmArgs g) {
   store4<EPI>(g, Cp, Op, m, n, acc.x, acc.y, acc.z, acc.w);
 }
 
-template <int MT, int EPI>
+template <int MT, int NT, int EPI>
 static hipError_t launch_skinny(const GemmArgs& g, hipStream_t st) {
-  using C = SkinnyCfg<MT>;
-  auto kern = gemm_skinny_kernel<MT, EPI>;
+  using C = SkinnyCfg<MT, NT>;
+  auto kern = gemm_skinny_kernel<MT, NT, EPI>;
   static bool attr = false;
   if (!attr) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
@@ -411,7 +429,7 @@ static hipError_t launch_skinny(const GemmArgs& g, hipStream_t st) {
   }
   const int z = g.ksplit > 1 ? g.ksplit : 1;
   if (z > 1 && !g.part) return hipErrorInvalidValue;
-  hipError_t e = launch(kern, dim3((g.N + 31) / 32, g.batches, z), dim3(256), C::LDS_BYTES, st, g);
+  hipError_t e = launch(kern, dim3((g.N + 32 * NT - 1) / (32 * NT), g.batches, z), dim3(256), C::LDS_BYTES, st, g);
   if (e != hipSuccess || z == 1) return e;
   const int64_t n4 = (int64_t)g.batches * g.M * (((g.N + 3) & ~3) / 4);
   return launch(gemm_splitk_reduce_kernel<EPI>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, g);
@@ -443,7 +461,10 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
     // the DMA offsets are 32-bit: every row start must be below 4 GiB
     if ((long long)g.N * g.ldw * 2 >= (1LL << 32) || (long long)g.M * g.lda * 2 >= (1LL << 32))
       return hipErrorInvalidValue;
-    return g.M <= 32 ? launch_skinny<1, EPI>(g, st) : launch_skinny<2, EPI>(g, st);
+    // 64-column workgroups when that still gives one per compute unit
+    const bool nt2 = kSkinnyNT2 && g.ksplit <= 1 && (long long)((g.N + 63) / 64) * g.batches >= 256;
+    if (g.M <= 32) return nt2 ? launch_skinny<1, 2, EPI>(g, st) : launch_skinny<1, 1, EPI>(g, st);
+    return nt2 ? launch_skinny<2, 2, EPI>(g, st) : launch_skinny<2, 1, EPI>(g, st);
   }
   const long long big_tiles = (long long)((g.N + 255) / 256) * ((g.M + 255) / 256) * g.batches;
   if (big_tiles >= 256) return launch_tile<256, 256, EPI>(g, st);
@@ -471,17 +492,34 @@ size_t gemm_part_bytes(int M, int N, int K, int batches, int npad) {
   return z > 1 ? (size_t)z * batches * M * (size_t)((N + 3) & ~3) * 4 : 0;
 }
 
+template <int MT, int NT>
+static hipError_t launch_group(const GemmGroup& gg, int wgs, hipStream_t st) {
+  using C = SkinnyCfg<MT, NT>;
+  auto kern = gemm_skinny_group_kernel<MT, NT>;
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  return launch(kern, dim3(wgs), dim3(256), C::LDS_BYTES, st, gg);
+}
+
 hipError_t launch_gemm_group_bf16(GemmGroup gg, hipStream_t st) {
   const GemmArgs& b = gg.base;
   if (gg.count < 1 || gg.count > 4 || b.M <= 0 || b.M > 64 || b.K % 64 != 0) return hipErrorInvalidValue;
   if ((long long)b.M * b.lda * 2 >= (1LL << 32)) return hipErrorInvalidValue;
+  // 64-column workgroups when that still gives one per compute unit
+  long long wide = 0;
+  for (int s = 0; s < gg.count; ++s) wide += (gg.N[s] + 63) / 64;
+  const int cols = kSkinnyNT2 && wide >= 256 ? 64 : 32;
   int first = 0;
   for (int s = 0; s < 4; ++s) {
     if (s < gg.count) {
       if (gg.N[s] <= 0 || gg.N[s] % 4 != 0 || (long long)gg.N[s] * gg.ldw[s] * 2 >= (1LL << 32))
         return hipErrorInvalidValue;
       if (s > 0) gg.first_wg[s] = first;
-      first += (gg.N[s] + 31) / 32;
+      first += (gg.N[s] + cols - 1) / cols;
     } else {
       gg.first_wg[s] = INT32_MAX;  // no workgroup reaches an unused segment
     }
@@ -491,20 +529,8 @@ hipError_t launch_gemm_group_bf16(GemmGroup gg, hipStream_t st) {
   gg.base.ksplit = 1;
   gg.base.epi = EPI_STORE;
   gg.base.npad = 0;
-  using C1 = SkinnyCfg<1>;
-  using C2 = SkinnyCfg<2>;
-  auto k1 = gemm_skinny_group_kernel<1>;
-  auto k2 = gemm_skinny_group_kernel<2>;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)k1, hipFuncAttributeMaxDynamicSharedMemorySize, C1::LDS_BYTES);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)k2, hipFuncAttributeMaxDynamicSharedMemorySize, C2::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
-  return b.M <= 32 ? launch(k1, dim3(first), dim3(256), C1::LDS_BYTES, st, gg)
-                   : launch(k2, dim3(first), dim3(256), C2::LDS_BYTES, st, gg);
+  if (b.M <= 32) return cols == 64 ? launch_group<1, 2>(gg, first, st) : launch_group<1, 1>(gg, first, st);
+  return cols == 64 ? launch_group<2, 2>(gg, first, st) : launch_group<2, 1>(gg, first, st);
 }
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t st) {

@@ -51,7 +51,11 @@ def test_prefill_fp32_tiny_config():
 
 
 @pytest.mark.parametrize("T,D,H,d_c,d_v", [(32, 1024, 64, 512, 128), (64, 512, 16, 256, 64), (8, 256, 8, 128, 32),
-                                           (5, 512, 4, 64, 128), (100, 512, 4, 128, 64)])
+                                           (5, 512, 4, 64, 128), (100, 512, 4, 128, 64),
+                                           # 64-column skinny workgroups (gate and value up-projection) and
+                                           # split-K W_o, at 33..64 and at <= 32 rows
+                                           (64, 512, 128, 512, 128), (20, 512, 128, 128, 128),
+                                           (37, 256, 136, 64, 128)])
 def test_gate_out_with_value_up_projection(T, D, H, d_c, d_v):
     say(f"[gate_out decode-side] T={T} D={D} H={H} d_c={d_c} d_v={d_v}")
     g = torch.Generator().manual_seed(5)
