@@ -11,8 +11,12 @@
  *         y_t = W_o [ Sigmoid(W_g x_t) (.) o~_t ]; NoPE in Kimi K3.
  *   [N03] "LLM 注意力与计算内核精读笔记 · 03 注意力头变体：MQA / GQA / MLA" --
  *         §5.1: W^UK folds into the query and W^UV moves past the weighted
- *         sum, so decode attends the latent directly; §5.2: decoupled RoPE,
- *         a shared d_h^R-wide rotated key cached next to the latent.
+ *         sum, so decode attends the latent directly, and the low-rank
+ *         query c^Q = W^DQ x; §5.2: decoupled RoPE, a shared d_h^R-wide
+ *         rotated key cached next to the latent.
+ *   [CD]  "Gated Multi-head Latent Attention (Gated MLA)" (concept page) --
+ *         Gating Mechanism, Mathematical Formulation: the per-head scalar
+ *         gate g_h = Sigmoid(W_g x + b_g) scaling head h's output.
  *
  * Conventions shared by every entry point
  *   - Every tensor is dense and row-major (last index fastest). Weights use
