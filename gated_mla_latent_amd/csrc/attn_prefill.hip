@@ -35,7 +35,8 @@
 //    workgroup redoes the pass once with the true maxima (exact for any
 //    input).
 //  * Each workgroup takes two query tiles, the k-th longest and the k-th
-//    shortest, so all workgroups carry the same causal work.
+//    shortest, so all workgroups carry the same causal work. The work items
+//    of one (b, h) are placed on one XCD, where they share its L2.
 //  * Decoupled RoPE ([N03] "LLM 注意力与计算内核精读笔记 · 03" §5.2): the
 //    score gains q^R . k^R over DR more features, the rotated RoPE query of
 //    the head and the RoPE key shared by all heads. They are DR / 16 more
@@ -105,8 +106,17 @@ void prefill_attn_kernel(AttnArgs a) {
   // short causal tile per workgroup, so every workgroup has the same work
   const int nqt = (a.L + C::BQ - 1) / C::BQ;
   const int npair = (nqt + 1) / 2;
-  const int pair = (int)(blockIdx.x % npair);
-  const int bh = blockIdx.x / npair;
+  // XCD-contiguous order: the hardware deals workgroup i to XCD i % 8, so
+  // XCD x takes the x-th eighth of the work items in order, and the
+  // workgroups of one (b, h), which all stream the same K and V, share
+  // that XCD's L2 instead of each XCD fetching them again
+  int wid = (int)blockIdx.x;
+  {
+    const int nwg = (int)gridDim.x, per = nwg >> 3, extra = nwg & 7, x = wid & 7;
+    wid = x * per + (x < extra ? x : extra) + (wid >> 3);
+  }
+  const int pair = wid % npair;
+  const int bh = wid / npair;
   const int b = bh / a.H, h = bh % a.H;
 
   const bf16* qb = a.q + b * a.sqb + h * a.sqh;
