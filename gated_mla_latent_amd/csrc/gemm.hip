@@ -256,9 +256,12 @@ __device__ __forceinline__ void skinny_wait(int pending) {
   wait_vmcnt<0>();
 }
 
-// Columns n0 .. n0 + 32 NT - 1 of batch `batch`, K slice zi of nz.
+// Columns n0 .. n0 + cw - 1 (cw <= 32 NT, a multiple of 4) of batch `batch`,
+// K slice zi of nz. Weight rows from n0 + cw on are not this workgroup's: the
+// tile re-reads its last row there (a cache hit) and those columns are not
+// stored, so each workgroup streams exactly its own cw rows.
 template <int MT, int NT, int EPI>
-__device__ __forceinline__ void skinny_body(const GemmArgs& g, int n0, int batch, int zi, int nz) {
+__device__ __forceinline__ void skinny_body(const GemmArgs& g, int n0, int cw, int batch, int zi, int nz) {
   using C = SkinnyCfg<MT, NT>;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
@@ -278,15 +281,16 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& g, int n0, int batch
 
   // DMA: instruction q of a 32-row tile moves rows 8q .. 8q + 7; lane l
   // writes physical piece l % 8 of row 8q + l / 8, i.e. logical piece
-  // (l % 8) ^ ((row >> 2) & 7). Rows past the end re-read the last row.
+  // (l % 8) ^ ((row >> 2) & 7). Rows past the workgroup's last re-read it.
   const int lr = lane >> 3;
+  const int n_end = (n0 + cw) < g.N ? (n0 + cw) : g.N;
   auto piece_off = [&](int row) { return ((lane & 7) ^ ((row >> 2) & 7)) * 16; };
   auto issue = [&](int b, int j) {
     const unsigned dst = ring_addr + b * C::BUF_BYTES;
 #pragma unroll
     for (int q = 0; q < 4 * NT; ++q) {
       int row = n0 + 8 * q + lr;
-      row = row < g.N ? row : g.N - 1;
+      row = row < n_end ? row : n_end - 1;
       const unsigned long long base = (unsigned long long)(uintptr_t)(W + (int64_t)j * 64);
       g2lds16_s(base, (unsigned)(row * g.ldw * 2 + piece_off(8 * q + lr)), dst + q * 1024);
     }
@@ -363,6 +367,7 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& g, int n0, int batch
     }
     const int m = 32 * t + (lane & 31);
     const int n = n0 + 32 * u + 8 * wave + 4 * (lane >> 5);
+    if (n >= n0 + cw) continue;  // another workgroup's columns
     if (nz > 1) {  // partial sums [slice][batch][M][N rounded up to 4]
       const int ldp = (g.N + 3) & ~3;
       if (m < g.M && n < g.N)
@@ -376,7 +381,7 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& g, int n0, int batch
 
 template <int MT, int NT, int EPI>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
-  skinny_body<MT, NT, EPI>(g, blockIdx.x * 32 * NT, blockIdx.y, blockIdx.z, gridDim.z);
+  skinny_body<MT, NT, EPI>(g, blockIdx.x * g.cw, g.cw, blockIdx.y, blockIdx.z, gridDim.z);
 }
 
 // Several plain-store GEMMs that share A, M and K in one grid: segment s
@@ -392,26 +397,49 @@ __global__ __launch_bounds__(256) void gemm_skinny_group_kernel(GemmGroup gg) {
   g.ldw = s == 0 ? gg.ldw[0] : s == 1 ? gg.ldw[1] : s == 2 ? gg.ldw[2] : gg.ldw[3];
   g.ldc = s == 0 ? gg.ldc[0] : s == 1 ? gg.ldc[1] : s == 2 ? gg.ldc[2] : gg.ldc[3];
   const int first = s == 0 ? 0 : s == 1 ? gg.first_wg[1] : s == 2 ? gg.first_wg[2] : gg.first_wg[3];
-  skinny_body<MT, NT, EPI_STORE>(g, (x - first) * 32 * NT, 0, 0, 1);
+  skinny_body<MT, NT, EPI_STORE>(g, (x - first) * g.cw, g.cw, 0, 0, 1);
 }
 
 // Sum the split-K partial sums of 4 consecutive columns and apply the
-// epilogue; one thread per (batch, m, 4 columns).
+// epilogue. Eight threads share one (batch, m, 4 columns) quad: thread j adds
+// slices j, j + 8, ..., keeping the loads of four slices in flight at once,
+// and a butterfly over the eight threads completes the sum, so a deep split
+// costs a few memory latencies instead of one per slice.
 template <int EPI>
 __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmArgs g) {
   const int ldp = (g.N + 3) & ~3, q4 = ldp / 4;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)g.batches * g.M * q4) return;
-  const int n = (int)(i % q4) * 4;
-  const int64_t bm = i / q4;
-  const int m = (int)(bm % g.M), batch = (int)(bm / g.M);
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 3;
+  const int j = threadIdx.x & 7;
+  const bool ok = i < (int64_t)g.batches * g.M * q4;
   const int64_t slice = (int64_t)g.batches * g.M * ldp;
-  const float* p = g.part + bm * ldp + n;
-  float4 acc = *(const float4*)p;
-  for (int z = 1; z < g.ksplit; ++z) {
-    const float4 v = *(const float4*)(p + z * slice);
-    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  const int64_t bm = i / q4;
+  const int n = (int)(i % q4) * 4;
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (ok) {
+    const float* p = g.part + bm * ldp + n;
+    for (int z0 = j; z0 < g.ksplit; z0 += 32) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int z = z0 + 8 * u;
+        v[u] = z < g.ksplit ? *(const float4*)(p + z * slice) : float4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        acc.x += v[u].x; acc.y += v[u].y; acc.z += v[u].z; acc.w += v[u].w;
+      }
+    }
   }
+  // every thread of the wave takes part in the exchange
+#pragma unroll
+  for (int off = 1; off < 8; off <<= 1) {
+    acc.x += __shfl_xor(acc.x, off);
+    acc.y += __shfl_xor(acc.y, off);
+    acc.z += __shfl_xor(acc.z, off);
+    acc.w += __shfl_xor(acc.w, off);
+  }
+  if (!ok || j != 0) return;
+  const int m = (int)(bm % g.M), batch = (int)(bm / g.M);
   bf16* Cp = g.C + batch * g.sC;
   const bf16* Op = (EPI == EPI_GATE) ? g.O + batch * g.sO : nullptr;
   store4<EPI>(g, Cp, Op, m, n, acc.x, acc.y, acc.z, acc.w);
@@ -429,10 +457,11 @@ static hipError_t launch_skinny(const GemmArgs& g, hipStream_t st) {
   }
   const int z = g.ksplit > 1 ? g.ksplit : 1;
   if (z > 1 && !g.part) return hipErrorInvalidValue;
-  hipError_t e = launch(kern, dim3((g.N + 32 * NT - 1) / (32 * NT), g.batches, z), dim3(256), C::LDS_BYTES, st, g);
+  if (g.cw <= 0 || g.cw > 32 * NT || g.cw % 4 != 0) return hipErrorInvalidValue;
+  hipError_t e = launch(kern, dim3((g.N + g.cw - 1) / g.cw, g.batches, z), dim3(256), C::LDS_BYTES, st, g);
   if (e != hipSuccess || z == 1) return e;
-  const int64_t n4 = (int64_t)g.batches * g.M * (((g.N + 3) & ~3) / 4);
-  return launch(gemm_splitk_reduce_kernel<EPI>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, g);
+  const int64_t n4 = (int64_t)g.batches * g.M * (((g.N + 3) & ~3) / 4);  // output quads, 8 threads each
+  return launch(gemm_splitk_reduce_kernel<EPI>, dim3((unsigned)((8 * n4 + 255) / 256)), dim3(256), 0, st, g);
 }
 
 
@@ -455,16 +484,53 @@ static hipError_t launch_tile(const GemmArgs& g, hipStream_t st) {
 
 static bool skinny_path(int M, int N, int npad) { return M <= 64 && !(npad > N); }
 
+// Columns per skinny workgroup. With up to 32 rows the kernel streams
+// weight rows at one workgroup per compute unit, so its time follows the
+// rows the busiest unit streams: (columns per workgroup) x (rounds of the
+// grid). Pick the width (a multiple of 4 up to 64; above 32 the 64-column
+// form) that minimises it, the widest among equals (fewer workgroups
+// re-read the activations): e.g. 7168 columns run as 256 workgroups of 28
+// rather than 224 of 32 (measured 29.5 -> 25.4 us at K = 8192). With 33..64
+// rows (two 32-row blocks, fewer ring buffers per wave) narrower
+// workgroups measured slower: there the widths stay 32, or 64 while that
+// still gives a workgroup per compute unit.
+static int skinny_cols(const int* N, int nseg, int batches, int M) {
+  if (M > 32) {
+    long long wide = 0;
+    for (int s = 0; s < nseg; ++s) wide += (long long)((N[s] + 63) / 64) * batches;
+    return kSkinnyNT2 && wide >= 256 ? 64 : 32;
+  }
+  int best = 32;
+  long long best_cost = -1;
+  for (int cw = 64; cw >= 4; cw -= 4) {
+    if (cw > 32 && !kSkinnyNT2) continue;
+    long long wgs = 0;
+    for (int s = 0; s < nseg; ++s) wgs += (long long)((N[s] + cw - 1) / cw) * batches;
+    const long long cost = (long long)cw * ((wgs + 255) / 256);
+    if (best_cost < 0 || cost < best_cost) {
+      best = cw;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 template <int EPI>
 static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
   if (skinny_path(g.M, g.N, EPI == EPI_STORE ? g.npad : 0)) {
     // the DMA offsets are 32-bit: every row start must be below 4 GiB
     if ((long long)g.N * g.ldw * 2 >= (1LL << 32) || (long long)g.M * g.lda * 2 >= (1LL << 32))
       return hipErrorInvalidValue;
-    // 64-column workgroups when that still gives one per compute unit
-    const bool nt2 = kSkinnyNT2 && g.ksplit <= 1 && (long long)((g.N + 63) / 64) * g.batches >= 256;
-    if (g.M <= 32) return nt2 ? launch_skinny<1, 2, EPI>(g, st) : launch_skinny<1, 1, EPI>(g, st);
-    return nt2 ? launch_skinny<2, 2, EPI>(g, st) : launch_skinny<2, 1, EPI>(g, st);
+    GemmArgs h = g;
+    if (g.ksplit > 1) {
+      h.cw = 32;
+    } else {
+      const int n1[1] = {g.N};
+      h.cw = skinny_cols(n1, 1, g.batches, g.M);
+    }
+    const bool nt2 = h.cw > 32;
+    if (g.M <= 32) return nt2 ? launch_skinny<1, 2, EPI>(h, st) : launch_skinny<1, 1, EPI>(h, st);
+    return nt2 ? launch_skinny<2, 2, EPI>(h, st) : launch_skinny<2, 1, EPI>(h, st);
   }
   const long long big_tiles = (long long)((g.N + 255) / 256) * ((g.M + 255) / 256) * g.batches;
   if (big_tiles >= 256) return launch_tile<256, 256, EPI>(g, st);
@@ -509,11 +575,10 @@ hipError_t launch_gemm_group_bf16(GemmGroup gg, hipStream_t st) {
   const GemmArgs& b = gg.base;
   if (gg.count < 1 || gg.count > 4 || b.M <= 0 || b.M > 64 || b.K % 64 != 0) return hipErrorInvalidValue;
   if ((long long)b.M * b.lda * 2 >= (1LL << 32)) return hipErrorInvalidValue;
-  // 64-column workgroups when that still gives one per compute unit
-  long long wide = 0;
-  for (int s = 0; s < gg.count; ++s) wide += (gg.N[s] + 63) / 64;
-  const int cols = kSkinnyNT2 && wide >= 256 ? 64 : 32;
   int first = 0;
+  for (int s = 0; s < gg.count; ++s)
+    if (gg.N[s] <= 0) return hipErrorInvalidValue;
+  const int cols = skinny_cols(gg.N, gg.count, 1, b.M);
   for (int s = 0; s < 4; ++s) {
     if (s < gg.count) {
       if (gg.N[s] <= 0 || gg.N[s] % 4 != 0 || (long long)gg.N[s] * gg.ldw[s] * 2 >= (1LL << 32))
@@ -529,8 +594,9 @@ hipError_t launch_gemm_group_bf16(GemmGroup gg, hipStream_t st) {
   gg.base.ksplit = 1;
   gg.base.epi = EPI_STORE;
   gg.base.npad = 0;
-  if (b.M <= 32) return cols == 64 ? launch_group<1, 2>(gg, first, st) : launch_group<1, 1>(gg, first, st);
-  return cols == 64 ? launch_group<2, 2>(gg, first, st) : launch_group<2, 1>(gg, first, st);
+  gg.base.cw = cols;
+  if (b.M <= 32) return cols > 32 ? launch_group<1, 2>(gg, first, st) : launch_group<1, 1>(gg, first, st);
+  return cols > 32 ? launch_group<2, 2>(gg, first, st) : launch_group<2, 1>(gg, first, st);
 }
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t st) {

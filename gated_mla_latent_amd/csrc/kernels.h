@@ -106,6 +106,7 @@ struct GemmArgs {
   int npad;                 // EPI_STORE: columns N .. npad - 1 of C are written as zeros (<= N: none)
   float* part;              // split-K partial sums (gemm_ksplit(...) > 1): gemm_part_bytes(...) bytes
   int ksplit;               // K slices of the skinny kernel (<= 1: none)
+  int cw;                   // skinny kernel: output columns per workgroup (set by the launcher)
 };
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t st);
 // Split-K plan of the skinny kernel (M <= 64) for an under-filled grid, and

@@ -55,7 +55,11 @@ def test_prefill_fp32_tiny_config():
                                            # 64-column skinny workgroups (gate and value up-projection) and
                                            # split-K W_o, at 33..64 and at <= 32 rows
                                            (64, 512, 128, 512, 128), (20, 512, 128, 128, 128),
-                                           (37, 256, 136, 64, 128)])
+                                           (37, 256, 136, 64, 128),
+                                           # workgroups narrower than 32 columns: W_o over 7168 columns
+                                           # as 256 x 28, and 2240 columns as 12-wide ones with an
+                                           # 8-column tail (gate and value up-projection 8 wide)
+                                           (32, 7168, 8, 128, 64), (24, 2240, 16, 128, 128)])
 def test_gate_out_with_value_up_projection(T, D, H, d_c, d_v):
     say(f"[gate_out decode-side] T={T} D={D} H={H} d_c={d_c} d_v={d_v}")
     g = torch.Generator().manual_seed(5)
