@@ -520,6 +520,11 @@ void decode_attn_kernel(DecodeArgs a) {
 // merge of split softmax sums. Workgroup = (sequence, group of 16 heads,
 // quarter of the features); thread = one 16-byte lane record of one store
 // index k of the pieces' wave-ordered layout (see the attention epilogue).
+// The loads of NB pieces are issued together, so the merge costs one memory
+// latency per NB pieces; the slot of every piece follows from the sequence's
+// first and last slice (three divisions per thread, plus one per piece only
+// when there are more slices than tokens and a slice can be empty).
+template <int NB>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   constexpr int D_C = 512;
   const int H16 = (a.H + 15) >> 4;
@@ -530,7 +535,11 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const int h = hg * 16 + (lane & 15);
   const int G4 = lane >> 4;
   if (h >= a.H) return;
+  // every length and offset this thread needs, loaded together
   const int Lb = a.seq_len[b];
+  const int Llast = a.seq_len[a.B - 1];
+  const long long Plast = a.prefix[a.B - 1];
+  const long long P = a.prefix[b];
   bf16* op = a.o_lat + ((int64_t)b * a.H + h) * D_C + 32 * k + 4 * G4;  // features +0..3 and +16..19
   if (Lb <= 0) {
     *(u32x2*)op = u32x2{0u, 0u};
@@ -538,30 +547,28 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     if (k == 0 && G4 == 0 && a.lse) a.lse[(int64_t)b * a.H + h] = -INFINITY;
     return;
   }
-  const long long N = a.prefix[a.B - 1] + (a.seq_len[a.B - 1] > 0 ? a.seq_len[a.B - 1] : 0);
+  const long long N = Plast + (Llast > 0 ? Llast : 0);
   const int G = a.G;
-  const long long P = a.prefix[b];
   // slice holding token p: the largest g with floor(g N / G) <= p
   const long long g_lo = ((P + 1) * G - 1) / N;
   const long long g_hi = ((P + Lb) * G - 1) / N;
   if (g_lo == g_hi) return;  // whole sequence inside one slice: already final
-  // online merge over the pieces (slices with an empty range hold none); the
-  // loads of eight pieces are issued together, so the merge costs one memory
-  // latency per eight pieces rather than one per piece
+  // a piece that starts its slice sits in slot 2g, one that starts inside it
+  // in 2g + 1; only the first piece can start inside its slice
+  const bool lo_inside = g_lo * N / G != P;
+  const bool may_empty = N < G;  // otherwise every slice holds at least one token
   float M = -INFINITY, den = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  constexpr int NB = 8;
   for (long long g0 = g_lo; g0 <= g_hi; g0 += NB) {
     float l[NB];
     u32x4 raw[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const long long g = g0 + i;
-      const long long start_g = g * N / G;
       l[i] = -INFINITY;
       raw[i] = u32x4{0u, 0u, 0u, 0u};
-      if (g <= g_hi && start_g != (g + 1) * N / G) {
-        const long long slot = (P <= start_g) ? 2 * g : 2 * g + 1;
+      if (g <= g_hi && (!may_empty || g * N / G != (g + 1) * N / G)) {
+        const long long slot = (g == g_lo && lo_inside) ? 2 * g + 1 : 2 * g;
         l[i] = a.part_lse[slot * a.H + h];
         raw[i] = *(const u32x4*)(a.part_o + ((slot * H16 + hg) * 16 + k) * (int64_t)512 + lane * 8);
       }
@@ -618,7 +625,12 @@ hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st) {
   if (a.d_c != 512) return hipErrorInvalidValue;
   const long long blocks = (long long)a.B * ((a.H + 15) / 16) * 4;
   if (blocks > 2147483647LL) return hipErrorInvalidValue;
-  return launch(decode_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  // pieces per sequence are about G / B + 1: issue the loads of that many
+  // together (at most 16, which bounds the registers)
+  const long long per_seq = a.B > 0 ? (long long)a.G / a.B + 1 : 1;
+  if (per_seq > 8) return launch(decode_combine_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  if (per_seq > 4) return launch(decode_combine_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  return launch(decode_combine_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, st, a);
 }
 
 // Only the d_c = 512 latent (the width every supported workload uses) is

@@ -65,7 +65,7 @@ def test_decode_narrow_latent_widths_are_rejected():
     assert e.value.status == 2
 
 
-@pytest.mark.parametrize("num_splits", [1, 2, 7, 64, 0])
+@pytest.mark.parametrize("num_splits", [1, 2, 7, 36, 64, 0])
 def test_decode_split_invariance(num_splits):
     say(f"[decode splits] num_splits={num_splits}")
     inp = W.make_decode(6, 128, 512, 64, 1, 700, seed=3, name="splits")
