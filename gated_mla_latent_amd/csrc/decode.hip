@@ -96,7 +96,7 @@ struct DecodeCfg {
   static_assert(D_R == 0 || D_R == 64, "RoPE rows are 8 chunks of 16 bytes");
   static_assert(ROPE_ROWS * 8 <= 64, "RoPE rows of a wave fit one instruction");
   static_assert(LDS_BYTES <= 163840, "LDS budget");
-  static_assert(NW * 8 + 16 <= LDS_BYTES, "scan scratch fits in the ring");
+  static_assert(NW * 8 + 32 <= LDS_BYTES, "scan scratch fits in the ring");
   static_assert(PD >= 1 && PD <= 3, "ring of 3 to 5 slots");
   static_assert((PD - 1) * ROUNDS < 64, "vmcnt range");
 };
@@ -169,15 +169,18 @@ void decode_attn_kernel(DecodeArgs a) {
   // wave and one pass over the NW wave totals give every thread its
   // exclusive prefix with a single barrier
   LDS_AS long long* s_wsum = (LDS_AS long long*)smem;  // [NW] wave totals
-  LDS_AS long long* s_first = s_wsum + C::NW;          // [2] first sequence of the slice, its offset
+  LDS_AS long long* s_first = s_wsum + C::NW;          // [4] first sequence of the slice: index, offset, length, cache row
   const int B = a.B;
   const int cb = (B + NT - 1) / NT;
   long long mysum = 0;
-  int L0 = 0;  // the length of this thread's first sequence (the only one when B <= NT)
+  int L0 = 0;         // the length of this thread's first sequence (the only one when B <= NT)
+  long long S0 = 0;   // ... and its first cache row, loaded alongside so that the
+                      // slice's first DMA needs no further round trip
   for (int i = 0; i < cb; ++i) {
     int bb = tid * cb + i;
     if (bb < B) {
       int L = a.seq_len[bb];
+      if (i == 0) S0 = a.seq_start[bb];
       L = L > 0 ? L : 0;
       if (i == 0) L0 = L;
       mysum += L;
@@ -210,13 +213,20 @@ void decode_attn_kernel(DecodeArgs a) {
       int L = L0;
       if (i > 0) { L = a.seq_len[bb]; L = L > 0 ? L : 0; }
       if (blockIdx.x == 0) a.prefix[bb] = p;
-      if (L > 0 && p <= start_g && start_g < p + L) { s_first[0] = bb; s_first[1] = p; }
+      if (L > 0 && p <= start_g && start_g < p + L) {
+        s_first[0] = bb;
+        s_first[1] = p;
+        s_first[2] = L;
+        s_first[3] = i == 0 ? S0 : a.seq_start[bb];
+      }
       p += L;
     }
   }
   __syncthreads();
   int b = (int)s_first[0];
   long long P = s_first[1];
+  const int L_first = (int)s_first[2];
+  const long long S_first = s_first[3];
   __syncthreads();  // the scan scratch becomes ring space
   if (b < 0 || start_g >= end_g) return;
 
@@ -250,15 +260,16 @@ void decode_attn_kernel(DecodeArgs a) {
 
   const unsigned long long cache_addr = (unsigned long long)(uintptr_t)a.cache;
 
-  for (; b < B && P < end_g; ++b) {
-    const int Lb = a.seq_len[b];
+  for (bool first_seg = true; b < B && P < end_g; ++b, first_seg = false) {
+    const int Lb = first_seg ? L_first : a.seq_len[b];
     if (Lb <= 0) continue;
     const long long seg_lo = P > start_g ? P : start_g;
     const long long seg_hi = (P + Lb) < end_g ? (P + Lb) : end_g;
     const bool complete = (P >= start_g) && (P + Lb <= end_g);
     const int t0 = (int)(seg_lo - P);             // first token of the segment in sequence b
     const int n = (int)(seg_hi - seg_lo);         // tokens in the segment
-    const unsigned long long seg_addr = cache_addr + (unsigned long long)(a.seq_start[b] + t0) * C::RWB;
+    const long long row0 = first_seg ? S_first : a.seq_start[b];
+    const unsigned long long seg_addr = cache_addr + (unsigned long long)(row0 + t0) * C::RWB;
     P += Lb;
 
     const int nslots = (n + 31) >> 5;             // 32-token slots of the segment
