@@ -45,7 +45,7 @@ namespace {
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRedo = 32.0f;  // log2 headroom before a segment is redone
-constexpr int kPF = 8;          // LDS operand fragments in flight ahead of the MFMA
+constexpr int kPF = 4;          // LDS operand fragments in flight ahead of the MFMA
 constexpr bool kSpreadDMA = true;  // interleave the next slot's DMA with the score MFMAs
 constexpr int kRing = 4;           // LDS ring slots (slots in flight = kRing - 2)
 
