@@ -165,13 +165,20 @@ void decode_attn_kernel(DecodeArgs a) {
   const int g = item / chunks;
   const int head_base = (item % chunks) * (16 * HG);  // first head of this chunk
 
-  // ---- prefix sums of the sequence lengths (cooperative, any B); scratch in the ring ----
-  // thread i sums sequences i*cb .. i*cb + cb - 1; a shuffle scan inside each
-  // wave and one pass over the NW wave totals give every thread its
-  // exclusive prefix with a single barrier
+  // ---- slicing by cost (cooperative, any B); scratch in the ring ----
+  // A nonempty sequence costs its length plus a.seg_cost tokens (its segment
+  // start: query loads, the first DMA round trip, the softmax exchanges and
+  // the output stores of a piece), and the G slices are equal ranges of
+  // the total cost, so a slice that holds the start of a sequence gets
+  // correspondingly fewer tokens. Sequence b occupies the cost range
+  // [Q_b, Q_b + c + L_b): c units of start cost, then one per token.
+  // Thread i sums the costs of sequences i*cb .. i*cb + cb - 1; a shuffle
+  // scan inside each wave and one pass over the NW wave totals give every
+  // thread its exclusive prefix with a single barrier.
   LDS_AS long long* s_wsum = (LDS_AS long long*)smem;  // [NW] wave totals
-  LDS_AS long long* s_first = s_wsum + C::NW;          // [4] first sequence of the slice: index, offset, length, cache row
+  LDS_AS long long* s_first = s_wsum + C::NW;          // [4] first sequence of the slice: index, cost offset, length, cache row
   const int B = a.B;
+  const long long c = a.seg_cost;
   const int cb = (B + NT - 1) / NT;
   long long mysum = 0;
   int L0 = 0;         // the length of this thread's first sequence (the only one when B <= NT)
@@ -184,7 +191,7 @@ void decode_attn_kernel(DecodeArgs a) {
       if (i == 0) S0 = a.seq_start[bb];
       L = L > 0 ? L : 0;
       if (i == 0) L0 = L;
-      mysum += L;
+      mysum += L > 0 ? L + c : 0;
     }
   }
   long long incl = mysum;
@@ -196,16 +203,17 @@ void decode_attn_kernel(DecodeArgs a) {
   if (lane == 63) s_wsum[wave] = incl;
   if (tid == 0) { s_first[0] = -1; s_first[1] = 0; }
   __syncthreads();
-  long long N = 0, before = 0;
+  long long Ctot = 0, before = 0;
 #pragma unroll
   for (int w = 0; w < C::NW; ++w) {
     const long long t = s_wsum[w];
-    N += t;
+    Ctot += t;
     before += w < wave ? t : 0;
   }
   const long long excl = before + incl - mysum;
-  const long long start_g = (long long)g * N / G;
-  const long long end_g = (long long)(g + 1) * N / G;
+  // this slice's cost range
+  const long long lo_g = (long long)g * Ctot / G;
+  const long long hi_g = (long long)(g + 1) * Ctot / G;
   {
     long long p = excl;
     for (int i = 0; i < cb; ++i) {
@@ -214,22 +222,22 @@ void decode_attn_kernel(DecodeArgs a) {
       int L = L0;
       if (i > 0) { L = a.seq_len[bb]; L = L > 0 ? L : 0; }
       if (blockIdx.x == 0) a.prefix[bb] = p;
-      if (L > 0 && p <= start_g && start_g < p + L) {
+      if (L > 0 && p <= lo_g && lo_g < p + c + L) {
         s_first[0] = bb;
         s_first[1] = p;
         s_first[2] = L;
         s_first[3] = i == 0 ? S0 : a.seq_start[bb];
       }
-      p += L;
+      p += L > 0 ? L + c : 0;
     }
   }
   __syncthreads();
   int b = (int)s_first[0];
-  long long P = s_first[1];
+  long long Q = s_first[1];  // cost offset of sequence b
   const int L_first = (int)s_first[2];
   const long long S_first = s_first[3];
   __syncthreads();  // the scan scratch becomes ring space
-  if (b < 0 || start_g >= end_g) return;
+  if (b < 0 || lo_g >= hi_g) return;
 
   // ---- per-lane constants ----
   const float scale2 = a.scale_log2;
@@ -261,17 +269,22 @@ void decode_attn_kernel(DecodeArgs a) {
 
   const unsigned long long cache_addr = (unsigned long long)(uintptr_t)a.cache;
 
-  for (bool first_seg = true; b < B && P < end_g; ++b, first_seg = false) {
+  for (bool first_seg = true; b < B && Q < hi_g; ++b, first_seg = false) {
     const int Lb = first_seg ? L_first : a.seq_len[b];
     if (Lb <= 0) continue;
-    const long long seg_lo = P > start_g ? P : start_g;
-    const long long seg_hi = (P + Lb) < end_g ? (P + Lb) : end_g;
-    const bool complete = (P >= start_g) && (P + Lb <= end_g);
-    const int t0 = (int)(seg_lo - P);             // first token of the segment in sequence b
+    const long long tok_c = Q + c;                // cost position of the sequence's first token
+    const long long seg_lo = tok_c > lo_g ? tok_c : lo_g;
+    const long long seg_hi = (tok_c + Lb) < hi_g ? (tok_c + Lb) : hi_g;
+    const bool complete = (tok_c >= lo_g) && (tok_c + Lb <= hi_g);
+    // a partial piece that follows another piece of the slice goes to slot
+    // 2g + 1, the one that opens the slice to slot 2g
+    const bool inside = lo_g < Q;
+    Q += Lb + c;
+    if (seg_lo >= seg_hi) continue;               // the slice ends within this sequence's start cost
+    const int t0 = (int)(seg_lo - tok_c);         // first token of the segment in sequence b
     const int n = (int)(seg_hi - seg_lo);         // tokens in the segment
     const long long row0 = first_seg ? S_first : a.seq_start[b];
     const unsigned long long seg_addr = cache_addr + (unsigned long long)(row0 + t0) * C::RWB;
-    P += Lb;
 
     const int nslots = (n + 31) >> 5;             // 32-token slots of the segment
 
@@ -491,7 +504,7 @@ void decode_attn_kernel(DecodeArgs a) {
     lsum = head_sum(lsum);
     if (G4 == 0) s_ls[th * 16 * HG + xi] = lsum;
     lds_barrier();
-    const long long slot = (seg_lo > start_g) ? (2LL * g + 1) : (2LL * g);
+    const long long slot = inside ? (2LL * g + 1) : (2LL * g);
     if (th == 0 && h_ok && G4 == 0) {
       const float lse_nat = m * kLn2 + __logf(s_ls[xi] + s_ls[16 * HG + xi]);
       if (!complete) a.part_lse[slot * a.H + h] = lse_nat;
@@ -551,8 +564,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   // every length and offset this thread needs, loaded together
   const int Lb = a.seq_len[b];
   const int Llast = a.seq_len[a.B - 1];
-  const long long Plast = a.prefix[a.B - 1];
-  const long long P = a.prefix[b];
+  const long long Qlast = a.prefix[a.B - 1];
+  const long long Q = a.prefix[b];  // cost offset of sequence b (the attention kernel's slicing)
   bf16* op = a.o_lat + ((int64_t)b * a.H + h) * D_C + 32 * k + 4 * G4;  // features +0..3 and +16..19
   if (Lb <= 0) {
     *(u32x2*)op = u32x2{0u, 0u};
@@ -560,16 +573,18 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     if (k == 0 && G4 == 0 && a.lse) a.lse[(int64_t)b * a.H + h] = -INFINITY;
     return;
   }
-  const long long N = Plast + (Llast > 0 ? Llast : 0);
+  const long long c = a.seg_cost;
+  const long long N = Qlast + (Llast > 0 ? Llast + c : 0);  // total cost
   const int G = a.G;
-  // slice holding token p: the largest g with floor(g N / G) <= p
-  const long long g_lo = ((P + 1) * G - 1) / N;
-  const long long g_hi = ((P + Lb) * G - 1) / N;
+  // slice whose cost range holds position x: the largest g with floor(g N / G) <= x;
+  // the sequence's tokens hold the cost positions Q + c .. Q + c + Lb - 1
+  const long long g_lo = ((Q + c + 1) * G - 1) / N;
+  const long long g_hi = ((Q + c + Lb) * G - 1) / N;
   if (g_lo == g_hi) return;  // whole sequence inside one slice: already final
-  // a piece that starts its slice sits in slot 2g, one that starts inside it
-  // in 2g + 1; only the first piece can start inside its slice
-  const bool lo_inside = g_lo * N / G != P;
-  const bool may_empty = N < G;  // otherwise every slice holds at least one token
+  // a piece that opens its slice sits in slot 2g, one that follows another
+  // piece of the slice in 2g + 1; only the first piece can follow another
+  const bool lo_inside = g_lo * N / G < Q;
+  const bool may_empty = N < G;  // otherwise every slice holds at least one cost unit
   float M = -INFINITY, den = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (long long g0 = g_lo; g0 <= g_hi; g0 += NB) {

@@ -42,8 +42,9 @@ struct DecodeArgs {
   float* lse;               // [B, H] or null
   bf16* part_o;             // [2G, H/16 head groups, 16 x d_c] partial outputs of cut sequences (wave order)
   float* part_lse;          // [2G, H]
-  long long* prefix;        // [B] exclusive prefix sums of seq_len
+  long long* prefix;        // [B] cost offsets: exclusive prefix sums of seq_len[b] + seg_cost (nonempty b)
   int B, H, d_c, d_r, G;
+  int seg_cost;             // slicing cost of a sequence start, in tokens (0: slices of equal tokens)
   float scale_log2;         // sm_scale * log2(e)
   float rope_base;          // 0 = no rotation of the query's RoPE part
 };
