@@ -111,10 +111,12 @@ gmla_status_t gmla_prefill(const void* x, const void* W_c, const void* W_dq, con
  * part c_j only. L_b >= 1 is required; a sequence with L_b <= 0 yields
  * o_lat = 0 and lse = -inf. The seq_* arrays are read on the device and
  * trusted (rows must lie inside `cache`).
- * num_splits: number of equal slices the concatenated token range of all
- * sequences is cut into; each slice runs as ceil(H/64) workgroups of up to
- * 64 heads (one if H <= 32). 0 = automatic: compute units / workgroups per
- * slice, rounded down to a multiple of 8.
+ * num_splits (BF16): number of slices the concatenated token range of all
+ * sequences is cut into, slices of equal cost where a token counts 1 and
+ * the start of a nonempty sequence 384; each slice runs as ceil(H/64)
+ * workgroups of up to 64 heads (one if H <= 32). 0 = automatic: compute
+ * units / workgroups per slice, rounded down to a multiple of 8. F32 runs
+ * one workgroup per sequence and head and ignores it.
  * The result does not depend on it beyond fp32 rounding.
  * BF16 needs d_c == 512 and d_r in {0, 64}; F32 needs
  * d_c + d_r <= 1024 and d_c <= 512.
