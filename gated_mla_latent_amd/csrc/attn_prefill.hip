@@ -360,11 +360,9 @@ template <int D, int DR>
 static hipError_t launch_d(const AttnArgs& a, hipStream_t st) {
   using C = FaCfg<D, DR>;
   auto kern = prefill_attn_kernel<D, DR>;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+  {
+    hipError_t e = lds_opt_in((const void*)kern, C::LDS);
     if (e != hipSuccess) return e;
-    attr = true;
   }
   // the loads use 32-bit offsets from a per-tile scalar base
   if ((long long)C::BK * a.skt * 2 >= (1LL << 31) || (long long)D * a.svj * 2 >= (1LL << 31) ||

@@ -627,11 +627,9 @@ template <int D_R, int HG, int R>
 static hipError_t launch_variant(const DecodeArgs& a, hipStream_t st) {
   using C = DecodeCfg<D_R, HG, R>;
   auto kern = decode_attn_kernel<D_R, HG, R>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+  {
+    hipError_t e = lds_opt_in((const void*)kern, C::LDS_BYTES);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int chunks = (a.H + 16 * HG - 1) / (16 * HG);
   return launch(kern, dim3(a.G * chunks), dim3(C::NW * 64), C::LDS_BYTES, st, a);

@@ -449,11 +449,9 @@ template <int MT, int NT, int EPI>
 static hipError_t launch_skinny(const GemmArgs& g, hipStream_t st) {
   using C = SkinnyCfg<MT, NT>;
   auto kern = gemm_skinny_kernel<MT, NT, EPI>;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+  {
+    hipError_t e = lds_opt_in((const void*)kern, C::LDS_BYTES);
     if (e != hipSuccess) return e;
-    attr = true;
   }
   const int z = g.ksplit > 1 ? g.ksplit : 1;
   if (z > 1 && !g.part) return hipErrorInvalidValue;
@@ -471,11 +469,9 @@ static hipError_t launch_tile(const GemmArgs& g, hipStream_t st) {
   constexpr int RING = 2 * (BN + BM) * 64 * 2, EPIL = BM * ((BN / 2) * 4 + 16);
   constexpr int LDS = RING > EPIL ? RING : EPIL;
   auto kern = gemm_tile_kernel<BN, BM, EPI>;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+  {
+    hipError_t e = lds_opt_in((const void*)kern, LDS);
     if (e != hipSuccess) return e;
-    attr = true;
   }
   const int ncols = (EPI == EPI_STORE && g.npad > g.N) ? g.npad : g.N;
   const int tiles = ((ncols + BN - 1) / BN) * ((g.M + BM - 1) / BM);
@@ -562,11 +558,9 @@ template <int MT, int NT>
 static hipError_t launch_group(const GemmGroup& gg, int wgs, hipStream_t st) {
   using C = SkinnyCfg<MT, NT>;
   auto kern = gemm_skinny_group_kernel<MT, NT>;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+  {
+    hipError_t e = lds_opt_in((const void*)kern, C::LDS_BYTES);
     if (e != hipSuccess) return e;
-    attr = true;
   }
   return launch(kern, dim3(wgs), dim3(256), C::LDS_BYTES, st, gg);
 }

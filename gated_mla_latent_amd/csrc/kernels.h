@@ -4,6 +4,10 @@
 #include <hip/hip_ext.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <set>
+#include <utility>
+
 namespace gmla {
 
 // Every kernel goes out through launch(). While the C-ABI layer traces a
@@ -17,6 +21,21 @@ struct LaunchEvents {
   int launched;
 };
 extern thread_local LaunchEvents* g_launch_events;
+
+// Let kernel `fn` use `bytes` of dynamic LDS on the current device. The
+// attribute belongs to a device, so it is set once per (kernel, device).
+inline hipError_t lds_opt_in(const void* fn, int bytes) {
+  static std::mutex mu;
+  static std::set<std::pair<const void*, int>> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(mu);
+  if (done.count({fn, dev})) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.insert({fn, dev});
+  return e;
+}
 
 template <typename K, typename... Args>
 inline hipError_t launch(K kern, dim3 grid, dim3 block, unsigned shmem, hipStream_t st, Args... args) {
