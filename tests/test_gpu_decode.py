@@ -77,6 +77,16 @@ def test_decode_split_invariance(num_splits):
     assert float((lse - l1).abs().max()) <= 1e-4
 
 
+def test_decode_more_slices_than_cost_units():
+    """Two short sequences cut into 1000 slices: the slices' cost ranges hold
+    fewer units than there are slices, so many slices are empty and many
+    hold only the start cost of a sequence (no tokens)."""
+    say("[decode 1000 slices]")
+    inp = W.make_decode(2, 64, 512, 64, 0, lengths=[3, 5], seed=6, name="slices")
+    o, lse = _run(inp, 1000)
+    _check(inp, o, lse)
+
+
 @pytest.mark.parametrize("B,H", [(130, 64), (1100, 64), (600, 16)])
 def test_decode_many_sequences(B, H):
     """More sequences than one wave (or one workgroup) of the prefix scan
