@@ -39,8 +39,6 @@ reason in the design notes of the repository):
 """
 from __future__ import annotations
 
-import math
-
 import numpy as np
 
 __all__ = [
@@ -106,8 +104,10 @@ def reconstruct_kv(c, W_uk, W_uv):
     Returns k: [..., H, d_k], v: [..., H, d_v].
     """
     c = _f64(c)
-    k = np.einsum("...c,hdc->...hd", c, _f64(W_uk))
-    v = np.einsum("...c,hdc->...hd", c, _f64(W_uv))
+    # optimize=True lets numpy hand the contraction over c to the BLAS matrix
+    # product; the sums are the same
+    k = np.einsum("...c,hdc->...hd", c, _f64(W_uk), optimize=True)
+    v = np.einsum("...c,hdc->...hd", c, _f64(W_uv), optimize=True)
     return k, v
 
 
@@ -128,19 +128,29 @@ def attend_rows(q_rows, k, v, t_rows, scale: float):
     k = _f64(k)
     v = _f64(v)
     R, H, _ = q_rows.shape
+    t_rows = np.asarray([int(t) for t in t_rows], dtype=np.int64)
+    S = int(t_rows.max()) + 1 if R else 0  # keys any requested row can see
+    kh = np.ascontiguousarray(k[:S].transpose(1, 2, 0))  # [H, d_k, S]
+    vh = np.ascontiguousarray(v[:S].transpose(1, 0, 2))  # [H, S, d_v]
     o = np.empty((R, H, v.shape[-1]))
     lse = np.empty((R, H))
-    for r, t in enumerate(t_rows):
-        t = int(t)
-        ks = k[: t + 1]  # [S, H, d_k], S = t+1 keys with s <= t
-        vs = v[: t + 1]
-        z = np.einsum("hd,shd->hs", q_rows[r], ks) * scale  # [H, S]
-        m = z.max(axis=1, keepdims=True)
+    # Rows are independent; they are taken a few at a time so that each
+    # head's scores of those rows are one matrix product (a library step).
+    # Keys past a row's position get z = -inf, i.e. weight exp(-inf) = 0:
+    # exactly the sums over s <= t.
+    step = max(1, (1 << 24) // max(1, H * S))
+    for r0 in range(0, R, step):
+        rs = slice(r0, min(R, r0 + step))
+        qh = q_rows[rs].transpose(1, 0, 2)  # [H, r, d_k]
+        z = (qh @ kh) * scale  # [H, r, S]: z[h, i, s] = scale * q_(t_i)^(h) . k_s^(h)
+        visible = np.arange(S)[None, :] <= t_rows[rs][:, None]  # [r, S]: s <= t
+        z = np.where(visible[None], z, -np.inf)
+        m = z.max(axis=2, keepdims=True)
         e = np.exp(z - m)
-        den = e.sum(axis=1, keepdims=True)
+        den = e.sum(axis=2, keepdims=True)
         a = e / den
-        o[r] = np.einsum("hs,shd->hd", a, vs)
-        lse[r] = (m + np.log(den))[:, 0]
+        o[rs] = (a @ vh).transpose(1, 0, 2)  # sum_s a_s v_s^(h)
+        lse[rs] = (m + np.log(den))[:, :, 0].T
     return o, lse
 
 
@@ -196,7 +206,7 @@ def decode_reference(q_abs, cache, seq_start, seq_len, d_c: int, d_r: int,
       Sequence b owns rows seq_start[b] .. seq_start[b] + seq_len[b] - 1.
     Because q~ is given, the per-head up-projection of the key is the identity
     on the latent: every head's key is k_j^h = [c_j ; k^R_j] and its value is
-    v_j^h = c_j, built explicitly per head. The query's RoPE part is rotated
+    v_j^h = c_j (the shared row itself). The query's RoPE part is rotated
     at position seq_len[b] - 1 (the current token); rope_base == 0 or
     d_r == 0 means NoPE.
 
@@ -220,13 +230,19 @@ def decode_reference(q_abs, cache, seq_start, seq_len, d_c: int, d_r: int,
         q_r = q[:, d_c:]
         if d_r > 0 and rope_base != 0.0:
             q_r = rope_rotate(q_r, L - 1, rope_base)
-        qh = np.concatenate([q_c, q_r], axis=1)[None]  # [1, H, d_c+d_r]
-        # explicit per-head keys and values (identity up-projection per head)
-        k = np.broadcast_to(rows[:, None, :], (L, H, d_c + d_r))
-        v = np.broadcast_to(rows[:, None, :d_c], (L, H, d_c))
-        o, l = attend_rows(qh, k, v, [L - 1], sm_scale)
-        o_lat[b] = o[0]
-        lse[b] = l[0]
+        qh = np.concatenate([q_c, q_r], axis=1)  # [H, d_c + d_r]
+        # The up-projection of every head is the identity on the cached row,
+        # so head h's key for row j is k_j^h = rows[j] and its value
+        # v_j^h = rows[j, :d_c]. The H per-head dot products with the rows
+        # are then one matrix product (a library step; nothing is blocked or
+        # reordered beyond the sums the definition states).
+        z = (qh @ rows.T) * sm_scale  # [H, L]: z[h, j] = scale * q~_h . k_j^h
+        m = z.max(axis=1, keepdims=True)
+        e = np.exp(z - m)
+        den = e.sum(axis=1, keepdims=True)
+        a = e / den  # softmax over the L_b cached rows (all j <= L_b - 1)
+        o_lat[b] = a @ rows[:, :d_c]  # sum_j a_{h,j} v_j^h
+        lse[b] = (m + np.log(den))[:, 0]
     return o_lat, lse
 
 
@@ -393,8 +409,3 @@ def gated_mla_layer(x, W_c, W_q, W_uk, W_uv, W_g, W_o, sm_scale: float):
     y = gate_out_reference(x.reshape(B * L, D), o_tilde.reshape(B * L, -1), W_g, W_o)
     return c, o_tilde, y.reshape(B, L, -1)
 
-
-def default_sm_scale(d_k: int, d_r: int = 0) -> float:
-    """1/sqrt(d_k + d_r): the pages' 1/sqrt(d_h) with the RoPE columns counted
-    as part of the key width (the scale is an explicit argument everywhere)."""
-    return 1.0 / math.sqrt(d_k + d_r)

@@ -40,6 +40,24 @@ def _attend_no_max(q_rows, k, v, t_rows, scale):
     return o, lse - 1.0  # lse off by a constant
 
 
+def _decode_drops_current_token(q_abs, cache, seq_start, seq_len, *a, **kw):
+    # the current token's row left out of the softmax (exclusive boundary)
+    return _orig_decode(q_abs, cache, seq_start, [max(int(n) - 1, 1) for n in seq_len], *a, **kw)
+
+
+def _decode_lse_off(*a, **kw):
+    o, lse = _orig_decode(*a, **kw)
+    return o, lse + 0.5
+
+
+def _decode_query_rotated_one_further(q_abs, cache, seq_start, seq_len, d_c, d_r, rope_base, sm_scale, **kw):
+    # the RoPE query turned to position L_b instead of L_b - 1
+    q = np.array(q_abs, dtype=np.float64)
+    if d_r and rope_base:
+        q[..., d_c:] = _orig_rope(q[..., d_c:], 1.0, rope_base)
+    return _orig_decode(q, cache, seq_start, seq_len, d_c, d_r, rope_base, sm_scale, **kw)
+
+
 def _sigmoid_wrong(z):
     return 1.0 / (1.0 + np.exp(np.asarray(z, dtype=np.float64)))
 
@@ -102,6 +120,8 @@ def _prefill_unrotated(x, W_c, W_q, W_uk, W_uv, sm_scale, rows=None, **kw):
 
 
 _orig_attend = G.attend_rows
+_orig_decode = G.decode_reference
+_orig_rope = G.rope_rotate
 _orig_reconstruct = G.reconstruct_kv
 _orig_prepare = G.decode_prepare_reference
 _orig_prefill = G.prefill_reference
@@ -114,7 +134,12 @@ MUTATIONS = [
     ("attend_rows", _attend_strict, [lambda: P.test_causal_attention_matches_torch_sdpa(7, 3, 5, 6),
                                      P.test_whole_layer_matches_scalar_brute_force]),
     ("attend_rows", _attend_no_max, [P.test_zero_query_gives_uniform_mean_and_log_count,
-                                     P.test_decode_single_token_and_lse_closed_form]),
+                                     P.test_first_position_returns_its_own_value_and_lse]),
+    ("decode_reference", _decode_drops_current_token, [lambda: P.test_decode_matches_mqa_sdpa(0),
+                                                       P.test_decode_equals_last_prefill_row]),
+    ("decode_reference", _decode_lse_off, [P.test_decode_single_token_and_lse_closed_form,
+                                           P.test_decode_equals_last_prefill_row]),
+    ("decode_reference", _decode_query_rotated_one_further, [lambda: P.test_decode_matches_mqa_sdpa(8)]),
     ("sigmoid", _sigmoid_wrong, [P.test_sigmoid_matches_scipy_and_range, P.test_gate_special_cases,
                                  P.test_whole_layer_matches_scalar_brute_force]),
     ("value_up_projection", _value_up_transposed_heads,
