@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -180,6 +181,13 @@ gmla_status_t gmla_prefill(const void* x, const void* W_c, const void* W_dq, con
           GMLA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   REQUIRE((long long)B * L * std::max({d_model, H * (d_k + d_r), H * d_v, d_cq}) < (1LL << 40), GMLA_ERR_UNSUPPORTED,
           "problem too large");
+  // the token count B*L is a GEMM row count (int), and the bf16 attention
+  // grid holds one workgroup per (b, h, pair of 256-query tiles)
+  REQUIRE((long long)B * L <= INT_MAX, GMLA_ERR_UNSUPPORTED, "B * L must not exceed INT_MAX");
+  REQUIRE((long long)H * std::max(d_k, d_v) <= INT_MAX && (long long)H * (d_k + d_r) <= INT_MAX, GMLA_ERR_UNSUPPORTED,
+          "H * d_k and H * d_v must not exceed INT_MAX");
+  REQUIRE(dtype != GMLA_BF16 || ((long long)L + 511) / 512 * B * H <= INT_MAX, GMLA_ERR_UNSUPPORTED,
+          "prefill attention grid too large");
   REQUIRE(d_r == 0 || dtype == GMLA_BF16, GMLA_ERR_UNSUPPORTED, "decoupled RoPE in prefill is bf16 only");
   if (dtype == GMLA_BF16) {
     REQUIRE(d_r == 0 || d_r == 64, GMLA_ERR_UNSUPPORTED, "bf16 prefill needs d_r in {0, 64}");
@@ -539,6 +547,16 @@ gmla_status_t gmla_head_gate_out(const void* x, const void* o, const void* W_uv,
   if ((s = run("head_gate", st, [&] { return launch_head_gate(hg, st); }))) return s;
   if ((s = run("gemm_out", st, [&] { return launch_gemm_bf16(with_split(gemm(gated, HV, W_o, HV, y, d_model, T, d_model, HV), part), st); }))) return s;
   return ok();
+}
+
+// ============================================================ probe
+gmla_status_t gmla_probe_read(const void* src, size_t bytes, void* sink, void* stream) {
+  REQUIRE(src && sink, GMLA_ERR_INVALID_ARG, "null pointer");
+  REQUIRE(al16(src) && al16(sink) && bytes % 16 == 0, GMLA_ERR_INVALID_ARG,
+          "src and sink must be 16-byte aligned and bytes a multiple of 16");
+  hipStream_t st = (hipStream_t)stream;
+  gmla_status_t s = run("probe_read", st, [&] { return launch_probe_read(src, bytes, (unsigned*)sink, GMLA_PROBE_BLOCKS, st); });
+  return s ? s : ok();
 }
 
 // ============================================================ trace

@@ -123,6 +123,16 @@ def test_prefill_argument_checks(L):
     assert need == 2 * 16 * 2 * 128 * 2 + 2 * 128 * 64 * 2  # q, K, and V^T padded to 64 keys
 
 
+def test_prefill_rejects_token_counts_past_int(L):
+    """B * L is a GEMM row count: a product past INT_MAX (with widths small
+    enough for the 2^40 element bound) is rejected, not wrapped."""
+    kw = dict(D=64, H=1, d_c=64, d_k=64, d_v=64, dt=0)
+    assert _pre(L, B=2, Lq=1 << 30, **kw) == UNSUPPORTED
+    assert b"INT_MAX" in L.gmla_last_error()
+    assert _pre(L, B=1 << 16, Lq=1 << 15, **kw) == UNSUPPORTED
+    assert _pre(L, B=1 << 15, Lq=1 << 16, **{**kw, "dt": 1}) == UNSUPPORTED
+
+
 def _prep(L, **kw):
     a = dict(x=A, Wc=A, Wkr=A, Wdq=0, Wq=A, Wqr=A, Wuk=A, cache=A, start=A, len_=A, q=A, ws=A, wsb=1 << 40, B=4,
              D=256, H=16, d_c=512, d_cq=0, d_k=128, d_r=64, base=10000.0, dt=1)
