@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the Gated-MLA hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload decode_nope]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload all]
 
 A step is one pass of the hot path over one batch of synthetic input:
   decode_*  : gmla_decode (attention over the latent cache + split combine)
@@ -24,8 +24,14 @@ pass over as many steps with the library's event trace on (hipEvents
 recorded on the launch stream around every kernel), since those events add
 work to the stream themselves.
 
-Prints one JSON line (rank 0). The fp64 CPU oracle is timed on a bounded
-sample of the same workload on the host cores (cpu_baseline).
+By default every workload of the path runs, one after the other, and one
+JSON line carries them all: the top-level value, roofline and cpu_baseline
+are those of the causal prefill (B=2, L=8192, d_model=7168, H=64), the
+largest single-GPU workload by work, and "configs" holds the same record
+for each workload (the three decode workloads and the tiny fp32 prefill
+too). --workload NAME runs one workload alone. The fp64 CPU oracle is
+timed on a bounded sample of each workload on the host cores
+(cpu_baseline).
 """
 from __future__ import annotations
 
@@ -43,7 +49,14 @@ sys.path.insert(0, ROOT)
 METRIC = "decode tokens/s + HBM GB/s (or MFMA %) of roofline; prefill TFLOP/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
-F32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector, published
+# The fp32 path runs plain (non-packed) fp32 FMAs on the vector ALUs: 256
+# compute units x 64 FMA lanes x 2 flops x 2.4 GHz = 78.6 TFLOP/s. The
+# published 157.3 TFLOP/s fp32 vector figure counts packed fp32 (two FMAs per
+# lane and instruction), which this library never emits.
+F32_FMA_PEAK_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12
+
+ALL_WORKLOADS = ["prefill", "decode_nope", "decode_rope", "decode_long", "tiny_fp32"]
+HEADLINE = "prefill"
 
 WORKLOADS = {
     "decode_nope": ("decode_nope_b32_h64", "decode NoPE, B=32, H=64, d_c=512, L_b~U[1024,8192], bf16 + gate/W_o (d_model 7168, d_v 128)"),
@@ -64,14 +77,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode_nope", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="all", choices=["all"] + sorted(WORKLOADS))
     ap.add_argument("--copies", type=int, default=3, help="rotating input copies (cache-defeating)")
     ap.add_argument("--num-splits", type=int, default=0)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of each oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
     ap.add_argument("--no-measured-peak", action="store_true",
-                    help="skip the measured reference peaks (device copy, library GEMM)")
+                    help="skip the measured reference peaks (read-only streaming kernel, library GEMM)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (reference for HBM byte counters)")
     return ap.parse_args()
@@ -266,20 +279,25 @@ def build_prefill(args, p, torch, ops):
 
 
 # ----------------------------------------------------------------------------- cpu baseline
+def _oracle_threads():
+    """Threads the oracle's numpy work can use: the BLAS pool (matrix
+    products); elementwise numpy runs on one thread."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] + [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
 def cpu_baseline_decode(inp, budget_s):
     import numpy as np
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+    threads = _oracle_threads()
     q = inp.q_abs.float().numpy()
     cache = inp.cache  # bf16 torch; rows are upcast per sequence inside the oracle
-    # time one sequence, then size the sample to the budget
-    order = list(range(inp.B))
+    # whole sequences until the budget is spent (or the batch is done)
     done, tokens, t0 = [], 0, time.perf_counter()
-    for b in order:
+    for b in range(inp.B):
         s0, Lb = int(inp.seq_start[b]), int(inp.seq_len[b])
         rows = cache[s0:s0 + Lb].float().numpy()
         O.decode_reference(q[b:b + 1], rows, np.array([0]), np.array([Lb]), inp.d_c, inp.d_r, inp.rope_base,
@@ -296,7 +314,8 @@ def cpu_baseline_decode(inp, budget_s):
     O.gate_out_reference(inp.x[done].float().numpy(), ot, inp.W_g.float().numpy(), inp.W_o.float().numpy())
     t_go = time.perf_counter() - t1
     secs = t_dec + t_go
-    return {"value": len(done) / secs, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": len(done) / secs, "unit": "tokens/s", "cores": threads, "host_cpus": os.cpu_count(),
+            "kind": "oracle",
             "sample": f"fp64 oracle: decode of {len(done)} of {inp.B} sequences ({tokens} cached tokens) plus "
                       f"gate/W_o for those {len(done)} query tokens; {secs:.1f} s on the host"}
 
@@ -304,11 +323,7 @@ def cpu_baseline_decode(inp, budget_s):
 def cpu_baseline_prefill(p, budget_s):
     import numpy as np
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+    threads = _oracle_threads()
     # sample: the first Ls positions of sequence 0; Ls doubles until the
     # oracle run takes about a third of the budget (or covers the sequence)
     Ls = min(p.L, 64)
@@ -316,44 +331,51 @@ def cpu_baseline_prefill(p, budget_s):
          for k in ("W_c", "W_q", "W_uk", "W_uv", "W_g", "W_o", "W_kr", "W_qr")}
     while True:
         x = p.x[:1, :Ls].float().numpy()
-        t0 = time.perf_counter()
-        _, ot, _ = O.prefill_reference(x, W["W_c"], W["W_q"], W["W_uk"], W["W_uv"], p.sm_scale, W_kr=W["W_kr"],
-                                       W_qr=W["W_qr"], rope_base=p.rope_base)
-        O.gate_out_reference(x[0], ot[0], W["W_g"], W["W_o"])
-        secs = time.perf_counter() - t0
-        if secs >= budget_s / 3 or Ls >= p.L:
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            _, ot, _ = O.prefill_reference(x, W["W_c"], W["W_q"], W["W_uk"], W["W_uv"], p.sm_scale, W_kr=W["W_kr"],
+                                           W_qr=W["W_qr"], rope_base=p.rope_base)
+            O.gate_out_reference(x[0], ot[0], W["W_g"], W["W_o"])
+            reps += 1
+            secs = time.perf_counter() - t0
+            if secs >= min(1.0, budget_s / 3):
+                break
+        if secs / reps >= budget_s / 3 or Ls >= p.L:
             break
         Ls = min(p.L, Ls * 2)
     fl = prefill_flops(p.__class__(**{**p.__dict__, "B": 1, "L": Ls}))
-    return {"value": sum(fl.values()) / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    per = secs / reps
+    return {"value": sum(fl.values()) / per / 1e12, "unit": "TFLOP/s", "cores": threads, "host_cpus": os.cpu_count(),
+            "kind": "oracle",
             "sample": f"fp64 oracle: whole layer on the first {Ls} positions of one sequence "
-                      f"({sum(fl.values()) / 1e9:.1f} GFLOP); {secs:.1f} s on the host"}
+                      f"({sum(fl.values()) / 1e9:.2f} GFLOP), {reps} run(s) in {secs:.1f} s on the host"}
 
 
-def measured_peak(torch, bound):
-    """A measured reference beside the published peak, labelled separately:
-    HBM: a device-to-device copy of 1 GiB (bytes read + written per second);
-    MFMA: torch.matmul (the vendor GEMM library) on an 8192^3 bf16 product."""
+def measured_peaks(torch, ops):
+    """Measured references beside the published peaks, labelled separately:
+    HBM: the library's read-bandwidth probe streaming 2 GiB (read-only, the
+    access the HBM-bound kernels make); MFMA: torch.matmul (the vendor GEMM
+    library) on an 8192^3 bf16 product."""
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     reps = 10
-    if bound == "hbm":
-        n = 1 << 30
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(reps):
-            dst.copy_(src)
-        e1.record()
-        torch.cuda.synchronize()
-        v = 2 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
-        del src, dst
-        return {"value": v, "unit": "GB/s", "how": "device-to-device copy of 1 GiB, read + write bytes"}
-    n = 8192
-    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
-    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    out = {}
+    n = 2 << 30
+    src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+    sink = torch.empty(ops.PROBE_BLOCKS, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        ops.probe_read(src, sink)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        ops.probe_read(src, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    out["hbm"] = {"value": n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, "unit": "GB/s",
+                  "how": "read-only streaming kernel (16-byte loads) over 2 GiB"}
+    del src, sink
+    m = 8192
+    a = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    b = torch.randn(m, m, device="cuda").to(torch.bfloat16)
     for _ in range(3):
         torch.matmul(a, b)
     torch.cuda.synchronize()
@@ -362,9 +384,11 @@ def measured_peak(torch, bound):
         torch.matmul(a, b)
     e1.record()
     torch.cuda.synchronize()
-    v = 2 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    out["mfma"] = {"value": 2 * m ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12, "unit": "TFLOP/s",
+                   "how": "torch.matmul (vendor library) bf16 8192 x 8192 x 8192"}
     del a, b
-    return {"value": v, "unit": "TFLOP/s", "how": "torch.matmul (vendor library) bf16 8192 x 8192 x 8192"}
+    torch.cuda.empty_cache()
+    return out
 
 
 # ----------------------------------------------------------------------------- main
@@ -411,6 +435,162 @@ def traffic_record(kernel: str, workload: str):
     except (KeyError, ValueError):
         return None
 
+def time_region(torch, fn, n, first):
+    """Mean ms per call of fn(first), ..., fn(first + n - 1), from events
+    around the calls alone."""
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(n):
+        fn(first + i)
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / n
+
+
+def trace_region(torch, ops, fn, n, first):
+    """Per-kernel launch counts and mean device times (us) over n calls, from
+    the library's launch trace (events recorded by each kernel's dispatch)."""
+    kern = {}
+    ops.trace_begin(16 * n + 64)
+    for i in range(n):
+        fn(first + i)
+    torch.cuda.synchronize()
+    ops.trace_end()
+    for k in ops.trace_kernels():
+        cnt, ms = ops.trace_summary(k)
+        kern[k] = {"launches_per_step": cnt / n, "avg_us": ms * 1e3}
+    ops.trace_reset()
+    return kern
+
+
+def run_workload(name, args, torch, ops, W, peaks):
+    """Time one workload; returns its record (value, unit, ms_per_step,
+    config, roofline, kernels, cpu_baseline, ...)."""
+    cfg_name, desc = WORKLOADS[name]
+    log(f"[bench] {name}: generating ({desc})")
+    inp = getattr(W, cfg_name)()
+    is_decode = name.startswith("decode")
+    step, keep = (build_decode if is_decode else build_prefill)(args, inp, torch, ops)
+
+    log(f"[bench] {name}: warmup {args.warmup}")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # timed region 1: the steps alone (this gives ms_per_step and value)
+    t0 = time.perf_counter()
+    ms_step = time_region(torch, step, args.steps, args.warmup)
+    wall = (time.perf_counter() - t0) / args.steps
+    log(f"[bench] {name}: {ms_step * 1e3:.1f} us/step (wall {wall * 1e6:.1f} us/step)")
+    # timed region 2: the same steps again with the library's launch trace on;
+    # the events add work to the stream, so the step time comes from region 1
+    kern = {} if args.no_trace else trace_region(torch, ops, step, args.steps, args.warmup + args.steps)
+
+    rec = {"workload": name, "ms_per_step": ms_step, "steps": args.steps, "warmup": args.warmup,
+           "dtype": "f32" if name == "tiny_fp32" else "bf16"}
+    if is_decode:
+        # timed regions 3, 4: the step's input side alone, and the per-head
+        # gate variant of its output side, each then with its kernels
+        extra = {}
+        for xname, fn in keep[1].items():
+            for i in range(args.warmup):
+                fn(i)
+            us = time_region(torch, fn, args.steps, args.warmup) * 1e3
+            log(f"[bench] {name}: {xname} {us:.1f} us")
+            extra[xname] = (us, {} if args.no_trace else trace_region(torch, ops, fn, args.steps, 0))
+        db = decode_bytes(inp)
+        gb = gate_out_bytes(inp)
+        gf = gate_out_flops(inp)
+        alg = {"decode_attn": db["cache"] + db["q"] + db["out"], **gb}
+        flops = {"decode_attn": decode_attn_flops(inp), **gf}
+        step_bytes = sum(alg.values())
+        rec.update({"value": inp.B / (ms_step * 1e-3), "unit": "tokens/s",
+                    "config": {"workload": desc, "batch": inp.B, "heads": inp.H, "d_c": inp.d_c, "d_r": inp.d_r,
+                               "cached_tokens": db["tokens"], "num_splits": args.num_splits or "auto",
+                               "input_copies": args.copies},
+                    "step_hbm_gbs": step_bytes / (ms_step * 1e-3) / 1e9,
+                    "step_hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        for k, v in kern.items():
+            if k in alg:
+                v["alg_bytes"] = alg[k]
+                v["gbs"] = alg[k] / (v["avg_us"] * 1e-6) / 1e9
+                v["tflops"] = flops[k] / (v["avg_us"] * 1e-6) / 1e12
+        if "decode_attn" in kern:
+            # the roofline kernel: the attention over the latent cache (HBM-bound)
+            a = alg["decode_attn"] / (kern["decode_attn"]["avg_us"] * 1e-6) / 1e9
+            rec["roofline"] = {"bound": "hbm", "kernel": "decode_attn", "achieved": a, "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s", "frac": a / HBM_PEAK_GBS, "traffic": traffic_record("decode_attn", name),
+                               "alg_bytes_per_launch": alg["decode_attn"],
+                               "mfma_tflops": kern["decode_attn"]["tflops"],
+                               "mfma_frac": kern["decode_attn"]["tflops"] / BF16_PEAK_TFLOPS}
+        rec["kernels"] = kern
+        if "decode_attn" in kern and "decode_combine" in kern:
+            # the attention part of the step alone (latent-cache attention and
+            # the split-L combine, per launch), as tokens/s for one layer
+            t_att = sum(kern[k]["avg_us"] * kern[k]["launches_per_step"] for k in ("decode_attn", "decode_combine"))
+            rec["attention_only"] = {"us": t_att, "tokens_per_s": inp.B / (t_att * 1e-6),
+                                     "hbm_frac": (db["cache"] + db["q"] + db["out"]) / (t_att * 1e-6) / 1e9
+                                     / HBM_PEAK_GBS}
+        go_us = sum(kern[k]["avg_us"] for k in gb if k in kern)
+        if go_us:
+            rec["gate_out"] = {"us": go_us, "alg_bytes": sum(gb.values()),
+                               "hbm_frac": sum(gb.values()) / (go_us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+        pb = prepare_bytes(inp)
+        prep_us, prep_kern = extra["decode_prepare"]
+        rec["decode_prepare"] = {"us": prep_us, "alg_bytes": pb, "hbm_gbs": pb / (prep_us * 1e-6) / 1e9,
+                                 "hbm_frac": pb / (prep_us * 1e-6) / 1e9 / HBM_PEAK_GBS, "d_k": DECODE_D_K,
+                                 "kernels": prep_kern,
+                                 "layer_us": ms_step * 1e3 + prep_us,
+                                 "layer_tokens_per_s": inp.B / ((ms_step * 1e3 + prep_us) * 1e-6)}
+        hb = head_gate_bytes(inp)
+        hg_us, hg_kern = extra["head_gate_out"]
+        rec["head_gate_out"] = {"us": hg_us, "alg_bytes": hb, "hbm_gbs": hb / (hg_us * 1e-6) / 1e9,
+                                "hbm_frac": hb / (hg_us * 1e-6) / 1e9 / HBM_PEAK_GBS, "kernels": hg_kern,
+                                "per_channel_gate_out_us": go_us}
+        if not args.no_cpu_baseline:
+            log(f"[bench] {name}: cpu baseline (fp64 oracle)")
+            rec["cpu_baseline"] = cpu_baseline_decode(inp, args.cpu_seconds)
+    else:
+        fl = prefill_flops(inp)
+        total = sum(fl.values())
+        f32 = inp.dtype == torch.float32
+        peak = F32_FMA_PEAK_TFLOPS if f32 else BF16_PEAK_TFLOPS
+        rec.update({"value": total / (ms_step * 1e-3) / 1e12, "unit": "TFLOP/s",
+                    "config": {"workload": desc, "batch": inp.B, "seq_len": inp.L, "heads": inp.H,
+                               "gflop_per_step": total / 1e9, "input_copies": args.copies},
+                    "step_peak_frac": total / (ms_step * 1e-3) / 1e12 / peak})
+        for k, v in kern.items():
+            if k in fl:
+                v["tflops"] = fl[k] / (v["avg_us"] * 1e-6) / 1e12
+        # the roofline kernel: the causal attention, one launch per step
+        # (every GEMM of the step is listed under kernels with its TFLOP/s)
+        rk = "prefill_attn_f32" if f32 else "prefill_attn"
+        if rk in kern:
+            a = fl["prefill_attn"] / (kern[rk]["avg_us"] * 1e-6) / 1e12
+            rec["roofline"] = {"bound": "alu" if f32 else "mfma", "kernel": rk, "achieved": a, "peak": peak,
+                               "unit": "TFLOP/s", "frac": a / peak, "traffic": traffic_record(rk, name),
+                               "alg_flops_per_launch": fl["prefill_attn"]}
+            if f32:
+                rec["roofline"]["peak_how"] = "non-packed fp32 FMA: 256 CUs x 64 lanes x 2 flops x 2.4 GHz"
+        gemm_us = sum(v["avg_us"] * v["launches_per_step"] for k, v in kern.items() if k.startswith("gemm"))
+        if gemm_us:
+            gemm_fl = sum(v for k, v in fl.items() if k.startswith("gemm"))
+            rec["gemms"] = {"us": gemm_us, "tflops": gemm_fl / (gemm_us * 1e-6) / 1e12,
+                            "frac": gemm_fl / (gemm_us * 1e-6) / 1e12 / peak}
+        rec["kernels"] = kern
+        if not args.no_cpu_baseline:
+            log(f"[bench] {name}: cpu baseline (fp64 oracle)")
+            rec["cpu_baseline"] = cpu_baseline_prefill(inp, args.cpu_seconds)
+    roof = rec.get("roofline")
+    if roof and peaks and roof["bound"] in peaks:
+        roof["measured_peak"] = peaks[roof["bound"]]
+        roof["frac_of_measured"] = roof["achieved"] / peaks[roof["bound"]]["value"]
+    del step, keep, inp
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -435,155 +615,23 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
         return
 
-    cfg_name, desc = WORKLOADS[args.workload]
-    log(f"[bench] generating {args.workload} ({desc})")
-    gen = getattr(W, cfg_name)
-    inp = gen()
-    is_decode = args.workload.startswith("decode")
-    step, keep = (build_decode if is_decode else build_prefill)(args, inp, torch, ops)
-
-    log(f"[bench] warmup {args.warmup}")
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    trace = not args.no_trace
-    # timed region 1: the steps alone (this gives ms_per_step and value)
-    log(f"[bench] timing {args.steps} steps")
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = ev0.elapsed_time(ev1) / args.steps
-    log(f"[bench] {ms_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us/step)")
-
-    # timed region 2: the same steps again with the library's launch trace on
-    # (hipEvents recorded on the launch stream around every kernel); the
-    # events add work to the stream, so the step time is taken from region 1
-    kern = {}
-    if trace:
-        ops.trace_begin(16 * args.steps + 64)
-        for i in range(args.steps):
-            step(args.warmup + args.steps + i)
-        torch.cuda.synchronize()
-        ops.trace_end()
-        for k in ops.trace_kernels():
-            n, ms = ops.trace_summary(k)
-            kern[k] = {"launches_per_step": n / args.steps, "avg_us": ms * 1e3}
-        ops.trace_reset()
-
-    # timed regions 3, 4 (decode): the step's input side alone, and the
-    # per-head gate variant of its output side, each then with its kernels
-    extra = {}
-    if is_decode:
-        for name, fn in keep[1].items():
-            for i in range(args.warmup):
-                fn(i)
-            torch.cuda.synchronize()
-            ev0.record()
-            for i in range(args.steps):
-                fn(args.warmup + i)
-            ev1.record()
-            torch.cuda.synchronize()
-            us = ev0.elapsed_time(ev1) * 1e3 / args.steps
-            log(f"[bench] {name} {us:.1f} us")
-            kk = {}
-            if trace:
-                ops.trace_begin(16 * args.steps + 64)
-                for i in range(args.steps):
-                    fn(i)
-                torch.cuda.synchronize()
-                ops.trace_end()
-                for k in ops.trace_kernels():
-                    n, ms = ops.trace_summary(k)
-                    kk[k] = {"launches_per_step": n / args.steps, "avg_us": ms * 1e3}
-                ops.trace_reset()
-            extra[name] = (us, kk)
-
-    out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-           "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "f32" if args.workload == "tiny_fp32" else "bf16",
-           "data": "synthetic (seeded; random-init weights of the stated shapes)"}
-    if is_decode:
-        db = decode_bytes(inp)
-        gb = gate_out_bytes(inp)
-        gf = gate_out_flops(inp)
-        alg = {"decode_attn": db["cache"] + db["q"] + db["out"], **gb}
-        flops = {"decode_attn": decode_attn_flops(inp), **gf}
-        step_bytes = sum(alg.values())
-        value = inp.B / (ms_step * 1e-3)
-        out.update({"value": value, "unit": "tokens/s",
-                    "config": {"workload": desc, "batch": inp.B, "heads": inp.H, "d_c": inp.d_c, "d_r": inp.d_r,
-                               "cached_tokens": db["tokens"], "num_splits": args.num_splits or "auto",
-                               "input_copies": args.copies},
-                    "step_hbm_gbs": step_bytes / (ms_step * 1e-3) / 1e9,
-                    "step_hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS})
-        # dominant kernel: largest device time per step
-        if kern:
-            dom = max(kern, key=lambda k: kern[k]["avg_us"] * kern[k]["launches_per_step"])
-            for k, v in kern.items():
-                if k in alg:
-                    v["alg_bytes"] = alg[k]
-                    v["gbs"] = alg[k] / (v["avg_us"] * 1e-6) / 1e9
-                    v["tflops"] = flops[k] / (v["avg_us"] * 1e-6) / 1e12
-            if dom in alg:
-                a = alg[dom] / (kern[dom]["avg_us"] * 1e-6) / 1e9
-                out["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                   "frac": a / HBM_PEAK_GBS, "traffic": traffic_record(dom, args.workload),
-                                   "alg_bytes_per_launch": alg[dom]}
-        out["kernels"] = kern
-        if "decode_attn" in kern and "decode_combine" in kern:
-            # the attention part of the step alone (latent-cache attention and
-            # the split-L combine, per launch), as tokens/s for one layer
-            t_att = sum(kern[k]["avg_us"] * kern[k]["launches_per_step"] for k in ("decode_attn", "decode_combine"))
-            out["attention_only"] = {"us": t_att, "tokens_per_s": inp.B / (t_att * 1e-6)}
-        pb = prepare_bytes(inp)
-        prep_us, prep_kern = extra["decode_prepare"]
-        out["decode_prepare"] = {"us": prep_us, "alg_bytes": pb, "hbm_gbs": pb / (prep_us * 1e-6) / 1e9,
-                                 "hbm_frac": pb / (prep_us * 1e-6) / 1e9 / HBM_PEAK_GBS, "d_k": DECODE_D_K,
-                                 "kernels": prep_kern,
-                                 "layer_us": ms_step * 1e3 + prep_us,
-                                 "layer_tokens_per_s": inp.B / ((ms_step * 1e3 + prep_us) * 1e-6)}
-        hb = head_gate_bytes(inp)
-        hg_us, hg_kern = extra["head_gate_out"]
-        out["head_gate_out"] = {"us": hg_us, "alg_bytes": hb, "hbm_gbs": hb / (hg_us * 1e-6) / 1e9,
-                                "hbm_frac": hb / (hg_us * 1e-6) / 1e9 / HBM_PEAK_GBS, "kernels": hg_kern,
-                                "per_channel_gate_out_us": sum(kern[k]["avg_us"] for k in gb if k in kern)}
-        if not args.no_cpu_baseline:
-            log("[bench] cpu baseline (fp64 oracle)")
-            out["cpu_baseline"] = cpu_baseline_decode(inp, args.cpu_seconds)
-    else:
-        fl = prefill_flops(inp)
-        total = sum(fl.values())
-        out.update({"value": total / (ms_step * 1e-3) / 1e12, "unit": "TFLOP/s",
-                    "config": {"workload": desc, "batch": inp.B, "seq_len": inp.L, "heads": inp.H,
-                               "gflop_per_step": total / 1e9, "input_copies": args.copies}})
-        if kern:
-            peak = F32_VALU_PEAK_TFLOPS if inp.dtype == torch.float32 else BF16_PEAK_TFLOPS
-            for k, v in kern.items():
-                if k in fl:
-                    v["tflops"] = fl[k] / (v["avg_us"] * 1e-6) / 1e12
-            cand = {k: v for k, v in kern.items() if k in fl}
-            if cand:
-                dom = max(cand, key=lambda k: cand[k]["avg_us"] * cand[k]["launches_per_step"])
-                a = fl[dom] / (kern[dom]["avg_us"] * 1e-6) / 1e12
-                out["roofline"] = {"bound": "alu" if inp.dtype == torch.float32 else "mfma", "kernel": dom,
-                                   "achieved": a, "peak": peak, "unit": "TFLOP/s", "frac": a / peak,
-                                   "traffic": traffic_record(dom, args.workload),
-                                   "alg_flops_per_launch": fl[dom]}
-        out["kernels"] = kern
-        if not args.no_cpu_baseline:
-            log("[bench] cpu baseline (fp64 oracle)")
-            out["cpu_baseline"] = cpu_baseline_prefill(inp, args.cpu_seconds)
-    roof = out.get("roofline")
-    if roof and not args.no_measured_peak and roof["bound"] in ("hbm", "mfma"):
-        mp = measured_peak(torch, roof["bound"])
-        roof["measured_peak"] = mp
-        roof["frac_of_measured"] = roof["achieved"] / mp["value"]
+    peaks = None
+    if not args.no_measured_peak:
+        log("[bench] measured reference peaks")
+        peaks = measured_peaks(torch, ops)
+    names = ALL_WORKLOADS if args.workload == "all" else [args.workload]
+    recs = {n: run_workload(n, args, torch, ops, W, peaks) for n in names}
+    head = recs[HEADLINE] if HEADLINE in recs else recs[names[0]]
+    out = {"metric": METRIC, "value": head["value"], "unit": head["unit"], "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": head["dtype"],
+           "data": "synthetic (seeded; random-init weights of the stated shapes)",
+           "config": head["config"]}
+    for k in ("roofline", "cpu_baseline", "kernels", "gemms", "step_peak_frac"):
+        if k in head:
+            out[k] = head[k]
+    if len(recs) > 1:
+        out["configs"] = recs
     print(json.dumps(out), flush=True)
 
 

@@ -109,6 +109,10 @@ bool decode_bf16_supported(int d_c, int d_r);
 // workgroups per slice (head chunks) of the bf16 decode kernel for H heads
 int decode_head_chunks(int H);
 
+// read-bandwidth probe: `blocks` workgroups stream `bytes` (a multiple of 16)
+// of src and write one word each to sink[0 .. blocks - 1]
+hipError_t launch_probe_read(const void* src, size_t bytes, unsigned* sink, int blocks, hipStream_t st);
+
 // ---------------------------------------------------------------- GEMM
 // C[m, n] = epi( sum_k A[m, k] * W[n, k] ), all bf16 with fp32 accumulation.
 // A is [M, K] (row stride lda), W is [N, K] (row stride ldw), C is [M, N]

@@ -68,6 +68,8 @@ def lib():
     L.gmla_last_error.argtypes = []
     L.gmla_last_error.restype = C.c_char_p
     L.gmla_version.restype = i32
+    L.gmla_probe_read.argtypes = [vp, sz, vp, vp]
+    L.gmla_probe_read.restype = i32
     L.gmla_trace_begin.argtypes = [i32]
     L.gmla_trace_begin.restype = i32
     L.gmla_trace_end.restype = i32
@@ -232,6 +234,21 @@ def head_gate_out(x, o, W_g, W_o, b_g=None, W_uv=None, y=None, workspace=None):
     _check(lib().gmla_head_gate_out(_vp(x), _vp(o), _vp(W_uv), _vp(W_g), _vp(b_g), _vp(W_o), _vp(y), _vp(workspace),
                                     wsb, T, D, H, d_c, d_v, dt, _stream()))
     return y
+
+
+# ------------------------------------------------------------------ probe
+PROBE_BLOCKS = 2048  # GMLA_PROBE_BLOCKS
+
+
+def probe_read(src, sink=None):
+    """Stream the bytes of device tensor `src` (read-bandwidth probe); the
+    returned sink holds one word per workgroup."""
+    _dev(src, sink)
+    nbytes = src.numel() * src.element_size()
+    if sink is None:
+        sink = torch.empty(PROBE_BLOCKS, dtype=torch.int32, device=src.device)
+    _check(lib().gmla_probe_read(_vp(src), nbytes, _vp(sink), _stream()))
+    return sink
 
 
 # ------------------------------------------------------------------ trace

@@ -217,6 +217,15 @@ const char* gmla_last_error(void);
 /* Library version as 10000*major + 100*minor + patch. */
 int gmla_version(void);
 
+/* Read-bandwidth probe: streams `bytes` (a multiple of 16) of the device
+ * buffer `src` with 16-byte loads in GMLA_PROBE_BLOCKS workgroups, each of
+ * which writes one 32-bit word to `sink` (device, at least
+ * GMLA_PROBE_BLOCKS * 4 bytes), so that no load can be dropped. Not part
+ * of the attention path: the benchmark times it to measure the read-only
+ * HBM rate that the bandwidth-bound kernels are compared against. */
+#define GMLA_PROBE_BLOCKS 2048
+gmla_status_t gmla_probe_read(const void* src, size_t bytes, void* sink, void* stream);
+
 /* Kernel trace: while enabled, every kernel the library enqueues is bracketed
  * by a pair of HIP events recorded on the same stream, so per-kernel device
  * time can be read back without a profiler. gmla_trace_begin creates up to
