@@ -337,6 +337,57 @@ gmla_status_t gmla_decode(const void* q_abs, const void* cache, const int64_t* s
   return ok();
 }
 
+// ============================================================ decode without allocation
+// The scratch of gmla_decode_noalloc: one library-owned device array per GPU
+// (each device holds its own copy, at its own address, until the process
+// ends). Host code never uses the array's name as an address: it takes the
+// device address from hipGetSymbolAddress once per device.
+static __device__ __align__(256) unsigned char scratch[GMLA_DECODE_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call per device, with that device current).
+gmla_status_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GMLA_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(GMLA_ERR_UNSUPPORTED, "device index out of range");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(GMLA_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GMLA_OK;
+}
+}  // namespace
+
+gmla_status_t gmla_decode_noalloc(const void* q_abs, const void* cache, const int64_t* seq_start,
+                                  const int32_t* seq_len, void* o_lat, float* lse, int B, int H, int d_c, int d_r,
+                                  float rope_base, float sm_scale, int num_splits, gmla_dtype_t dtype, void* stream) {
+  REQUIRE(dtype == GMLA_F32 || dtype == GMLA_BF16, GMLA_ERR_INVALID_ARG, "dtype must be GMLA_F32 or GMLA_BF16");
+  REQUIRE(B > 0 && H > 0 && d_c > 0 && num_splits >= 0, GMLA_ERR_INVALID_ARG, "sizes must be positive");
+  const size_t need = gmla_decode_workspace_size(B, H, d_c, num_splits, dtype);
+  REQUIRE(need <= (size_t)GMLA_DECODE_SCRATCH_BYTES, GMLA_ERR_UNSUPPORTED,
+          "gmla_decode_noalloc: this call needs " + std::to_string(need) + " bytes of scratch, more than the " +
+              std::to_string((size_t)GMLA_DECODE_SCRATCH_BYTES) + " the library holds per GPU");
+  void* ws = nullptr;
+  if (need > 0) {
+    gmla_status_t s = scratch_address(&ws);
+    if (s) return s;
+  }
+  // the same checks and kernels as gmla_decode, on the library's scratch
+  return gmla_decode(q_abs, cache, seq_start, seq_len, o_lat, lse, ws, need > 0 ? (size_t)GMLA_DECODE_SCRATCH_BYTES : 0,
+                     B, H, d_c, d_r, rope_base, sm_scale, num_splits, dtype, stream);
+}
+
 // ============================================================ decode-step projections
 size_t gmla_decode_prepare_workspace_size(int B, int d_model, int H, int d_c, int d_cq, int d_k, int d_r,
                                           gmla_dtype_t dtype) {

@@ -51,6 +51,8 @@ def lib():
     L.gmla_decode_workspace_size.restype = sz
     L.gmla_decode.argtypes = [vp] * 6 + [vp, sz] + [i32] * 4 + [f32, f32, i32, i32, vp]
     L.gmla_decode.restype = i32
+    L.gmla_decode_noalloc.argtypes = [vp] * 6 + [i32] * 4 + [f32, f32, i32, i32, vp]
+    L.gmla_decode_noalloc.restype = i32
     L.gmla_decode_prepare_workspace_size.argtypes = [i32] * 8
     L.gmla_decode_prepare_workspace_size.restype = sz
     L.gmla_decode_prepare.argtypes = [vp] * 11 + [vp, sz] + [i32] * 7 + [f32, i32, vp]
@@ -166,6 +168,26 @@ def decode(q_abs, cache, seq_start, seq_len, d_c: int, d_r: int, rope_base: floa
     _check(lib().gmla_decode(_vp(q_abs), _vp(cache), _vp(seq_start), _vp(seq_len), _vp(o_lat), _vp(lse),
                              _vp(workspace), wsb, B, H, d_c, d_r, float(rope_base), float(sm_scale), int(num_splits),
                              dt, _stream()))
+    return o_lat, lse
+
+
+def decode_noalloc(q_abs, cache, seq_start, seq_len, d_c: int, d_r: int, rope_base: float, sm_scale: float,
+                   num_splits: int = 0, o_lat=None, lse=None):
+    """gmla_decode on the library's own scratch (no workspace argument, no
+    device allocation by the library); same arguments and results."""
+    _dev(q_abs, cache, seq_start, seq_len, o_lat, lse)
+    if seq_start.dtype != torch.int64 or seq_len.dtype != torch.int32:
+        raise TypeError("seq_start must be int64 and seq_len int32")
+    B, H, W = q_abs.shape
+    if W != d_c + d_r or cache.shape[-1] != W:
+        raise ValueError("q_abs/cache width must be d_c + d_r")
+    dt = _dtype_code(q_abs)
+    if o_lat is None:
+        o_lat = torch.empty((B, H, d_c), dtype=q_abs.dtype, device=q_abs.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q_abs.device)
+    _check(lib().gmla_decode_noalloc(_vp(q_abs), _vp(cache), _vp(seq_start), _vp(seq_len), _vp(o_lat), _vp(lse), B, H,
+                                     d_c, d_r, float(rope_base), float(sm_scale), int(num_splits), dt, _stream()))
     return o_lat, lse
 
 

@@ -127,6 +127,27 @@ gmla_status_t gmla_decode(const void* q_abs, const void* cache, const int64_t* s
                           int d_r, float rope_base, float sm_scale, int num_splits, gmla_dtype_t dtype, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Decode without allocation: gmla_decode for callers that cannot allocate
+ * device memory or pass a workspace -- code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. The arguments, checks,
+ * kernels and results are those of gmla_decode (bit-identical for the same
+ * num_splits); the split-L scratch (cost offsets and partial outputs) lives
+ * in a library-owned static device array of GMLA_DECODE_SCRATCH_BYTES per
+ * GPU, held by each GPU the library runs on until the process ends. No
+ * device memory is allocated by the call. A call whose scratch need
+ * (gmla_decode_workspace_size) exceeds GMLA_DECODE_SCRATCH_BYTES returns
+ * GMLA_ERR_UNSUPPORTED and enqueues nothing (the automatic slice count fits
+ * for every batch up to ~2^20 sequences with d_c = 512). Every call on a GPU
+ * shares that GPU's array and leaves its contents behind (nothing in it
+ * needs to start at zero): calls that overlap in time on one GPU, e.g. on
+ * two streams, race on it and must be serialised by the caller.
+ * ---------------------------------------------------------------------- */
+#define GMLA_DECODE_SCRATCH_BYTES (48u << 20)
+gmla_status_t gmla_decode_noalloc(const void* q_abs, const void* cache, const int64_t* seq_start,
+                                  const int32_t* seq_len, void* o_lat, float* lse, int B, int H, int d_c, int d_r,
+                                  float rope_base, float sm_scale, int num_splits, gmla_dtype_t dtype, void* stream);
+
+/* ------------------------------------------------------------------------
  * Decode-step projections: the new token's cache row and its absorbed query,
  * the inputs of gmla_decode ([N03] §5.1 and exercise 4 answer for the
  * absorbed query, §5.2 for the decoupled RoPE key that is rotated once and

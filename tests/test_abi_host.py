@@ -67,6 +67,17 @@ def test_decode_argument_checks(L):
     assert _dec(L, ws=A + 16) == INVALID            # workspace must be 256-byte aligned
 
 
+def test_decode_noalloc_refuses_scratch_past_its_size(L):
+    """The no-allocation decode refuses, before any HIP call, a request whose
+    workspace would exceed the library's static scratch."""
+    args = lambda B, H, splits: (A, A, A, A, A, 0, B, H, 512, 64, 10000.0, 0.1, splits, 1, None)
+    big = L.gmla_decode_workspace_size(64, 128, 512, 65535, 1)
+    assert big > 48 << 20
+    assert L.gmla_decode_noalloc(*args(64, 128, 65535)) == UNSUPPORTED
+    assert b"scratch" in L.gmla_last_error()
+    assert L.gmla_decode_noalloc(*args(0, 128, 0)) == INVALID
+
+
 def test_decode_workspace_size_formula(L):
     B, H, d_c, G = 4, 64, 512, 8
     up = lambda n: (n + 255) // 256 * 256
