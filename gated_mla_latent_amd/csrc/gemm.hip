@@ -11,9 +11,15 @@
 // The weight is the MFMA "A" side: the accumulator layout then gives each lane
 // four consecutive output columns, which become one 8-byte store.
 //
-// Two kernels:
+// Three kernels:
+//  * gemm_big: 256 x 256 x 64 tiles for grids of at least 256 tiles and
+//    K >= 2048 (the prefill projections of x and of o~): 4 waves, one per
+//    SIMD, each owning 128 x 128 of the tile (accumulators in AGPRs);
+//    operands staged through registers two k-tiles ahead with buffer loads,
+//    then into a double-buffered LDS tile with padded rows.
 //  * gemm_tile: LDS-tiled (BN x BM x 64 tiles, 2 stages, direct-to-LDS
-//    16-byte loads, XOR-swizzled rows, 8 waves) for token counts >= 65.
+//    16-byte loads, XOR-swizzled rows, 8 waves) for the other token counts
+//    >= 65.
 //  * gemm_skinny: M <= 64 (decode-step projections). Weight-streaming bound:
 //    each workgroup owns 32 output columns, its 4 waves split K and stream
 //    their chunks through private LDS rings (several chunks in flight per
@@ -212,6 +218,218 @@ void gemm_tile_kernel(GemmArgs g) {
             u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
       } else {
         store4<EPI>(g, Cp, Op, m, n, v[0], v[1], v[2], v[3]);  // the written width is a multiple of 4
+        store4<EPI>(g, Cp, Op, m, n + 4, v[4], v[5], v[6], v[7]);
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// 256 x 256 tiles, 4 waves (one per SIMD), wave (wn, wm) owns 128 weight rows
+// x 128 activation rows of the tile: 16 accumulators of 32 x 32 (AGPRs), and
+// each 16-wide k-step reads 8 fragments for 16 MFMAs (half the LDS reads per
+// MFMA of two waves per SIMD with 128 x 64 each).
+//
+// Loads: every thread moves 16 chunks of 16 bytes per 64-wide k-tile with
+// buffer loads into registers (two register sets: tiles t + 1 and t + 2 are
+// in flight while tile t is multiplied), and writes them to the LDS stage of
+// tile t + 1 a quarter at a time between the MFMAs of tile t; the refill of
+// the freed registers with tile t + 3 follows each quarter. The buffer
+// descriptors cover exactly the operand bytes, so rows past N (or M) read as
+// zeros and edge tiles need no clamping. LDS rows are 144 bytes (128 of data,
+// 16 of padding): the fragment reads (32 consecutive rows at one 16-byte
+// chunk per half-wave) fall on distinct banks, and every k-step is a
+// compile-time offset from one base address per operand.
+//
+// Measured at 16384 x 8192 x 7168 and 16384 x 7168 x 8192 (interleaved
+// medians, same box): 1462-1477 us against 1590 us for gemm_tile, with the
+// same bits. The shader clock during these GEMMs reads 1.6-1.7 GHz (s_memtime
+// against s_memrealtime), so power, not the MFMA issue rate, bounds them.
+namespace big {
+constexpr int BN = 256, BM = 256, BK = 64;
+constexpr int TN = 4, TM = 4;         // 32 x 32 blocks per wave (weights x activations)
+constexpr int RSB = 144;              // LDS row stride in bytes
+constexpr int STAGE = (BN + BM) * RSB;
+constexpr int LDS = 2 * STAGE;        // 144 KiB
+constexpr int NS = 16;                // 16-byte chunks per thread per k-tile
+constexpr int RS = (BN / 2) * 4 + 16; // epilogue row stride (fp32, half the columns)
+static_assert(BM * RS <= LDS, "epilogue tile fits in the ring");
+}  // namespace big
+
+template <int EPI>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void gemm_big_kernel(GemmArgs g) {
+  using namespace big;
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  LDS_AS char* smem = (LDS_AS char*)smem_raw;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave & 1, wm = wave >> 1;
+  const int tiles_n = (c_cols<EPI>(g) + BN - 1) / BN, tiles_m = (g.M + BM - 1) / BM;
+  const int total = tiles_n * tiles_m;
+  // XCD-contiguous tile ranges, then groups of 4 m-tiles (as gemm_tile)
+  int pid = blockIdx.x;
+  if (total % 8 == 0) pid = (pid % 8) * (total / 8) + pid / 8;
+  constexpr int GROUP = 4;
+  const int group_size = GROUP * tiles_n;
+  const int grp = pid / group_size;
+  const int first_m = grp * GROUP;
+  const int gm = (tiles_m - first_m) < GROUP ? (tiles_m - first_m) : GROUP;
+  const int tile_m = first_m + (pid % group_size) % gm;
+  const int tile_n = (pid % group_size) / gm;
+  const int n0 = tile_n * BN, m0 = tile_m * BM;
+  const int batch = blockIdx.y;
+  const bf16* A = g.A + batch * g.sA;
+  const bf16* W = g.W + batch * g.sW;
+  bf16* Cp = g.C + batch * g.sC;
+  const bf16* Op = (EPI == EPI_GATE) ? g.O + batch * g.sO : nullptr;
+
+  // descriptors over this batch's operand bytes (raw buffers, 32-bit sizes;
+  // the launcher checks that every offset fits)
+  const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)W, (short)0, (int)(((int64_t)(g.N - 1) * g.ldw + g.K) * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)A, (short)0, (int)(((int64_t)(g.M - 1) * g.lda + g.K) * 2), 0x00020000);
+  // chunk slot r of a k-tile: row 32 r + tid / 8 of the weight tile (r < 8)
+  // or of the activation tile (r >= 8), 16-byte piece tid % 8
+  const int rsub = tid >> 3, piece = tid & 7;
+  const int vW = ((n0 + rsub) * g.ldw + piece * 8) * 2;
+  const int vA = ((m0 + rsub) * g.lda + piece * 8) * 2;
+  const int sW = 32 * g.ldw * 2, sA = 32 * g.lda * 2;
+  const unsigned dst0 = (unsigned)(rsub * RSB + piece * 16);
+  const int ktiles = g.K / BK;
+  u32x4 R0[NS], R1[NS];
+  auto issue = [&](u32x4* R, int r, int kt) {
+    if (r < 8) R[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rW, vW, kt * 128 + r * sW, 0));
+    else R[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, vA, kt * 128 + (r - 8) * sA, 0));
+  };
+  auto put = [&](const u32x4* R, int r, int st) {
+    *(LDS_AS u32x4*)(smem + st * STAGE + dst0 + r * 32 * RSB) = R[r];
+  };
+
+  floatx16 acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = floatx16{};
+  // fragment rows: weights 128 wn + 32 i + lane % 32, activations 128 wm +
+  // 32 j + lane % 32; k-step kk reads 16-byte chunk 2 kk + lane / 32
+  const unsigned fw0 = (unsigned)((wn * (BN / 2) + (lane & 31)) * RSB + (lane >> 5) * 16);
+  const unsigned fa0 = (unsigned)(BN * RSB + (wm * (BM / 2) + (lane & 31)) * RSB + (lane >> 5) * 16);
+  auto read_frags = [&](bf16x8* wf, bf16x8* af, int st, int kk) {
+#pragma unroll
+    for (int i = 0; i < TN; ++i) wf[i] = as_bf16x8(lds_read16(smem + st * STAGE + fw0 + i * 32 * RSB + kk * 32));
+#pragma unroll
+    for (int j = 0; j < TM; ++j) af[j] = as_bf16x8(lds_read16(smem + st * STAGE + fa0 + j * 32 * RSB + kk * 32));
+  };
+
+  // prologue: tile 0 -> stage 0; tiles 1 and 2 in flight in R1 and R0
+#pragma unroll
+  for (int r = 0; r < NS; ++r) issue(R0, r, 0);
+  if (ktiles > 1) {
+#pragma unroll
+    for (int r = 0; r < NS; ++r) issue(R1, r, 1);
+  }
+#pragma unroll
+  for (int r = 0; r < NS; ++r) put(R0, r, 0);
+  if (ktiles > 2) {
+#pragma unroll
+    for (int r = 0; r < NS; ++r) issue(R0, r, 2);
+  }
+  lds_barrier();
+
+  // iteration t multiplies tile t (stage st = t % 2); quarter c reads the
+  // fragments of k-step c + 1 ahead, runs the 16 MFMAs of k-step c, writes
+  // chunk slots 4c .. 4c + 3 of tile t + 1 (register set R) to the other
+  // stage and refills them with tile t + 3. The scheduling groups put the
+  // fragment reads first and spread the writes and loads between the MFMAs.
+  auto body = [&](u32x4* R, int t, int st, bool wr, bool rf) {
+    bf16x8 wf[2][TN], af[2][TM];
+    read_frags(wf[0], af[0], st, 0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (c < 3) read_frags(wf[(c + 1) & 1], af[(c + 1) & 1], st, c + 1);
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) acc[i][j] = mfma32(wf[c & 1][i], af[c & 1][j], acc[i][j]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (wr) put(R, 4 * c + q, st ^ 1);
+        if (rf) issue(R, 4 * c + q, t + 3);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // DS reads
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    lds_barrier();
+  };
+  // the register set alternates with the tile, so iterations go in pairs
+  int t = 0;
+  for (; t + 4 < ktiles; t += 2) {
+    body(R1, t, 0, true, true);
+    body(R0, t + 1, 1, true, true);
+  }
+  for (; t < ktiles; t += 2) {
+    body(R1, t, 0, t + 1 < ktiles, t + 3 < ktiles);
+    if (t + 1 < ktiles) body(R0, t + 1, 1, t + 2 < ktiles, t + 4 < ktiles);
+  }
+
+  // Epilogue through LDS, one column half (BN/2) at a time, as gemm_tile.
+  LDS_AS float* ct = (LDS_AS float*)smem;
+  const bool vec16 = g.ldc % 8 == 0 && g.sC % 8 == 0 && (EPI != EPI_GATE || (g.ldo % 8 == 0 && g.sO % 8 == 0));
+  constexpr int HN = BN / 2;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    lds_barrier();
+    if (wn == half) {
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+          const int ml = wm * (BM / 2) + j * 32 + (lane & 31);
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int nl = i * 32 + 8 * r4 + 4 * (lane >> 5);
+            *(LDS_AS floatx4*)((LDS_AS char*)ct + ml * RS + nl * 4) =
+                floatx4{acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
+          }
+        }
+    }
+    lds_barrier();
+    constexpr int ITEMS = BM * HN / 8;  // 8 columns per item
+    const int ncols = c_cols<EPI>(g);
+#pragma unroll
+    for (int it = tid; it < ITEMS; it += 256) {
+      const int ml = it / (HN / 8), nl = (it % (HN / 8)) * 8;
+      const int m = m0 + ml, n = n0 + half * HN + nl;
+      if (m >= g.M || n >= ncols) continue;
+      const floatx4 v0 = *(const LDS_AS floatx4*)((const LDS_AS char*)ct + ml * RS + nl * 4);
+      const floatx4 v1 = *(const LDS_AS floatx4*)((const LDS_AS char*)ct + ml * RS + nl * 4 + 16);
+      float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      if (n + 8 > g.N) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = n + e < g.N ? v[e] : 0.f;  // padding columns
+      }
+      if (vec16 && n + 8 <= ncols) {
+        if constexpr (EPI == EPI_GATE) {
+          const u32x4 ov = *(const u32x4*)(Op + (int64_t)m * g.ldo + n);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[2 * e] = sigmoidf_fast(v[2 * e]) * bf16_bits_to_f32((unsigned short)(ov[e] & 0xffff));
+            v[2 * e + 1] = sigmoidf_fast(v[2 * e + 1]) * bf16_bits_to_f32((unsigned short)(ov[e] >> 16));
+          }
+        }
+        *(u32x4*)(Cp + (int64_t)m * g.ldc + n) =
+            u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+      } else {
+        store4<EPI>(g, Cp, Op, m, n, v[0], v[1], v[2], v[3]);
         store4<EPI>(g, Cp, Op, m, n + 4, v[4], v[5], v[6], v[7]);
       }
     }
@@ -478,6 +696,28 @@ static hipError_t launch_tile(const GemmArgs& g, hipStream_t st) {
   return launch(kern, dim3(tiles, g.batches), dim3(512), LDS, st, g);
 }
 
+// The big-tile kernel addresses its operands with 32-bit buffer offsets:
+// every row start of a batch's A and W (plus a tile of rows past the end,
+// which read as zeros) and the descriptor sizes must stay below 2^31.
+template <int EPI>
+static bool big_fits(const GemmArgs& g) {
+  const long long lim = 1LL << 31;
+  return ((long long)g.N + big::BN) * g.ldw * 2 < lim && ((long long)g.M + big::BM) * g.lda * 2 < lim &&
+         ((long long)(g.N - 1) * g.ldw + g.K) * 2 < lim && ((long long)(g.M - 1) * g.lda + g.K) * 2 < lim;
+}
+
+template <int EPI>
+static hipError_t launch_big(const GemmArgs& g, hipStream_t st) {
+  auto kern = gemm_big_kernel<EPI>;
+  {
+    hipError_t e = lds_opt_in((const void*)kern, big::LDS);
+    if (e != hipSuccess) return e;
+  }
+  const int ncols = (EPI == EPI_STORE && g.npad > g.N) ? g.npad : g.N;
+  const int tiles = ((ncols + big::BN - 1) / big::BN) * ((g.M + big::BM - 1) / big::BM);
+  return launch(kern, dim3(tiles, g.batches), dim3(256), big::LDS, st, g);
+}
+
 static bool skinny_path(int M, int N, int npad) { return M <= 64 && !(npad > N); }
 
 // Columns per skinny workgroup. With up to 32 rows the kernel streams
@@ -529,7 +769,11 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
     return nt2 ? launch_skinny<2, 2, EPI>(h, st) : launch_skinny<2, 1, EPI>(h, st);
   }
   const long long big_tiles = (long long)((g.N + 255) / 256) * ((g.M + 255) / 256) * g.batches;
-  if (big_tiles >= 256) return launch_tile<256, 256, EPI>(g, st);
+  // the big-tile kernel's two-tile lookahead pays off over long K; at short
+  // K (the K and V reconstruction, K = 512) its prologue dominates and
+  // gemm_tile measured faster (182 against 230 us)
+  if (big_tiles >= 256)
+    return g.K >= 2048 && big_fits<EPI>(g) ? launch_big<EPI>(g, st) : launch_tile<256, 256, EPI>(g, st);
   return launch_tile<128, 128, EPI>(g, st);
 }
 

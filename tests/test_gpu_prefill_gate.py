@@ -25,7 +25,10 @@ def _np(t):
 
 
 @pytest.mark.parametrize("B,L,D,H,d_c,d", [(2, 300, 256, 4, 128, 128), (1, 517, 512, 3, 64, 64),
-                                           (1, 64, 128, 2, 64, 128), (3, 33, 256, 5, 128, 64)])
+                                           (1, 64, 128, 2, 64, 128), (3, 33, 256, 5, 128, 64),
+                                           # 256 x 256 tiles for the query, key, value and gate GEMMs,
+                                           # ragged token rows (2000) and V^T padded from 1000 to 1024 keys
+                                           (2, 1000, 512, 64, 128, 128)])
 def test_prefill_bf16_matches_oracle(B, L, D, H, d_c, d):
     say(f"[prefill bf16] B={B} L={L} D={D} H={H} d_c={d_c} d={d}")
     inp = W.make_prefill(B, L, D, H, d_c, d, d, seed=21)
