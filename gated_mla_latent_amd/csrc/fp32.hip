@@ -4,7 +4,8 @@
 //
 //  * gemm_f32: C = epi(A . W^T) with the same epilogues as the bf16 GEMM
 //    (store, or Sigmoid(acc) * O -- "Gated MLA 计算公式" §二 boxed equation).
-//  * attn_row_f32: one workgroup per attention row. Prefill rows attend keys
+//  * attn_row: one workgroup per attention row (fp32 elements, or bf16
+//    elements widened to fp32 for the generic bf16 decode). Prefill rows attend keys
 //    s <= t of their own (b, h) ("Gated MLA 计算公式" §二 first equation);
 //    decode rows attend all L_b cached rows with the latent as value and the
 //    query's RoPE part rotated to position L_b - 1 ("LLM 注意力与计算内核精读笔记 · 03"
@@ -62,19 +63,28 @@ hipError_t launch_gemm_f32(const GemmF32Args& g, hipStream_t st) {
 }
 
 // --------------------------------------------------------------------------
+// element loads and stores of the row kernels: fp32, or bf16 widened to fp32
+// (the generic bf16 decode below)
+__device__ __forceinline__ float ld_f(const float* p) { return *p; }
+__device__ __forceinline__ float ld_f(const bf16* p) { return (float)*p; }
+__device__ __forceinline__ void st_f(float* p, float v) { *p = v; }
+__device__ __forceinline__ void st_f(bf16* p, float v) { *p = __builtin_bit_cast(bf16, f32_to_bf16_bits(v)); }
+
+template <typename E>
 struct RowJob {
   const float* q;     // Dk floats (already rotated)
-  const float* k;     // key s at k + s * ks
-  const float* v;     // value s at v + s * vs
+  const E* k;         // key s at k + s * ks
+  const E* v;         // value s at v + s * vs
   int64_t ks, vs;
   int n;              // keys 0 .. n-1
-  float* o;           // Dv floats
+  E* o;               // Dv elements
   float* lse;         // or null
 };
 
 constexpr int kMaxDk = 1024, kMaxDv = 512;
 
-__device__ void attn_row(const RowJob& j, int Dk, int Dv, float scale, float* qs, float* zs) {
+template <typename E>
+__device__ void attn_row(const RowJob<E>& j, int Dk, int Dv, float scale, float* qs, float* zs) {
   const int tid = threadIdx.x;
   // each thread owns output channels tid and tid + 256
   float o0 = 0.f, o1 = 0.f, m = -INFINITY, l = 0.f;
@@ -82,9 +92,9 @@ __device__ void attn_row(const RowJob& j, int Dk, int Dv, float scale, float* qs
     const int s = s0 + tid;
     float z = -INFINITY;
     if (s < j.n) {
-      const float* kr = j.k + s * j.ks;
+      const E* kr = j.k + s * j.ks;
       float acc = 0.f;
-      for (int d = 0; d < Dk; ++d) acc = fmaf(qs[d], kr[d], acc);
+      for (int d = 0; d < Dk; ++d) acc = fmaf(qs[d], ld_f(kr + d), acc);
       z = acc * scale;
     }
     zs[tid] = z;
@@ -98,17 +108,17 @@ __device__ void attn_row(const RowJob& j, int Dk, int Dv, float scale, float* qs
     for (int i = 0; i < cnt; ++i) {
       const float p = expf(zs[i] - m_new);
       l += p;
-      const float* vr = j.v + (s0 + i) * j.vs;
-      if (tid < Dv) o0 = fmaf(p, vr[tid], o0);
-      if (tid + 256 < Dv) o1 = fmaf(p, vr[tid + 256], o1);
+      const E* vr = j.v + (s0 + i) * j.vs;
+      if (tid < Dv) o0 = fmaf(p, ld_f(vr + tid), o0);
+      if (tid + 256 < Dv) o1 = fmaf(p, ld_f(vr + tid + 256), o1);
     }
     m = m_new;
     __syncthreads();
   }
   if (j.n <= 0) { m = -INFINITY; l = 0.f; }
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  if (tid < Dv) j.o[tid] = o0 * inv;
-  if (tid + 256 < Dv) j.o[tid + 256] = o1 * inv;
+  if (tid < Dv) st_f(j.o + tid, o0 * inv);
+  if (tid + 256 < Dv) st_f(j.o + tid + 256, o1 * inv);
   if (tid == 0 && j.lse) j.lse[0] = (l > 0.f) ? m + logf(l) : -INFINITY;
 }
 
@@ -121,7 +131,7 @@ __global__ __launch_bounds__(256) void prefill_attn_f32_kernel(AttnF32Args a) {
   const float* qp = a.q + b * a.sqb + t * a.sqt + h * a.sqh;
   for (int d = threadIdx.x; d < a.Dk; d += 256) qs[d] = qp[d];
   __syncthreads();
-  RowJob j;
+  RowJob<float> j;
   j.q = qs;
   j.k = a.k + b * a.skb + h * a.skh; j.ks = a.skt;
   j.v = a.v + b * a.svb + h * a.svh; j.vs = a.svt;
@@ -131,15 +141,19 @@ __global__ __launch_bounds__(256) void prefill_attn_f32_kernel(AttnF32Args a) {
   attn_row(j, a.Dk, a.Dv, a.scale, qs, zs);
 }
 
-__global__ __launch_bounds__(256) void decode_f32_kernel(DecodeF32Args a) {
+// One workgroup per (sequence, head): fp32 decode, and the generic bf16
+// decode for latent and RoPE widths the MFMA decode kernel does not take
+// (element type E of q, cache and o_lat; fp32 arithmetic either way).
+template <typename E>
+__global__ __launch_bounds__(256) void decode_row_kernel(DecodeF32Args a) {
   __shared__ float qs[kMaxDk];
   __shared__ float zs[256];
   const int b = blockIdx.x / a.H, h = blockIdx.x % a.H;
   const int W = a.d_c + a.d_r;
   const int Lb = a.seq_len[b];
-  const float* qp = a.q + ((int64_t)b * a.H + h) * W;
+  const E* qp = (const E*)a.q + ((int64_t)b * a.H + h) * W;
   for (int d = threadIdx.x; d < W; d += 256) {
-    float v = qp[d];
+    float v = ld_f(qp + d);
     if (d >= a.d_c && a.rope_base != 0.f) {
       // interleaved pairs (2i, 2i+1), theta_i = base^(-2i/d_r), position Lb-1
       const int col = d - a.d_c, i = col >> 1;
@@ -148,18 +162,18 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeF32Args a) {
       ang -= 6.283185307179586 * floor(ang * 0.15915494309189535);
       float sn, cs;
       sincosf((float)ang, &sn, &cs);
-      const float x0 = qp[a.d_c + 2 * i], x1 = qp[a.d_c + 2 * i + 1];
+      const float x0 = ld_f(qp + a.d_c + 2 * i), x1 = ld_f(qp + a.d_c + 2 * i + 1);
       v = (col & 1) ? (x0 * sn + x1 * cs) : (x0 * cs - x1 * sn);
     }
     qs[d] = v;
   }
   __syncthreads();
-  RowJob j;
+  RowJob<E> j;
   j.q = qs;
-  j.k = a.cache + a.seq_start[b] * W; j.ks = W;
+  j.k = (const E*)a.cache + a.seq_start[b] * W; j.ks = W;
   j.v = j.k; j.vs = W;
   j.n = Lb > 0 ? Lb : 0;
-  j.o = a.o_lat + ((int64_t)b * a.H + h) * a.d_c;
+  j.o = (E*)a.o_lat + ((int64_t)b * a.H + h) * a.d_c;
   j.lse = a.lse ? a.lse + (int64_t)b * a.H + h : nullptr;
   attn_row(j, W, a.d_c, a.scale, qs, zs);
 }
@@ -171,7 +185,14 @@ hipError_t launch_prefill_attn_f32(const AttnF32Args& a, hipStream_t st) {
 
 hipError_t launch_decode_f32(const DecodeF32Args& a, hipStream_t st) {
   if (a.d_c + a.d_r > kMaxDk || a.d_c > kMaxDv) return hipErrorInvalidValue;
-  return launch(decode_f32_kernel, dim3(a.B * a.H), dim3(256), 0, st, a);
+  if ((long long)a.B * a.H > 2147483647LL) return hipErrorInvalidValue;
+  return launch(decode_row_kernel<float>, dim3(a.B * a.H), dim3(256), 0, st, a);
+}
+
+hipError_t launch_decode_generic_bf16(const DecodeF32Args& a, hipStream_t st) {
+  if (a.d_c + a.d_r > kMaxDk || a.d_c > kMaxDv) return hipErrorInvalidValue;
+  if ((long long)a.B * a.H > 2147483647LL) return hipErrorInvalidValue;
+  return launch(decode_row_kernel<bf16>, dim3(a.B * a.H), dim3(256), 0, st, a);
 }
 
 }  // namespace gmla

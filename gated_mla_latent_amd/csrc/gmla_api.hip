@@ -285,7 +285,8 @@ gmla_status_t gmla_prefill(const void* x, const void* W_c, const void* W_dq, con
 // ============================================================ decode
 size_t gmla_decode_workspace_size(int B, int H, int d_c, int num_splits, gmla_dtype_t dtype) {
   if (B <= 0 || H <= 0 || d_c <= 0 || num_splits < 0) return 0;
-  if (dtype == GMLA_F32) return 0;
+  // the fp32 path and the generic bf16 path (d_c != 512) need none
+  if (dtype == GMLA_F32 || d_c != 512) return 0;
   const size_t G = (size_t)decode_slices(num_splits, H);
   const size_t H16 = ((size_t)H + 15) / 16 * 16;  // partial outputs are kept per group of 16 heads
   return up256((size_t)B * 8) + up256(2 * G * H * 4) + up256(2 * G * H16 * (size_t)d_c * 2);
@@ -308,13 +309,25 @@ gmla_status_t gmla_decode(const void* q_abs, const void* cache, const int64_t* s
   if (dtype == GMLA_F32) {
     REQUIRE(d_c + d_r <= 1024 && d_c <= 512, GMLA_ERR_UNSUPPORTED, "fp32 decode needs d_c + d_r <= 1024, d_c <= 512");
     DecodeF32Args a{};
-    a.q = (const float*)q_abs; a.cache = (const float*)cache; a.seq_start = seq_start; a.seq_len = seq_len;
-    a.o_lat = (float*)o_lat; a.lse = lse; a.B = B; a.H = H; a.d_c = d_c; a.d_r = d_r;
+    a.q = q_abs; a.cache = cache; a.seq_start = seq_start; a.seq_len = seq_len;
+    a.o_lat = o_lat; a.lse = lse; a.B = B; a.H = H; a.d_c = d_c; a.d_r = d_r;
     a.scale = sm_scale; a.rope_base = d_r > 0 ? rope_base : 0.f;
     gmla_status_t s = run("decode_f32", st, [&] { return launch_decode_f32(a, st); });
     return s ? s : ok();
   }
-  REQUIRE(decode_bf16_supported(d_c, d_r), GMLA_ERR_UNSUPPORTED, "bf16 decode needs d_c == 512 and d_r in {0, 64}");
+  if (!decode_bf16_supported(d_c, d_r)) {
+    // latent and RoPE widths outside the MFMA kernel's: the generic bf16
+    // decode (one workgroup per sequence and head, no workspace)
+    REQUIRE(d_c % 64 == 0 && d_c <= 512 && d_c + d_r <= 1024, GMLA_ERR_UNSUPPORTED,
+            "bf16 decode needs d_c % 64 == 0, d_c <= 512 and d_c + d_r <= 1024");
+    REQUIRE((long long)B * H <= INT_MAX, GMLA_ERR_UNSUPPORTED, "B * H must not exceed INT_MAX");
+    DecodeF32Args a{};
+    a.q = q_abs; a.cache = cache; a.seq_start = seq_start; a.seq_len = seq_len;
+    a.o_lat = o_lat; a.lse = lse; a.B = B; a.H = H; a.d_c = d_c; a.d_r = d_r;
+    a.scale = sm_scale; a.rope_base = d_r > 0 ? rope_base : 0.f;
+    gmla_status_t s = run("decode_generic", st, [&] { return launch_decode_generic_bf16(a, st); });
+    return s ? s : ok();
+  }
   const int G = decode_slices(num_splits, H);
   const size_t need = gmla_decode_workspace_size(B, H, d_c, num_splits, dtype);
   REQUIRE(workspace && workspace_bytes >= need, GMLA_ERR_WORKSPACE,

@@ -185,12 +185,16 @@ struct AttnF32Args {
   float scale;
 };
 hipError_t launch_prefill_attn_f32(const AttnF32Args& a, hipStream_t st);
+// one workgroup per (sequence, head); q, cache and o_lat are fp32
+// (launch_decode_f32) or bf16 (launch_decode_generic_bf16: latent and RoPE
+// widths outside the MFMA decode kernel's), fp32 arithmetic either way
 struct DecodeF32Args {
-  const float* q; const float* cache; const int64_t* seq_start; const int32_t* seq_len;
-  float* o_lat; float* lse;
+  const void* q; const void* cache; const int64_t* seq_start; const int32_t* seq_len;
+  void* o_lat; float* lse;
   int B, H, d_c, d_r;
   float scale, rope_base;
 };
 hipError_t launch_decode_f32(const DecodeF32Args& a, hipStream_t st);
+hipError_t launch_decode_generic_bf16(const DecodeF32Args& a, hipStream_t st);
 
 }  // namespace gmla

@@ -118,9 +118,13 @@ gmla_status_t gmla_prefill(const void* x, const void* W_c, const void* W_dq, con
  * units / workgroups per slice, rounded down to a multiple of 8. F32 runs
  * one workgroup per sequence and head and ignores it.
  * The result does not depend on it beyond fp32 rounding.
- * BF16 needs d_c == 512 and d_r in {0, 64}; F32 needs
- * d_c + d_r <= 1024 and d_c <= 512.
+ * BF16 with d_c == 512 and d_r in {0, 64} runs the MFMA kernel described
+ * above; every other BF16 width with d_c % 64 == 0, d_c <= 512 and
+ * d_c + d_r <= 1024 runs a generic kernel (one workgroup per sequence and
+ * head, fp32 arithmetic, no workspace; num_splits ignored), as does F32
+ * (d_c + d_r <= 1024, d_c <= 512). GMLA_ERR_UNSUPPORTED otherwise.
  * ---------------------------------------------------------------------- */
+/* Workspace bytes: 0 for F32 and for BF16 with d_c != 512. */
 size_t gmla_decode_workspace_size(int B, int H, int d_c, int num_splits, gmla_dtype_t dtype);
 gmla_status_t gmla_decode(const void* q_abs, const void* cache, const int64_t* seq_start, const int32_t* seq_len,
                           void* o_lat, float* lse, void* workspace, size_t workspace_bytes, int B, int H, int d_c,

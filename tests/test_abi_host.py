@@ -58,9 +58,9 @@ def test_decode_argument_checks(L):
     assert _dec(L, scale=float("nan")) == INVALID
     assert _dec(L, base=-1.0) == INVALID
     assert _dec(L, dt=7) == INVALID
-    assert _dec(L, d_c=384) == UNSUPPORTED          # bf16 kernels take d_c == 512
-    assert _dec(L, d_c=256) == UNSUPPORTED
-    assert _dec(L, d_r=32) == UNSUPPORTED
+    assert _dec(L, d_c=96) == UNSUPPORTED           # bf16 latent widths are multiples of 64 ...
+    assert _dec(L, d_c=576) == UNSUPPORTED          # ... up to 512
+    assert _dec(L, d_c=512, d_r=600) == UNSUPPORTED  # d_c + d_r <= 1024
     assert _dec(L, wsb=16) == WORKSPACE
     assert _dec(L, ws=0) == WORKSPACE
     assert b"workspace" in L.gmla_last_error()
@@ -85,6 +85,7 @@ def test_decode_workspace_size_formula(L):
     # partial outputs are padded to whole groups of 16 heads
     assert L.gmla_decode_workspace_size(B, 20, d_c, G, 1) == up(B * 8) + up(2 * G * 20 * 4) + up(2 * G * 32 * d_c * 2)
     assert L.gmla_decode_workspace_size(B, H, d_c, G, 0) == 0  # fp32 path needs none
+    assert L.gmla_decode_workspace_size(B, H, 256, G, 1) == 0  # nor the generic bf16 path
     assert L.gmla_decode_workspace_size(0, H, d_c, G, 1) == 0
 
 

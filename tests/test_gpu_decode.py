@@ -51,20 +51,22 @@ def test_decode_ragged_matches_oracle(H, d_c, d_r):
     _check(inp, o, lse)
 
 
-@pytest.mark.skip(reason="the bf16 decode kernel for d_c = 256 faulted on the GPU (cause not found); "
-                         "the d_c in {128, 256} paths are switched off and return GMLA_ERR_UNSUPPORTED")
-@pytest.mark.parametrize("d_c,d_r", [(256, 0), (256, 64), (128, 0)])
-def test_decode_narrow_latent_widths(d_c, d_r):
-    inp = W.make_decode(len(RAGGED), 64, d_c, d_r, 0, lengths=RAGGED, seed=11, name="narrow")
+@pytest.mark.parametrize("d_c,d_r", [(256, 0), (256, 64), (128, 0), (64, 64), (384, 64), (512, 32)])
+def test_decode_other_latent_widths(d_c, d_r):
+    """Latent and RoPE widths outside the MFMA kernel's (d_c = 512 with
+    d_r in {0, 64}) run the generic bf16 decode."""
+    say(f"[decode generic] d_c={d_c} d_r={d_r}")
+    inp = W.make_decode(len(RAGGED), 64, d_c, d_r, 0, lengths=RAGGED, seed=11, name="generic")
     o, lse = _run(inp)
     _check(inp, o, lse)
 
 
-def test_decode_narrow_latent_widths_are_rejected():
-    inp = W.make_decode(2, 64, 256, 0, 5, 9, seed=1)
-    with pytest.raises(ops.GmlaError) as e:
-        _run(inp)
-    assert e.value.status == 2
+def test_decode_unsupported_latent_widths_are_rejected():
+    for d_c, d_r in [(96, 0), (576, 0), (512, 600)]:
+        inp = W.make_decode(2, 8, d_c, d_r, 5, 9, seed=1)
+        with pytest.raises(ops.GmlaError) as e:
+            _run(inp)
+        assert e.value.status == 2
 
 
 @pytest.mark.parametrize("num_splits", [1, 2, 7, 36, 64, 0])
