@@ -559,9 +559,12 @@ def run_workload(name, args, torch, ops, W, peaks):
                     "config": {"workload": desc, "batch": inp.B, "seq_len": inp.L, "heads": inp.H,
                                "gflop_per_step": total / 1e9, "input_copies": args.copies},
                     "step_peak_frac": total / (ms_step * 1e-3) / 1e12 / peak})
+        # the projections of x may run as one grouped launch (gemm_input)
+        kfl = dict(fl, gemm_input=sum(fl.get(k, 0) for k in ("gemm_latent", "gemm_query", "gemm_rope_key",
+                                                              "gemm_rope_query")))
         for k, v in kern.items():
-            if k in fl:
-                v["tflops"] = fl[k] / (v["avg_us"] * 1e-6) / 1e12
+            if k in kfl:
+                v["tflops"] = kfl[k] / (v["avg_us"] * 1e-6) / 1e12
         # the roofline kernel: the causal attention, one launch per step
         # (every GEMM of the step is listed under kernels with its TFLOP/s)
         rk = "prefill_attn_f32" if f32 else "prefill_attn"

@@ -256,16 +256,21 @@ constexpr int RS = (BN / 2) * 4 + 16; // epilogue row stride (fp32, half the col
 static_assert(BM * RS <= LDS, "epilogue tile fits in the ring");
 }  // namespace big
 
+// Up to four GEMMs that share A, M and K run as one grid (GemmGroup): the
+// n-tiles of the segments sit side by side, each workgroup takes its
+// segment's weight, output, widths and strides. A single GEMM is a group of
+// one (with npad: its zero columns).
 template <int EPI>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void gemm_big_kernel(GemmArgs g) {
+void gemm_big_kernel(GemmGroup gg) {
   using namespace big;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave & 1, wm = wave >> 1;
-  const int tiles_n = (c_cols<EPI>(g) + BN - 1) / BN, tiles_m = (g.M + BM - 1) / BM;
+  GemmArgs g = gg.base;
+  const int tiles_n = gg.tiles_n, tiles_m = (g.M + BM - 1) / BM;
   const int total = tiles_n * tiles_m;
   // XCD-contiguous tile ranges, then groups of 4 m-tiles (as gemm_tile)
   int pid = blockIdx.x;
@@ -277,7 +282,17 @@ void gemm_big_kernel(GemmArgs g) {
   const int gm = (tiles_m - first_m) < GROUP ? (tiles_m - first_m) : GROUP;
   const int tile_m = first_m + (pid % group_size) % gm;
   const int tile_n = (pid % group_size) / gm;
-  const int n0 = tile_n * BN, m0 = tile_m * BM;
+  // this n-tile's segment (unused segments start at INT32_MAX)
+  const int seg = (tile_n >= gg.first_wg[1]) + (tile_n >= gg.first_wg[2]) + (tile_n >= gg.first_wg[3]);
+  const int seg_first = seg == 0 ? 0 : seg == 1 ? gg.first_wg[1] : seg == 2 ? gg.first_wg[2] : gg.first_wg[3];
+  if (gg.count > 1) {
+    g.W = seg == 0 ? gg.W[0] : seg == 1 ? gg.W[1] : seg == 2 ? gg.W[2] : gg.W[3];
+    g.C = seg == 0 ? gg.C[0] : seg == 1 ? gg.C[1] : seg == 2 ? gg.C[2] : gg.C[3];
+    g.N = seg == 0 ? gg.N[0] : seg == 1 ? gg.N[1] : seg == 2 ? gg.N[2] : gg.N[3];
+    g.ldw = seg == 0 ? gg.ldw[0] : seg == 1 ? gg.ldw[1] : seg == 2 ? gg.ldw[2] : gg.ldw[3];
+    g.ldc = seg == 0 ? gg.ldc[0] : seg == 1 ? gg.ldc[1] : seg == 2 ? gg.ldc[2] : gg.ldc[3];
+  }
+  const int n0 = (tile_n - seg_first) * BN, m0 = tile_m * BM;
   const int batch = blockIdx.y;
   const bf16* A = g.A + batch * g.sA;
   const bf16* W = g.W + batch * g.sW;
@@ -699,23 +714,60 @@ static hipError_t launch_tile(const GemmArgs& g, hipStream_t st) {
 // The big-tile kernel addresses its operands with 32-bit buffer offsets:
 // every row start of a batch's A and W (plus a tile of rows past the end,
 // which read as zeros) and the descriptor sizes must stay below 2^31.
+static bool big_fits_rows(long long rows, long long ld, long long K) {
+  const long long lim = 1LL << 31;
+  return (rows + 256) * ld * 2 < lim && ((rows - 1) * ld + K) * 2 < lim;
+}
 template <int EPI>
 static bool big_fits(const GemmArgs& g) {
-  const long long lim = 1LL << 31;
-  return ((long long)g.N + big::BN) * g.ldw * 2 < lim && ((long long)g.M + big::BM) * g.lda * 2 < lim &&
-         ((long long)(g.N - 1) * g.ldw + g.K) * 2 < lim && ((long long)(g.M - 1) * g.lda + g.K) * 2 < lim;
+  return big_fits_rows(g.N, g.ldw, g.K) && big_fits_rows(g.M, g.lda, g.K);
 }
 
 template <int EPI>
-static hipError_t launch_big(const GemmArgs& g, hipStream_t st) {
+static hipError_t launch_big_group(const GemmGroup& gg, hipStream_t st) {
   auto kern = gemm_big_kernel<EPI>;
   {
     hipError_t e = lds_opt_in((const void*)kern, big::LDS);
     if (e != hipSuccess) return e;
   }
+  const int tiles = gg.tiles_n * ((gg.base.M + big::BM - 1) / big::BM);
+  return launch(kern, dim3(tiles, gg.base.batches), dim3(256), big::LDS, st, gg);
+}
+
+template <int EPI>
+static hipError_t launch_big(const GemmArgs& g, hipStream_t st) {
+  GemmGroup gg{};
+  gg.base = g;
+  gg.count = 1;
+  gg.W[0] = g.W; gg.C[0] = g.C; gg.N[0] = g.N; gg.ldw[0] = g.ldw; gg.ldc[0] = g.ldc;
+  gg.first_wg[0] = 0;
+  gg.first_wg[1] = gg.first_wg[2] = gg.first_wg[3] = INT32_MAX;
   const int ncols = (EPI == EPI_STORE && g.npad > g.N) ? g.npad : g.N;
-  const int tiles = ((ncols + big::BN - 1) / big::BN) * ((g.M + big::BM - 1) / big::BM);
-  return launch(kern, dim3(tiles, g.batches), dim3(256), big::LDS, st, g);
+  gg.tiles_n = (ncols + big::BN - 1) / big::BN;
+  return launch_big_group<EPI>(gg, st);
+}
+
+hipError_t launch_gemm_group_big(GemmGroup gg, hipStream_t st) {
+  const GemmArgs& b = gg.base;
+  if (gg.count < 1 || gg.count > 4 || b.M <= 0 || b.K % 64 != 0 || b.K < 2048) return hipErrorNotSupported;
+  if (!big_fits_rows(b.M, b.lda, b.K)) return hipErrorNotSupported;
+  int tiles_n = 0;
+  for (int s = 0; s < 4; ++s) {
+    if (s < gg.count) {
+      if (gg.N[s] <= 0 || gg.N[s] % 4 != 0 || !big_fits_rows(gg.N[s], gg.ldw[s], b.K)) return hipErrorNotSupported;
+      gg.first_wg[s] = tiles_n;
+      tiles_n += (gg.N[s] + big::BN - 1) / big::BN;
+    } else {
+      gg.first_wg[s] = INT32_MAX;
+    }
+  }
+  if ((long long)tiles_n * ((b.M + big::BM - 1) / big::BM) < 256) return hipErrorNotSupported;
+  gg.tiles_n = tiles_n;
+  gg.base.batches = 1;
+  gg.base.epi = EPI_STORE;
+  gg.base.npad = 0;
+  gg.base.sA = gg.base.sW = gg.base.sC = 0;
+  return launch_big_group<EPI_STORE>(gg, st);
 }
 
 static bool skinny_path(int M, int N, int npad) { return M <= 64 && !(npad > N); }

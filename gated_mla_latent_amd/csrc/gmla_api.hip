@@ -221,18 +221,50 @@ gmla_status_t gmla_prefill(const void* x, const void* W_c, const void* W_dq, con
   const int CW = d_c + d_r;  // cache row width: [c ; RoPE key]
   gmla_status_t s;
   if (dtype == GMLA_BF16) {
-    // c = x W_c^T (cache rows), q = x W_q^T, K = c W_UK^T, V = c W_UV^T (W_UK as [H*d_k, d_c])
-    if ((s = run("gemm_latent", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_c, d_model, latent_out, CW, T, d_c, d_model), st); }))) return s;
-    if (d_cq > 0 &&
-        (s = run("gemm_query_down", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_dq, d_model, cq, d_cq, T, d_cq, d_model), st); })))
-      return s;
-    if ((s = run("gemm_query", st, [&] { return launch_gemm_bf16(gemm(xq, dq_in, W_q, dq_in, q, HK, T, HK, dq_in), st); }))) return s;
+    // c = x W_c^T (cache rows), q = x W_q^T, K = c W_UK^T, V = c W_UV^T (W_UK as [H*d_k, d_c]);
+    // with RoPE also k^R = x W_kr^T into the cache rows' tail and q^R = u W_qr^T.
+    // The projections that read x go out as one grid on the 256 x 256 tile
+    // kernel when the shape qualifies (the latent, 512 wide, then rides on
+    // the query's waves instead of a grid of its own); else one by one.
+    GemmGroup gx{};
+    gx.base = gemm(x, d_model, nullptr, d_model, nullptr, 0, T, 0, d_model);
+    auto add = [&](const void* Wt, void* Ct, int n, int64_t ldc) {
+      gx.W[gx.count] = (const bf16*)Wt; gx.C[gx.count] = (bf16*)Ct; gx.N[gx.count] = n;
+      gx.ldw[gx.count] = d_model; gx.ldc[gx.count] = ldc; ++gx.count;
+    };
+    add(W_c, latent_out, d_c, CW);
+    if (d_r > 0) add(W_kr, (bf16*)latent_out + d_c, d_r, CW);
+    if (d_cq > 0) add(W_dq, cq, d_cq, d_cq);
+    else {
+      add(W_q, q, HK, HK);
+      if (d_r > 0) add(W_qr, qr, H * d_r, (int64_t)H * d_r);
+    }
+    bool grouped = false;
+    {
+      const int tr = trace_pre("gemm_input", st);
+      const hipError_t e = launch_gemm_group_big(gx, st);
+      trace_post(tr, st);
+      if (e == hipSuccess) grouped = true;
+      else if (e != hipErrorNotSupported) return fail(GMLA_ERR_HIP, std::string("gemm_input: ") + hipGetErrorString(e));
+      else (void)hipGetLastError();
+    }
+    if (!grouped) {
+      if ((s = run("gemm_latent", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_c, d_model, latent_out, CW, T, d_c, d_model), st); }))) return s;
+      if (d_cq > 0 &&
+          (s = run("gemm_query_down", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_dq, d_model, cq, d_cq, T, d_cq, d_model), st); })))
+        return s;
+      if (d_r > 0 &&
+          (s = run("gemm_rope_key", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_kr, d_model, (bf16*)latent_out + d_c, CW, T, d_r, d_model), st); })))
+        return s;
+    }
+    if (!grouped || d_cq > 0) {
+      if ((s = run("gemm_query", st, [&] { return launch_gemm_bf16(gemm(xq, dq_in, W_q, dq_in, q, HK, T, HK, dq_in), st); }))) return s;
+      if (d_r > 0 &&
+          (s = run("gemm_rope_query", st, [&] { return launch_gemm_bf16(gemm(xq, dq_in, W_qr, dq_in, qr, (int64_t)H * d_r, T, H * d_r, dq_in), st); })))
+        return s;
+    }
     if (d_r > 0) {
-      // k^R = RoPE(x W_kr^T, s) into the cache rows' tail; q^R = RoPE(u W_qr^T, t)
-      if ((s = run("gemm_rope_key", st, [&] { return launch_gemm_bf16(gemm(x, d_model, W_kr, d_model, (bf16*)latent_out + d_c, CW, T, d_r, d_model), st); })))
-        return s;
-      if ((s = run("gemm_rope_query", st, [&] { return launch_gemm_bf16(gemm(xq, dq_in, W_qr, dq_in, qr, (int64_t)H * d_r, T, H * d_r, dq_in), st); })))
-        return s;
+      // k^R = RoPE(x W_kr^T, s) in the cache rows' tail, q^R = RoPE(u W_qr^T, t), in place
       RopeRowsArgs rk{(bf16*)latent_out + d_c, CW, T, 1, d_r, L, rope_base};
       RopeRowsArgs rq{(bf16*)qr, (int64_t)H * d_r, T, H, d_r, L, rope_base};
       if ((s = run("rope_rows", st, [&] { return launch_rope_rows(rk, st); }))) return s;

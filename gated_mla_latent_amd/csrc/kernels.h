@@ -146,10 +146,16 @@ struct GemmGroup {
   bf16* C[4];
   int N[4];
   int64_t ldw[4], ldc[4];
-  int first_wg[4];
+  int first_wg[4];   // first workgroup (skinny) or first n-tile (big tiles) of each segment
   int count;
+  int tiles_n;       // big tiles: n-tiles over all segments (set by the launcher)
 };
 hipError_t launch_gemm_group_bf16(GemmGroup gg, hipStream_t st);
+// The same with M >= 65 on the 256 x 256 tile kernel, when it applies (grid
+// of >= 256 tiles, K >= 2048, 32-bit offsets): one launch whose n-tiles run
+// over the segments side by side. Returns hipErrorNotSupported (and
+// launches nothing) when the shape does not qualify.
+hipError_t launch_gemm_group_big(GemmGroup gg, hipStream_t st);
 
 // ---------------------------------------------------------------- prefill attention
 // Causal flash attention, one head per (b, h): q,k,v rows of width D.
