@@ -397,9 +397,27 @@ void gemm_big_kernel(GemmGroup gg) {
   }
 
   // Epilogue through LDS, one column half (BN/2) at a time, as gemm_tile.
+  // The gate's O values of both halves are loaded first, into the registers
+  // the operand staging no longer needs, so their latency overlaps the
+  // staging of the accumulators instead of following it.
   LDS_AS float* ct = (LDS_AS float*)smem;
   const bool vec16 = g.ldc % 8 == 0 && g.sC % 8 == 0 && (EPI != EPI_GATE || (g.ldo % 8 == 0 && g.sO % 8 == 0));
   constexpr int HN = BN / 2;
+  constexpr int ITEMS = BM * HN / 8;      // 8 columns per item
+  constexpr int IPT = ITEMS / 256;        // items per thread and half
+  const int ncols = c_cols<EPI>(g);
+  u32x4 ov[2][IPT];
+  if constexpr (EPI == EPI_GATE) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int k = 0; k < IPT; ++k) {
+        const int it = tid + 256 * k;
+        const int m = m0 + it / (HN / 8), n = n0 + half * HN + (it % (HN / 8)) * 8;
+        ov[half][k] = (vec16 && m < g.M && n + 8 <= ncols) ? *(const u32x4*)(Op + (int64_t)m * g.ldo + n)
+                                                           : u32x4{0u, 0u, 0u, 0u};
+      }
+  }
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     lds_barrier();
@@ -418,10 +436,9 @@ void gemm_big_kernel(GemmGroup gg) {
         }
     }
     lds_barrier();
-    constexpr int ITEMS = BM * HN / 8;  // 8 columns per item
-    const int ncols = c_cols<EPI>(g);
 #pragma unroll
-    for (int it = tid; it < ITEMS; it += 256) {
+    for (int k = 0; k < IPT; ++k) {
+      const int it = tid + 256 * k;
       const int ml = it / (HN / 8), nl = (it % (HN / 8)) * 8;
       const int m = m0 + ml, n = n0 + half * HN + nl;
       if (m >= g.M || n >= ncols) continue;
@@ -434,11 +451,10 @@ void gemm_big_kernel(GemmGroup gg) {
       }
       if (vec16 && n + 8 <= ncols) {
         if constexpr (EPI == EPI_GATE) {
-          const u32x4 ov = *(const u32x4*)(Op + (int64_t)m * g.ldo + n);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            v[2 * e] = sigmoidf_fast(v[2 * e]) * bf16_bits_to_f32((unsigned short)(ov[e] & 0xffff));
-            v[2 * e + 1] = sigmoidf_fast(v[2 * e + 1]) * bf16_bits_to_f32((unsigned short)(ov[e] >> 16));
+            v[2 * e] = sigmoidf_fast(v[2 * e]) * bf16_bits_to_f32((unsigned short)(ov[half][k][e] & 0xffff));
+            v[2 * e + 1] = sigmoidf_fast(v[2 * e + 1]) * bf16_bits_to_f32((unsigned short)(ov[half][k][e] >> 16));
           }
         }
         *(u32x4*)(Cp + (int64_t)m * g.ldc + n) =
