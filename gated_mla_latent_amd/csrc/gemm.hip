@@ -26,6 +26,10 @@
 //    wave, no barrier in the loop), partial sums meet in LDS. A grid of
 //    fewer than 512 workgroups (narrow N) also splits K across workgroups:
 //    fp32 partial sums, then gemm_splitk_reduce applies the epilogue.
+//  * gemm_skinny_shared: 33..64 rows where 64-column workgroups would not
+//    fill the grid: a workgroup owns 128 columns and shares each activation
+//    chunk among its 4 waves (a quarter of the activation bytes per weight
+//    byte), 256-byte row pieces, K split across workgroups.
 #include "common.h"
 #include "kernels.h"
 
@@ -628,6 +632,130 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& g, int n0, int cw, i
   }
 }
 
+// ----------------------------------------------------------------------------
+// Skinny GEMM, 33..64 rows, with the activation chunk shared by the
+// workgroup. A workgroup owns 128 output columns (wave w: columns 32 w ..
+// 32 w + 31) and one K slice; its 4 waves walk the slice's 128-wide chunks
+// together, each chunk one ring stage: the 128 weight rows (each wave DMAs
+// its own 32) and the 32 MT activation rows (a quarter per wave), 256 bytes
+// per row, with one barrier per stage. Sharing the activation chunk cuts
+// the activation bytes per weight byte from M / 32 to M / 128, and the
+// 256-byte row pieces stream faster than 128-byte ones. K is split across
+// workgroups to fill the grid; fp32 partial sums go to the split-K reduce.
+// Rows are 256 bytes; 16-byte piece p of row r sits at p ^ (r % 16).
+template <int MT>
+struct SharedCfg {
+  static constexpr int KB = 128, ROWB = 256;
+  static constexpr int W_BYTES = 128 * ROWB;
+  static constexpr int A_BYTES = MT * 32 * ROWB;
+  static constexpr int STAGE = W_BYTES + A_BYTES;
+  static constexpr int NST = 163840 / STAGE;
+  static constexpr int LDS_BYTES = NST * STAGE;
+  static constexpr int WI = 8;           // weight DMA instructions per wave and stage
+  static constexpr int AI = 2 * MT;      // activation DMA instructions per wave and stage
+  static constexpr int IPS = WI + AI;
+  static_assert(NST >= 3 && NST <= 4, "ring of 3 or 4 stages");
+  static_assert((NST - 2) * IPS < 64, "vmcnt range");
+};
+
+template <int MT, int EPI>
+__global__ __launch_bounds__(256) void gemm_skinny_shared_kernel(GemmArgs g) {
+  using C = SharedCfg<MT>;
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  LDS_AS char* smem = (LDS_AS char*)smem_raw;
+  const unsigned smem_base = (unsigned)(uintptr_t)smem;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = blockIdx.x * 128;
+  const int batch = blockIdx.y, zi = blockIdx.z, nz = gridDim.z;
+  const bf16* A = g.A + batch * g.sA;
+  const bf16* W = g.W + batch * g.sW;
+  bf16* Cp = g.C + batch * g.sC;
+  const bf16* Op = (EPI == EPI_GATE) ? g.O + batch * g.sO : nullptr;
+  const int all_chunks = g.K / C::KB;
+  const int per = (all_chunks + nz - 1) / nz;
+  const int c_lo = zi * per;
+  const int c_hi = (c_lo + per) < all_chunks ? (c_lo + per) : all_chunks;
+  const int n = c_hi > c_lo ? c_hi - c_lo : 0;
+
+  // DMA: instruction q of a wave moves 4 rows of 256 bytes; lane l writes
+  // physical piece l % 16 of row 4 q + l / 16, i.e. logical piece
+  // (l % 16) ^ (row % 16) of that row
+  const int lr = lane >> 4, lp = lane & 15;
+  auto issue = [&](int st, int j) {
+    const unsigned dst = smem_base + st * C::STAGE;
+    const unsigned long long wbase = (unsigned long long)(uintptr_t)(W + (int64_t)j * C::KB);
+#pragma unroll
+    for (int q = 0; q < C::WI; ++q) {
+      const int trow = 32 * wave + 4 * q + lr;  // row of the weight tile
+      int row = n0 + trow;
+      row = row < g.N ? row : g.N - 1;
+      g2lds16_s(wbase, (unsigned)(row * g.ldw * 2 + ((lp ^ (trow & 15)) << 4)), dst + (8 * wave + q) * 1024);
+    }
+    const unsigned long long abase = (unsigned long long)(uintptr_t)(A + (int64_t)j * C::KB);
+#pragma unroll
+    for (int q = 0; q < C::AI; ++q) {
+      const int trow = 4 * (C::AI * wave + q) + lr;  // row of the activation tile
+      const int row = trow < g.M ? trow : g.M - 1;
+      g2lds16_s(abase, (unsigned)(row * g.lda * 2 + ((lp ^ (trow & 15)) << 4)),
+                dst + C::W_BYTES + (C::AI * wave + q) * 1024);
+    }
+  };
+  auto frag = [&](const LDS_AS char* tile, int r, int p) -> bf16x8 {
+    return as_bf16x8(lds_read16(tile + r * C::ROWB + ((p ^ (r & 15)) << 4)));
+  };
+
+  floatx16 acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = floatx16{};
+  const int r32 = lane & 31, hk = lane >> 5;
+#pragma unroll
+  for (int s = 0; s < C::NST - 1; ++s)
+    if (s < n) issue(s, c_lo + s);
+  for (int i = 0; i < n; ++i) {
+    // stage i has landed once at most min(NST - 2, n - 1 - i) later stages
+    // of this wave are in flight; the barrier then makes every wave's share
+    // of it visible, and frees the stage of chunk i - 1 for chunk i + NST - 1
+    const int later = (n - 1 - i) < C::NST - 2 ? (n - 1 - i) : C::NST - 2;
+    if constexpr (C::NST == 4) {
+      if (later >= 2) wait_vmcnt<2 * C::IPS>();
+      else if (later == 1) wait_vmcnt<C::IPS>();
+      else wait_vmcnt<0>();
+    } else {
+      if (later >= 1) wait_vmcnt<C::IPS>();
+      else wait_vmcnt<0>();
+    }
+    lds_barrier();
+    if (i + C::NST - 1 < n) issue((i + C::NST - 1) % C::NST, c_lo + i + C::NST - 1);
+    const LDS_AS char* wt = smem + (i % C::NST) * C::STAGE;
+    const LDS_AS char* at = wt + C::W_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < C::KB / 16; ++kk) {
+      const bf16x8 wf = frag(wt, 32 * wave + r32, 2 * kk + hk);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[t] = mfma32(wf, frag(at, 32 * t + r32, 2 * kk + hk), acc[t]);
+    }
+  }
+  // register r of lane l: output row m = 32 t + l % 32, column
+  // n0 + 32 wave + 8 (r / 4) + 4 (l / 32) + r % 4
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int m = 32 * t + r32;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int col = n0 + 32 * wave + 8 * r4 + 4 * hk;
+      const float v0 = acc[t][4 * r4], v1 = acc[t][4 * r4 + 1], v2 = acc[t][4 * r4 + 2], v3 = acc[t][4 * r4 + 3];
+      if (nz > 1) {
+        const int ldp = (g.N + 3) & ~3;
+        if (m < g.M && col < g.N)
+          *(float4*)(g.part + (((int64_t)zi * g.batches + batch) * g.M + m) * ldp + col) = make_float4(v0, v1, v2, v3);
+      } else {
+        store4<EPI>(g, Cp, Op, m, col, v0, v1, v2, v3);
+      }
+    }
+  }
+}
+
 template <int MT, int NT, int EPI>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
   skinny_body<MT, NT, EPI>(g, blockIdx.x * g.cw, g.cw, blockIdx.y, blockIdx.z, gridDim.z);
@@ -713,6 +841,22 @@ static hipError_t launch_skinny(const GemmArgs& g, hipStream_t st) {
 
 
 // ----------------------------------------------------------------------------
+template <int EPI>
+static hipError_t launch_shared(const GemmArgs& g, hipStream_t st) {
+  using C = SharedCfg<2>;
+  auto kern = gemm_skinny_shared_kernel<2, EPI>;
+  {
+    hipError_t e = lds_opt_in((const void*)kern, C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+  }
+  const int z = g.ksplit > 1 ? g.ksplit : 1;
+  if (z > 1 && !g.part) return hipErrorInvalidValue;
+  hipError_t e = launch(kern, dim3((g.N + 127) / 128, g.batches, z), dim3(256), C::LDS_BYTES, st, g);
+  if (e != hipSuccess || z == 1) return e;
+  const int64_t n4 = (int64_t)g.batches * g.M * (((g.N + 3) & ~3) / 4);  // output quads, 8 threads each
+  return launch(gemm_splitk_reduce_kernel<EPI>, dim3((unsigned)((8 * n4 + 255) / 256)), dim3(256), 0, st, g);
+}
+
 template <int BN, int BM, int EPI>
 static hipError_t launch_tile(const GemmArgs& g, hipStream_t st) {
   constexpr int RING = 2 * (BN + BM) * 64 * 2, EPIL = BM * ((BN / 2) * 4 + 16);
@@ -788,6 +932,28 @@ hipError_t launch_gemm_group_big(GemmGroup gg, hipStream_t st) {
 
 static bool skinny_path(int M, int N, int npad) { return M <= 64 && !(npad > N); }
 
+// 33..64 rows over long K, where 64-column workgroups would not give one per
+// compute unit: the shared-activation form, K split to fill the grid. It
+// took W_o at 64 rows, 7168 x 16384, from 58.5 to 50.6 us (with the split-K
+// reduce); at 32 rows or fewer, and where 64-column workgroups fill the
+// grid, it measured slower than the per-wave rings.
+static bool shared_path(int M, int N, int K, int batches) {
+  if (M <= 32 || M > 64 || K % 128 != 0 || K < 2048) return false;
+  const long long groups = (long long)((N + 127) / 128) * batches;
+  // at least 32 workgroups before the split (narrow products keep the
+  // per-wave form, whose split reaches more workgroups)
+  return groups >= 32 && (long long)((N + 63) / 64) * batches < 256;
+}
+static int shared_split(int N, int K, int batches) {
+  const long long groups = (long long)((N + 127) / 128) * batches;
+  int z = (int)(256 / groups);
+  const int most = K / 128 / 8;  // at least 8 chunks per slice
+  z = z < most ? z : most;
+  if (z <= 1) return 1;
+  const int per = (K / 128 + z - 1) / z;  // no empty slice
+  return (K / 128 + per - 1) / per;
+}
+
 // Columns per skinny workgroup. With up to 32 rows the kernel streams
 // weight rows at one workgroup per compute unit, so its time follows the
 // rows the busiest unit streams: (columns per workgroup) x (rounds of the
@@ -825,6 +991,7 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
     // the DMA offsets are 32-bit: every row start must be below 4 GiB
     if ((long long)g.N * g.ldw * 2 >= (1LL << 32) || (long long)g.M * g.lda * 2 >= (1LL << 32))
       return hipErrorInvalidValue;
+    if (shared_path(g.M, g.N, g.K, g.batches)) return launch_shared<EPI>(g, st);
     GemmArgs h = g;
     if (g.ksplit > 1) {
       h.cw = 32;
@@ -851,6 +1018,7 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
 // workgroup (one per wave).
 int gemm_ksplit(int M, int N, int K, int batches, int npad) {
   if (M <= 0 || N <= 0 || K <= 0 || batches <= 0 || !skinny_path(M, N, npad)) return 1;
+  if (shared_path(M, N, K, batches)) return shared_split(N, K, batches);
   const long long wgs = (long long)((N + 31) / 32) * batches;
   if (wgs >= 64) return 1;
   const int want = (int)((256 + wgs - 1) / wgs);

@@ -176,11 +176,25 @@ def test_decode_prepare_argument_checks(L):
 
 
 def _ksplit(M, N, K, batches):
-    """The documented split-K rule of the skinny GEMM (M <= 64): split when the
-    grid has fewer than 64 workgroups of 32 columns, towards 256 workgroups,
-    keeping at least four 64-wide K chunks per workgroup and no empty slice."""
+    """The documented split-K rule of the skinny GEMM (M <= 64).
+    33..64 rows with K a multiple of 128, K >= 2048, at least 32 workgroups
+    of 128 columns and fewer than 256 of 64 columns take the
+    shared-activation form: workgroups of 128 columns, split towards 256
+    workgroups with at least eight 128-wide K chunks per slice. Otherwise:
+    split when the grid has fewer than 64 workgroups of 32 columns, towards
+    256 workgroups, keeping at least four 64-wide K chunks per workgroup.
+    Never an empty slice."""
+    if M > 64:
+        return 1
+    groups = -(-N // 128) * batches
+    if 32 < M and K % 128 == 0 and K >= 2048 and groups >= 32 and -(-N // 64) * batches < 256:
+        z = min(256 // groups, K // 128 // 8)
+        if z <= 1:
+            return 1
+        per = -(-(K // 128) // z)
+        return -(-(K // 128) // per)
     wgs = (N + 31) // 32 * batches
-    if M > 64 or wgs >= 64:
+    if wgs >= 64:
         return 1
     z = min(-(-256 // wgs), K // 64 // 4)
     if z <= 1:
@@ -195,12 +209,14 @@ def _part(M, N, K, batches=1):
 
 
 def test_split_k_rule_examples():
-    assert _ksplit(64, 512, 7168, 1) == 16      # 16 workgroups -> 256
-    assert _ksplit(64, 128, 7168, 1) == 28      # 4 workgroups, capped at 4 chunks each
+    assert _ksplit(64, 512, 7168, 1) == 16      # narrow: 16 workgroups of 32 columns -> 256
+    assert _ksplit(64, 128, 7168, 1) == 28      # 4 workgroups, capped at 4 chunks of 64 each
     assert _ksplit(64, 64, 7168, 1) == 28
-    assert _ksplit(64, 16384, 7168, 1) == 1     # 512 workgroups already
-    assert _ksplit(64, 7168, 16384, 1) == 1     # 224: not split
-    assert _ksplit(64, 128, 512, 128) == 1      # batched value up-projection: 512
+    assert _ksplit(64, 4096, 7168, 1) == 7      # shared form: 32 groups of 128 columns, 8 chunks of 128 each
+    assert _ksplit(64, 16384, 7168, 1) == 1     # 256 workgroups of 64 columns already
+    assert _ksplit(64, 7168, 16384, 1) == 4     # W_o at 64 rows: 56 groups of 128 columns -> 224
+    assert _ksplit(32, 7168, 16384, 1) == 1     # 32 rows: 224 workgroups of 32 columns, not split
+    assert _ksplit(64, 128, 512, 128) == 1      # batched value up-projection: short K, 512 workgroups
     assert _ksplit(65, 512, 7168, 1) == 1       # tile kernel, no split
 
 

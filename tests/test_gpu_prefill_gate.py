@@ -95,7 +95,11 @@ def test_prefill_fp32_tiny_config():
                                            # workgroups narrower than 32 columns: W_o over 7168 columns
                                            # as 256 x 28, and 2240 columns as 12-wide ones with an
                                            # 8-column tail (gate and value up-projection 8 wide)
-                                           (32, 7168, 8, 128, 64), (24, 2240, 16, 128, 128)])
+                                           (32, 7168, 8, 128, 64), (24, 2240, 16, 128, 128),
+                                           # shared-activation workgroups of 128 columns at 33..64
+                                           # rows, K split: W_o and the gate (gate epilogue in the
+                                           # split-K reduce); 4160 columns end in a partial group
+                                           (64, 7168, 32, 512, 128), (40, 4160, 40, 256, 64)])
 def test_gate_out_with_value_up_projection(T, D, H, d_c, d_v):
     say(f"[gate_out decode-side] T={T} D={D} H={H} d_c={d_c} d_v={d_v}")
     g = torch.Generator().manual_seed(5)
@@ -188,6 +192,27 @@ def test_prefill_full_size_sampled_rows():
     say(f"  rel err c {e[0]:.2e}  o~ {e[1]:.2e}  y {e[2]:.2e} (o~ per row {row_err(ot[:, rows].float(), rot):.2e}, "
         f"y per row {row_err(y[:, rows].float().reshape(xr.shape[0], -1), ry):.2e})")
     assert max(e) <= BF16_TOL
+
+
+@pytest.mark.slow
+def test_decode_output_side_full_size_h128():
+    """gate_out on the RoPE decode workload's output side at full size (T =
+    64, d_model = 7168, H = 128, d_c = 512, d_v = 128): W_o runs as shared-
+    activation workgroups with K split four ways."""
+    say("[gate_out full decode-side H=128]")
+    g = torch.Generator().manual_seed(2)
+    T, D, H, d_c, d_v = 64, 7168, 128, 512, 128
+    o_lat = torch.randn(T, H, d_c, generator=g).to(torch.bfloat16)
+    x = torch.randn(T, D, generator=g).to(torch.bfloat16)
+    W_uv = (torch.randn(H, d_v, d_c, generator=g) / d_c ** 0.5).to(torch.bfloat16)
+    W_g = (torch.randn(H * d_v, D, generator=g) / D ** 0.5).to(torch.bfloat16)
+    W_o = (torch.randn(D, H * d_v, generator=g) / (H * d_v) ** 0.5).to(torch.bfloat16)
+    y = ops.gate_out(dev(x), dev(o_lat), dev(W_g), dev(W_o), W_uv=dev(W_uv))
+    torch.cuda.synchronize()
+    ry = O.gate_out_reference(_np(x), O.value_up_projection(_np(o_lat), _np(W_uv)), _np(W_g), _np(W_o))
+    e = rel_err(y.float(), ry)
+    say(f"  rel err y {e:.2e} (per row {row_err(y.float(), ry):.2e})")
+    assert e <= BF16_TOL
 
 
 @pytest.mark.slow
