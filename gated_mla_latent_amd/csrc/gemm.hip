@@ -658,16 +658,15 @@ struct SharedCfg {
   static_assert((NST - 2) * IPS < 64, "vmcnt range");
 };
 
+// Columns n0 .. n0 + 127 of batch `batch`, K slice zi of nz.
 template <int MT, int EPI>
-__global__ __launch_bounds__(256) void gemm_skinny_shared_kernel(GemmArgs g) {
+__device__ __forceinline__ void shared_body(const GemmArgs& g, int n0, int batch, int zi, int nz) {
   using C = SharedCfg<MT>;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
   const unsigned smem_base = (unsigned)(uintptr_t)smem;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n0 = blockIdx.x * 128;
-  const int batch = blockIdx.y, zi = blockIdx.z, nz = gridDim.z;
   const bf16* A = g.A + batch * g.sA;
   const bf16* W = g.W + batch * g.sW;
   bf16* Cp = g.C + batch * g.sC;
@@ -754,6 +753,27 @@ __global__ __launch_bounds__(256) void gemm_skinny_shared_kernel(GemmArgs g) {
       }
     }
   }
+}
+
+template <int MT, int EPI>
+__global__ __launch_bounds__(256) void gemm_skinny_shared_kernel(GemmArgs g) {
+  shared_body<MT, EPI>(g, blockIdx.x * 128, blockIdx.y, blockIdx.z, gridDim.z);
+}
+
+// Several plain-store GEMMs that share A, M and K (one K slice each): segment
+// s owns workgroups first_wg[s] .. first_wg[s + 1] - 1, 128 columns each.
+template <int MT>
+__global__ __launch_bounds__(256) void gemm_skinny_shared_group_kernel(GemmGroup gg) {
+  const int x = blockIdx.x;
+  const int s = (x >= gg.first_wg[1]) + (x >= gg.first_wg[2]) + (x >= gg.first_wg[3]);
+  GemmArgs g = gg.base;
+  g.W = s == 0 ? gg.W[0] : s == 1 ? gg.W[1] : s == 2 ? gg.W[2] : gg.W[3];
+  g.C = s == 0 ? gg.C[0] : s == 1 ? gg.C[1] : s == 2 ? gg.C[2] : gg.C[3];
+  g.N = s == 0 ? gg.N[0] : s == 1 ? gg.N[1] : s == 2 ? gg.N[2] : gg.N[3];
+  g.ldw = s == 0 ? gg.ldw[0] : s == 1 ? gg.ldw[1] : s == 2 ? gg.ldw[2] : gg.ldw[3];
+  g.ldc = s == 0 ? gg.ldc[0] : s == 1 ? gg.ldc[1] : s == 2 ? gg.ldc[2] : gg.ldc[3];
+  const int first = s == 0 ? 0 : s == 1 ? gg.first_wg[1] : s == 2 ? gg.first_wg[2] : gg.first_wg[3];
+  shared_body<MT, EPI_STORE>(g, (x - first) * 128, 0, 0, 1);
 }
 
 template <int MT, int NT, int EPI>
@@ -1051,12 +1071,37 @@ hipError_t launch_gemm_group_bf16(GemmGroup gg, hipStream_t st) {
   if ((long long)b.M * b.lda * 2 >= (1LL << 32)) return hipErrorInvalidValue;
   int first = 0;
   for (int s = 0; s < gg.count; ++s)
-    if (gg.N[s] <= 0) return hipErrorInvalidValue;
+    if (gg.N[s] <= 0 || gg.N[s] % 4 != 0 || (long long)gg.N[s] * gg.ldw[s] * 2 >= (1LL << 32))
+      return hipErrorInvalidValue;
+  gg.base.batches = 1;
+  gg.base.ksplit = 1;
+  gg.base.epi = EPI_STORE;
+  gg.base.npad = 0;
+  if (b.M > 32 && b.K % 128 == 0 && b.K >= 2048) {
+    // 33..64 rows: shared-activation workgroups of 128 columns when they fit
+    // one round of the grid (no K split here)
+    long long groups = 0;
+    for (int s = 0; s < gg.count; ++s) groups += (gg.N[s] + 127) / 128;
+    if (groups >= 32 && groups <= 256) {
+      for (int s = 0; s < 4; ++s) {
+        if (s < gg.count) {
+          gg.first_wg[s] = first;
+          first += (gg.N[s] + 127) / 128;
+        } else {
+          gg.first_wg[s] = INT32_MAX;
+        }
+      }
+      gg.base.cw = 128;
+      using C = SharedCfg<2>;
+      auto kern = gemm_skinny_shared_group_kernel<2>;
+      hipError_t e = lds_opt_in((const void*)kern, C::LDS_BYTES);
+      if (e != hipSuccess) return e;
+      return launch(kern, dim3(first), dim3(256), C::LDS_BYTES, st, gg);
+    }
+  }
   const int cols = skinny_cols(gg.N, gg.count, 1, b.M);
   for (int s = 0; s < 4; ++s) {
     if (s < gg.count) {
-      if (gg.N[s] <= 0 || gg.N[s] % 4 != 0 || (long long)gg.N[s] * gg.ldw[s] * 2 >= (1LL << 32))
-        return hipErrorInvalidValue;
       if (s > 0) gg.first_wg[s] = first;
       first += (gg.N[s] + cols - 1) / cols;
     } else {
@@ -1064,10 +1109,6 @@ hipError_t launch_gemm_group_bf16(GemmGroup gg, hipStream_t st) {
     }
   }
   gg.first_wg[0] = 0;
-  gg.base.batches = 1;
-  gg.base.ksplit = 1;
-  gg.base.epi = EPI_STORE;
-  gg.base.npad = 0;
   gg.base.cw = cols;
   if (b.M <= 32) return cols > 32 ? launch_group<1, 2>(gg, first, st) : launch_group<1, 1>(gg, first, st);
   return cols > 32 ? launch_group<2, 2>(gg, first, st) : launch_group<2, 1>(gg, first, st);

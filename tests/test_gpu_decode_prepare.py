@@ -63,6 +63,8 @@ def _check_prepare(dec, st, cache, q_abs):
 @pytest.mark.parametrize("B,H,d_c,d_r,d_model,d_k", [
     (37, 64, 512, 0, 512, 128),     # NoPE, ragged batch (two LDS row blocks, partial tile)
     (37, 128, 512, 64, 1024, 128),  # decoupled RoPE
+    (40, 32, 512, 64, 2176, 128),   # 33..64 rows, K = 17 x 128: shared-activation workgroups of 128
+                                    # columns over the segments (the 64-wide RoPE key one partial)
     (5, 16, 256, 64, 256, 64),
     (1, 8, 128, 4, 192, 32),
     (70, 32, 64, 64, 128, 128),
