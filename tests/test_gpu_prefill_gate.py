@@ -99,7 +99,10 @@ def test_prefill_fp32_tiny_config():
                                            # shared-activation workgroups of 128 columns at 33..64
                                            # rows, K split: W_o and the gate (gate epilogue in the
                                            # split-K reduce); 4160 columns end in a partial group
-                                           (64, 7168, 32, 512, 128), (40, 4160, 40, 256, 64)])
+                                           (64, 7168, 32, 512, 128), (40, 4160, 40, 256, 64),
+                                           # ... and batched: the value up-projection over d_c = 2048
+                                           # (one 128-column group per head, K split in two)
+                                           (48, 512, 64, 2048, 128)])
 def test_gate_out_with_value_up_projection(T, D, H, d_c, d_v):
     say(f"[gate_out decode-side] T={T} D={D} H={H} d_c={d_c} d_v={d_v}")
     g = torch.Generator().manual_seed(5)
