@@ -6,6 +6,10 @@
 //   EPI_GATE:  C = Sigmoid(acc) * O[m, n]            ("Gated MLA 计算公式" §二:
 //                                                      the per-channel gate
 //                                                      applied to o~ before W_o)
+//   EPI_GATE_VU: the same with O[m, h d_v + j] = sum_c o_lat[m, h, c] W_UV[h, j, c]
+//              formed by the skinny workgroup that gates it ("LLM 注意力与计算
+//              内核精读笔记 · 03" §5.2: the value up-projection applied once
+//              to the latent-space output)
 //
 // Both operands are K-contiguous, so every MFMA fragment is a 16-byte read.
 // The weight is the MFMA "A" side: the accumulator layout then gives each lane
@@ -567,10 +571,35 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& g, int n0, int cw, i
     for (int t = 0; t < MT; ++t) acc[u][t] = floatx16{};
   const int span = c_hi > c_lo ? c_hi - c_lo : 0;
   const int nmy = span > wave ? (span - wave + 3) / 4 : 0;  // this wave's chunks: c_lo + wave, + 4, ...
+  const int r32 = lane & 31, hk = lane >> 5;
+  // EPI_GATE_VU: the operands of this workgroup's value up-projection (head
+  // h = n0 / d_v, its rows j0 .. j0 + 32 NT - 1 of W_uv, all M rows of
+  // o_lat), k-steps wave, wave + 4, ... of the 32 over d_c = 512. They are
+  // loaded before the weight stream starts and multiplied after it ends:
+  // their wait then holds nothing up (memory operations complete in issue
+  // order, so a wait for loads issued after the weight DMA would drain it).
+  constexpr int KV = 8;  // value up-projection k-steps per wave
+  bf16x8 vwf[EPI == EPI_GATE_VU ? KV : 1][NT], vof[EPI == EPI_GATE_VU ? KV : 1][MT];
+  if constexpr (EPI == EPI_GATE_VU) {
+    const int h = n0 / g.vdv, j0 = n0 - h * g.vdv;
+    const bf16* wv = g.vw + ((int64_t)h * g.vdv + j0 + r32) * g.vdc + 8 * hk;
+    const bf16* ov = g.vo + (int64_t)h * g.vdc + 8 * hk;
+#pragma unroll
+    for (int x = 0; x < KV; ++x) {
+      const int c = 16 * (wave + 4 * x);
+#pragma unroll
+      for (int u = 0; u < NT; ++u) vwf[x][u] = as_bf16x8(*(const u32x4*)(wv + (int64_t)32 * u * g.vdc + c));
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        int m = 32 * t + r32;
+        m = m < g.M ? m : g.M - 1;
+        vof[x][t] = as_bf16x8(*(const u32x4*)(ov + (int64_t)m * g.ldvo + c));
+      }
+    }
+  }
 #pragma unroll
   for (int b = 0; b < C::NBUF; ++b)
     if (b < nmy) issue(b, c_lo + wave + 4 * b);
-  const int r32 = lane & 31, hk = lane >> 5;
   for (int i = 0; i < nmy; ++i) {
     const int b = i % C::NBUF;
     int pend = nmy - 1 - i;
@@ -596,31 +625,68 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& g, int n0, int cw, i
     }
   }
 
+  floatx16 vacc[EPI == EPI_GATE_VU ? NT : 1][EPI == EPI_GATE_VU ? MT : 1];
+  if constexpr (EPI == EPI_GATE_VU) {
+#pragma unroll
+    for (int u = 0; u < NT; ++u)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) vacc[u][t] = floatx16{};
+#pragma unroll
+    for (int x = 0; x < KV; ++x)
+#pragma unroll
+      for (int u = 0; u < NT; ++u)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) vacc[u][t] = mfma32(vwf[x][u], vof[x][t], vacc[u][t]);
+  }
+
   __syncthreads();  // every wave is done with its ring: reuse it for the reduction
   constexpr int NA = NT * MT;  // accumulators per wave
   LDS_AS float* red = (LDS_AS float*)smem;  // [4 waves][NT MT][16][64]
+  LDS_AS float* vred = red + 4 * NA * 16 * 64;  // EPI_GATE_VU: the same for the value up-projection
+  static_assert(EPI != EPI_GATE_VU || 2 * 4 * NA * 16 * 64 * 4 <= C::LDS_BYTES, "both reductions fit in the ring");
 #pragma unroll
   for (int u = 0; u < NT; ++u)
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) red[((wave * NA + u * MT + t) * 16 + r) * 64 + lane] = acc[u][t][r];
+      for (int r = 0; r < 16; ++r) {
+        red[((wave * NA + u * MT + t) * 16 + r) * 64 + lane] = acc[u][t][r];
+        if constexpr (EPI == EPI_GATE_VU) vred[((wave * NA + u * MT + t) * 16 + r) * 64 + lane] = vacc[u][t][r];
+      }
   __syncthreads();
   // wave w finishes register group r4 = w (4 consecutive columns per lane)
 #pragma unroll
   for (int ut = 0; ut < NA; ++ut) {
     const int u = ut / MT, t = ut % MT;
-    float v[4];
+    float v[4], vo[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * wave + e;
       v[e] = 0.f;
+      vo[e] = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) v[e] += red[((w * NA + ut) * 16 + r) * 64 + lane];
+      for (int w = 0; w < 4; ++w) {
+        v[e] += red[((w * NA + ut) * 16 + r) * 64 + lane];
+        if constexpr (EPI == EPI_GATE_VU) vo[e] += vred[((w * NA + ut) * 16 + r) * 64 + lane];
+      }
     }
     const int m = 32 * t + (lane & 31);
     const int n = n0 + 32 * u + 8 * wave + 4 * (lane >> 5);
     if (n >= n0 + cw) continue;  // another workgroup's columns
+    if constexpr (EPI == EPI_GATE_VU) {
+      // o~ as the separate up-projection would store it (bf16), then the gate
+      if (m < g.M && n < g.N) {
+        u32x2 w;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const unsigned pk = pack_bf16x2(vo[2 * e], vo[2 * e + 1]);
+          w[e] = pack_bf16x2(sigmoidf_fast(v[2 * e]) * bf16_bits_to_f32((unsigned short)(pk & 0xffff)),
+                             sigmoidf_fast(v[2 * e + 1]) * bf16_bits_to_f32((unsigned short)(pk >> 16)));
+        }
+        *(u32x2*)(Cp + (int64_t)m * g.ldc + n) = w;
+      }
+      continue;
+    }
     if (nz > 1) {  // partial sums [slice][batch][M][N rounded up to 4]
       const int ldp = (g.N + 3) & ~3;
       if (m < g.M && n < g.N)
@@ -778,7 +844,15 @@ __global__ __launch_bounds__(256) void gemm_skinny_shared_group_kernel(GemmGroup
 
 template <int MT, int NT, int EPI>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
-  skinny_body<MT, NT, EPI>(g, blockIdx.x * g.cw, g.cw, blockIdx.y, blockIdx.z, gridDim.z);
+  int x = blockIdx.x;
+  if constexpr (EPI == EPI_GATE_VU) {
+    // workgroups are dealt to the 8 XCDs in turn: give each XCD a run of
+    // adjacent column blocks, so the workgroups of one head, which all read
+    // that head's o_lat, share it through one L2
+    const int G = gridDim.x;
+    if (G % 8 == 0) x = (x % 8) * (G / 8) + x / 8;
+  }
+  skinny_body<MT, NT, EPI>(g, x * g.cw, g.cw, blockIdx.y, blockIdx.z, gridDim.z);
 }
 
 // Several plain-store GEMMs that share A, M and K in one grid: segment s
@@ -1007,29 +1081,40 @@ static int skinny_cols(const int* N, int nseg, int batches, int M) {
 
 template <int EPI>
 static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
-  if (skinny_path(g.M, g.N, EPI == EPI_STORE ? g.npad : 0)) {
-    // the DMA offsets are 32-bit: every row start must be below 4 GiB
-    if ((long long)g.N * g.ldw * 2 >= (1LL << 32) || (long long)g.M * g.lda * 2 >= (1LL << 32))
+  // the skinny kernels' DMA offsets are 32-bit: every row start below 4 GiB
+  const bool offsets32 = (long long)g.N * g.ldw * 2 < (1LL << 32) && (long long)g.M * g.lda * 2 < (1LL << 32);
+  if constexpr (EPI == EPI_GATE_VU) {
+    if (!gemm_gate_vu_supported(g.M, g.N, g.K, g.vdc, g.vdv) || g.batches != 1 || !g.vo || !g.vw || !offsets32)
       return hipErrorInvalidValue;
-    if (shared_path(g.M, g.N, g.K, g.batches)) return launch_shared<EPI>(g, st);
     GemmArgs h = g;
-    if (g.ksplit > 1) {
-      h.cw = 32;
-    } else {
-      const int n1[1] = {g.N};
-      h.cw = skinny_cols(n1, 1, g.batches, g.M);
-    }
+    const int n1[1] = {g.N};
+    h.cw = skinny_cols(n1, 1, 1, g.M);
     const bool nt2 = h.cw > 32;
     if (g.M <= 32) return nt2 ? launch_skinny<1, 2, EPI>(h, st) : launch_skinny<1, 1, EPI>(h, st);
     return nt2 ? launch_skinny<2, 2, EPI>(h, st) : launch_skinny<2, 1, EPI>(h, st);
+  } else {
+    if (skinny_path(g.M, g.N, EPI == EPI_STORE ? g.npad : 0)) {
+      if (!offsets32) return hipErrorInvalidValue;
+      if (shared_path(g.M, g.N, g.K, g.batches)) return launch_shared<EPI>(g, st);
+      GemmArgs h = g;
+      if (g.ksplit > 1) {
+        h.cw = 32;
+      } else {
+        const int n1[1] = {g.N};
+        h.cw = skinny_cols(n1, 1, g.batches, g.M);
+      }
+      const bool nt2 = h.cw > 32;
+      if (g.M <= 32) return nt2 ? launch_skinny<1, 2, EPI>(h, st) : launch_skinny<1, 1, EPI>(h, st);
+      return nt2 ? launch_skinny<2, 2, EPI>(h, st) : launch_skinny<2, 1, EPI>(h, st);
+    }
+    const long long big_tiles = (long long)((g.N + 255) / 256) * ((g.M + 255) / 256) * g.batches;
+    // the big-tile kernel's two-tile lookahead pays off over long K; at short
+    // K (the K and V reconstruction, K = 512) its prologue dominates and
+    // gemm_tile measured faster (182 against 230 us)
+    if (big_tiles >= 256)
+      return g.K >= 2048 && big_fits<EPI>(g) ? launch_big<EPI>(g, st) : launch_tile<256, 256, EPI>(g, st);
+    return launch_tile<128, 128, EPI>(g, st);
   }
-  const long long big_tiles = (long long)((g.N + 255) / 256) * ((g.M + 255) / 256) * g.batches;
-  // the big-tile kernel's two-tile lookahead pays off over long K; at short
-  // K (the K and V reconstruction, K = 512) its prologue dominates and
-  // gemm_tile measured faster (182 against 230 us)
-  if (big_tiles >= 256)
-    return g.K >= 2048 && big_fits<EPI>(g) ? launch_big<EPI>(g, st) : launch_tile<256, 256, EPI>(g, st);
-  return launch_tile<128, 128, EPI>(g, st);
 }
 
 // Split K when the skinny grid has fewer than 64 workgroups (a quarter of
@@ -1118,7 +1203,17 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t st) {
   if (g.M <= 0 || g.N <= 0 || g.batches <= 0) return hipSuccess;
   if (g.npad > g.N && (g.epi != EPI_STORE || g.npad % 4 != 0)) return hipErrorInvalidValue;
   if (g.K % 64 != 0 || (g.npad > g.N ? g.npad : g.N) % 4 != 0) return hipErrorInvalidValue;
+  if (g.epi == EPI_GATE_VU) return launch_epi<EPI_GATE_VU>(g, st);
   return g.epi == EPI_GATE ? launch_epi<EPI_GATE>(g, st) : launch_epi<EPI_STORE>(g, st);
+}
+
+bool gemm_gate_vu_supported(int M, int N, int K, int d_c, int d_v) {
+  if (M <= 0 || M > 64 || N <= 0 || K <= 0 || K % 64 != 0 || N % 4 != 0 || d_c != 512 || d_v <= 0) return false;
+  if (!skinny_path(M, N, 0) || shared_path(M, N, K, 1) || gemm_ksplit(M, N, K, 1, 0) > 1) return false;
+  const int n1[1] = {N};
+  const int cw = skinny_cols(n1, 1, 1, M);
+  // whole 32- or 64-column workgroups, each inside one head
+  return (cw == 32 || cw == 64) && d_v % cw == 0 && N % d_v == 0;
 }
 
 }  // namespace gmla

@@ -569,6 +569,15 @@ gmla_status_t gmla_gate_out(const void* x, const void* o, const void* W_uv, cons
   gmla_status_t s;
   if (dtype == GMLA_BF16) {
     void* part = ws + (W_uv ? 2 : 1) * up256((size_t)T * HV * es);
+    if (W_uv && gemm_gate_vu_supported(T, HV, d_model, d_c, d_v)) {
+      // the value up-projection folded into the gate GEMM: each workgroup
+      // computes the o~ columns it gates from o_lat and W_uv itself
+      GemmArgs g = gemm(x, d_model, W_g, d_model, gated, HV, T, HV, d_model, EPI_GATE_VU);
+      g.vo = (const bf16*)o; g.vw = (const bf16*)W_uv; g.vdc = d_c; g.vdv = d_v; g.ldvo = (int64_t)H * d_c;
+      if ((s = run("gemm_gate", st, [&] { return launch_gemm_bf16(g, st); }))) return s;
+      if ((s = run("gemm_out", st, [&] { return launch_gemm_bf16(with_split(gemm(gated, HV, W_o, HV, y, d_model, T, d_model, HV), part), st); }))) return s;
+      return ok();
+    }
     if (W_uv) {
       void* otw = ws + up256((size_t)T * HV * es);
       GemmArgs g = gemm(o, (int64_t)H * d_c, W_uv, d_c, otw, HV, T, d_v, d_c);

@@ -117,7 +117,9 @@ hipError_t launch_probe_read(const void* src, size_t bytes, unsigned* sink, int 
 // C[m, n] = epi( sum_k A[m, k] * W[n, k] ), all bf16 with fp32 accumulation.
 // A is [M, K] (row stride lda), W is [N, K] (row stride ldw), C is [M, N]
 // (row stride ldc). Batches advance every pointer by its batch stride.
-enum GemmEpilogue { EPI_STORE = 0, EPI_GATE = 1 };
+// EPI_GATE_VU: EPI_GATE whose O is the value up-projection of o_lat,
+// computed in the epilogue (skinny GEMMs whose column block lies in one head)
+enum GemmEpilogue { EPI_STORE = 0, EPI_GATE = 1, EPI_GATE_VU = 2 };
 struct GemmArgs {
   const bf16* A;
   const bf16* W;
@@ -131,7 +133,18 @@ struct GemmArgs {
   float* part;              // split-K partial sums (gemm_ksplit(...) > 1): gemm_part_bytes(...) bytes
   int ksplit;               // K slices of the skinny kernel (<= 1: none)
   int cw;                   // skinny kernel: output columns per workgroup (set by the launcher)
+  // EPI_GATE_VU: O[m, h d_v + j] = sum_c vo[m, h, c] vw[h, j, c] (bf16-rounded),
+  // vo [M, H, d_c] with row stride ldvo, vw [H, d_v, d_c]
+  const bf16* vo;
+  const bf16* vw;
+  int vdc, vdv;
+  int64_t ldvo;
 };
+// Whether gemm_bf16 with EPI_GATE_VU runs for this product (M rows, N = H d_v
+// columns, K, value up-projection width d_c and head width d_v): the skinny
+// per-wave form without K split, 32- or 64-column workgroups that divide d_v,
+// d_c = 512.
+bool gemm_gate_vu_supported(int M, int N, int K, int d_c, int d_v);
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t st);
 // Split-K plan of the skinny kernel (M <= 64) for an under-filled grid, and
 // the fp32 partial-sum space it needs (0 when it does not split).

@@ -120,6 +120,35 @@ def test_gate_out_with_value_up_projection(T, D, H, d_c, d_v):
     assert e <= BF16_TOL
 
 
+@pytest.mark.parametrize("T,H,d_v", [(1, 64, 128), (5, 64, 128), (32, 64, 128), (33, 24, 128), (37, 24, 128),
+                                     (64, 24, 128)])
+def test_gate_out_fused_value_up_gated_elementwise(T, H, d_v):
+    """d_c = 512 with a wide enough gate GEMM computes o~ inside the gate
+    GEMM's workgroups (no separate value up-projection launch). W_o = I
+    makes y the gated product itself, compared element by element."""
+    d_c = 512
+    HV = H * d_v
+    say(f"[gate_out fused value up] T={T} H={H} d_v={d_v}")
+    g = torch.Generator().manual_seed(11)
+    o_lat = torch.randn(T, H, d_c, generator=g).to(torch.bfloat16)
+    x = torch.randn(T, HV, generator=g).to(torch.bfloat16)
+    W_uv = (torch.randn(H, d_v, d_c, generator=g) / d_c ** 0.5).to(torch.bfloat16)
+    W_g = (torch.randn(HV, HV, generator=g) / HV ** 0.5).to(torch.bfloat16)
+    W_o = torch.eye(HV, dtype=torch.bfloat16)
+    ops.trace_begin(64)
+    y = ops.gate_out(dev(x), dev(o_lat), dev(W_g), dev(W_o), W_uv=dev(W_uv))
+    torch.cuda.synchronize()
+    ops.trace_end()
+    kernels = ops.trace_kernels()
+    ops.trace_reset()
+    assert "gemm_value_up" not in kernels, kernels
+    _, gated = O.gate_out_reference(_np(x), O.value_up_projection(_np(o_lat), _np(W_uv)), _np(W_g), _np(W_o),
+                                    return_gated=True)
+    e = rel_err(y.float(), gated)
+    say(f"  rel err gated {e:.2e}")
+    assert e <= BF16_TOL
+
+
 @pytest.mark.parametrize("T,D,HV", [(4133, 4224, 4096), (2144, 4160, 8192)])
 def test_gate_out_large_tiles_sampled_rows(T, D, HV):
     """gate_out at sizes whose GEMMs take the 256 x 256 tile kernels (at least
