@@ -28,12 +28,15 @@
 //    half the rate and would make LDS, not the MFMAs, the bound.
 //  * K and V^T rows are 16-byte-chunk XOR-swizzled so that neither read
 //    conflicts in LDS.
-//  * Softmax: the scale (log2 e included) is folded into one FMA per score,
-//    exp2(|c| s - |c| m); a negative scale is handled by negating Q on load.
-//    No rescale of O inside the loop: each query's reference max is fixed at
-//    its first key tile; if a later score outgrows it by more than 2^32 the
-//    workgroup redoes the pass once with the true maxima (exact for any
-//    input).
+//  * Softmax: the scale (log2 e included) is folded into the queries when
+//    they are loaded (rounded to bf16), so scores are base-2 exponents. No
+//    rescale of O inside the loop: each query's reference max m is fixed at
+//    its first key tile, and from then on the S^T accumulators start at -m
+//    (the MFMA's C operand), so a weight is exp2 of the accumulator with no
+//    per-score arithmetic and no per-tile max. If the weights' sum exceeds
+//    2^32 (a later score outgrew the reference by as much), the workgroup
+//    sweeps the scores once for the true maxima and redoes the pass with
+//    them (exact for any input).
 //  * Without RoPE the P.V MFMAs of a tile run at raised wave priority, so
 //    the two waves of a SIMD settle into opposite phases: one issues MFMAs
 //    while the other computes its softmax.
@@ -129,9 +132,17 @@ void prefill_attn_kernel(AttnArgs a) {
   const bf16* qrb = DR ? a.qr + b * a.sqrb + h * a.sqrh : nullptr;
   const bf16* krb = DR ? a.kr + b * a.skrb : nullptr;
 
-  // softmax constant: |scale| log2 e; a negative scale negates the queries
-  const float cabs = fabsf(a.scale_log2);
-  const unsigned qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+  // the softmax scale (log2 e included) is folded into the queries, so the
+  // scores come out in base-2 exponent units
+  const float qs = a.scale_log2;
+  auto scaled = [&](const u32x4 v) -> bf16x8 {
+    u32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      r[e] = pack_bf16x2(bf16_bits_to_f32((unsigned short)(v[e] & 0xffff)) * qs,
+                         bf16_bits_to_f32((unsigned short)(v[e] >> 16)) * qs);
+    return as_bf16x8(r);
+  };
 
   for (int rep = 0; rep < 2; ++rep) {
   const int qt = rep == 0 ? nqt - 1 - pair : pair;
@@ -146,17 +157,11 @@ void prefill_attn_kernel(AttnArgs a) {
     t = t < a.L ? t : a.L - 1;
     const bf16* qp = qb + (int64_t)t * a.sqt + 8 * (lane >> 5);
 #pragma unroll
-    for (int kk = 0; kk < C::KSC; ++kk) {
-      u32x4 v = *(const u32x4*)(qp + 16 * kk);
-      qf[kk] = as_bf16x8(u32x4{v[0] ^ qsign, v[1] ^ qsign, v[2] ^ qsign, v[3] ^ qsign});
-    }
+    for (int kk = 0; kk < C::KSC; ++kk) qf[kk] = scaled(*(const u32x4*)(qp + 16 * kk));
     if constexpr (DR > 0) {
       const bf16* qrp = qrb + (int64_t)t * a.sqrt_ + 8 * (lane >> 5);
 #pragma unroll
-      for (int kk = C::KSC; kk < C::KS; ++kk) {
-        u32x4 v = *(const u32x4*)(qrp + 16 * (kk - C::KSC));
-        qf[kk] = as_bf16x8(u32x4{v[0] ^ qsign, v[1] ^ qsign, v[2] ^ qsign, v[3] ^ qsign});
-      }
+      for (int kk = C::KSC; kk < C::KS; ++kk) qf[kk] = scaled(*(const u32x4*)(qrp + 16 * (kk - C::KSC)));
     }
   }
 
@@ -194,9 +199,12 @@ void prefill_attn_kernel(AttnArgs a) {
   };
 
   floatx16 o[C::DB];
-  float m = -INFINITY;      // reference max per query (raw score units)
-  float m_all = -INFINITY;  // largest raw score of this lane's keys
+  float m = 0.f;               // reference max of this lane's query (scaled units)
+  float m_true = -INFINITY;    // redo sweep: the largest score of this lane's keys
   float lsum = 0.f;
+  // NoPE: the S^T accumulators start at -m (the MFMA adds its C operand),
+  // so the weights are exp2 of the accumulator with no arithmetic per score
+  floatx16 negm = floatx16{};
 
   int last_q = q0 + C::BQ - 1;
   last_q = last_q < a.L - 1 ? last_q : a.L - 1;
@@ -237,11 +245,15 @@ void prefill_attn_kernel(AttnArgs a) {
     }
   };
 
-  for (int pass = 0; pass < 2; ++pass) {
+  // pass 0: reference max from the first key tile; pass 1 (only if pass 0
+  // overflowed its bound): the true maxima, tracked over a pass at
+  // reference 0; pass 2: again with those
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const bool sweep = pass == 1;
 #pragma unroll
     for (int d = 0; d < C::DB; ++d) o[d] = floatx16{};
     lsum = 0.f;
-    m_all = -INFINITY;
     lds_barrier();
     constexpr int PRE = DR ? 2 : kSync;  // tiles issued before the loop
 #pragma unroll
@@ -270,7 +282,14 @@ void prefill_attn_kernel(AttnArgs a) {
       const LDS_AS char* kt_l = smem + (it % C::NST) * C::STAGE;
 
       // ---- S^T: 64 keys (2 blocks of 32) x 32 queries ----
-      floatx16 s[2] = {floatx16{}, floatx16{}};
+      floatx16 s[2];
+      if constexpr (DR == 0) {
+        s[0] = negm;
+        s[1] = negm;
+      } else {
+        s[0] = floatx16{};
+        s[1] = floatx16{};
+      }
       auto readK = [&](int kk, int i) -> bf16x8 {
         const int row = 32 * i + krow;
         if (kk < C::KSC) {
@@ -313,21 +332,41 @@ void prefill_attn_kernel(AttnArgs a) {
             s[i][r] = key <= tq ? s[i][r] : -INFINITY;
           }
       }
-      float mx = -INFINITY;
+      auto tile_max = [&]() {
+        float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[i][r]);
-      if (pass == 0 && it == 0) m = fmaxf(mx, xor32(mx));  // key 0 is visible to every query
-      m_all = fmaxf(m_all, mx);
-      const float mc = m * cabs;
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[i][r]);
+        return mx;
+      };
+      if (sweep) {
+        // the redo's first pass also tracks the true maxima (its weights,
+        // from a zero reference, are discarded)
+        asm volatile("");
+        m_true = fmaxf(m_true, tile_max());
+      }
+      if (pass == 0 && it == 0) {
+        // the reference: this tile's max (key 0 is visible to every query)
+        asm volatile("");
+        const float mx = tile_max();
+        m = fmaxf(mx, xor32(mx));
+        if constexpr (DR == 0) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) negm[r] = -m;
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[i][r] -= m;
+        }
+      }
       bf16x8 pb[4];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         float p[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          p[r] = fast_exp2(__builtin_fmaf(s[i][r], cabs, -mc));
+          p[r] = fast_exp2(DR == 0 ? s[i][r] : s[i][r] - m);
           lsum += p[r];
         }
 #pragma unroll
@@ -347,10 +386,20 @@ void prefill_attn_kernel(AttnArgs a) {
       pv(it % C::NST, pb);
       if constexpr (DR == 0) __builtin_amdgcn_s_setprio(0);
     }
-    const float mall = fmaxf(m_all, xor32(m_all));
-    const bool redo = (m != -INFINITY) && ((mall - m) * cabs > 32.0f);
-    if (!__syncthreads_or(redo)) break;
-    m = mall;
+    if (pass == 0) {
+      // every weight is at most the sum: a sum within 2^32 (and not NaN)
+      // bounds each weight by 2^32, the bound the pass was made for
+      const float l = lsum + xor32(lsum);
+      if (!__syncthreads_or(!(l <= 0x1p32f))) break;
+      m = 0.f;
+      negm = floatx16{};
+    } else if (pass == 1) {
+      m = fmaxf(m_true, xor32(m_true));
+      if constexpr (DR == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) negm[r] = -m;
+      }
+    }
   }
 
   // ---- write o~ ----

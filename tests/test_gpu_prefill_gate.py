@@ -43,7 +43,8 @@ def test_prefill_bf16_matches_oracle(B, L, D, H, d_c, d):
 def test_prefill_score_range_forces_redo_pass():
     """Scores whose range defeats the first-tile reference of the attention
     kernel, with operands that bf16 holds exactly, so that the oracle's
-    scores are the kernel's up to fp32 summation: d_model = d_c = d_k = d_v
+    scores are the kernel's up to fp32 summation and the bf16 rounding of
+    the scaled queries: d_model = d_c = d_k = d_v
     = 128, W_c, W_UK and W_UV identities, each head's W_q a permutation
     (entries 0 and 1), so c = K = V = x and q = P_h x exactly. Tokens from 64
     on get 4 added to every feature; the ones direction is left unchanged by
