@@ -293,13 +293,12 @@ void gemm_big_kernel(GemmGroup gg) {
   // this n-tile's segment (unused segments start at INT32_MAX)
   const int seg = (tile_n >= gg.first_wg[1]) + (tile_n >= gg.first_wg[2]) + (tile_n >= gg.first_wg[3]);
   const int seg_first = seg == 0 ? 0 : seg == 1 ? gg.first_wg[1] : seg == 2 ? gg.first_wg[2] : gg.first_wg[3];
-  if (gg.count > 1) {
-    g.W = seg == 0 ? gg.W[0] : seg == 1 ? gg.W[1] : seg == 2 ? gg.W[2] : gg.W[3];
-    g.C = seg == 0 ? gg.C[0] : seg == 1 ? gg.C[1] : seg == 2 ? gg.C[2] : gg.C[3];
-    g.N = seg == 0 ? gg.N[0] : seg == 1 ? gg.N[1] : seg == 2 ? gg.N[2] : gg.N[3];
-    g.ldw = seg == 0 ? gg.ldw[0] : seg == 1 ? gg.ldw[1] : seg == 2 ? gg.ldw[2] : gg.ldw[3];
-    g.ldc = seg == 0 ? gg.ldc[0] : seg == 1 ? gg.ldc[1] : seg == 2 ? gg.ldc[2] : gg.ldc[3];
-  }
+  // every launch fills the segment arrays, a single GEMM as segment 0
+  g.W = seg == 0 ? gg.W[0] : seg == 1 ? gg.W[1] : seg == 2 ? gg.W[2] : gg.W[3];
+  g.C = seg == 0 ? gg.C[0] : seg == 1 ? gg.C[1] : seg == 2 ? gg.C[2] : gg.C[3];
+  g.N = seg == 0 ? gg.N[0] : seg == 1 ? gg.N[1] : seg == 2 ? gg.N[2] : gg.N[3];
+  g.ldw = seg == 0 ? gg.ldw[0] : seg == 1 ? gg.ldw[1] : seg == 2 ? gg.ldw[2] : gg.ldw[3];
+  g.ldc = seg == 0 ? gg.ldc[0] : seg == 1 ? gg.ldc[1] : seg == 2 ? gg.ldc[2] : gg.ldc[3];
   const int n0 = (tile_n - seg_first) * BN, m0 = tile_m * BM;
   const int batch = blockIdx.y;
   const bf16* A = g.A + batch * g.sA;
