@@ -52,6 +52,31 @@ def test_rope_prefill_matches_oracle(B, L, D, H, d_c, d):
     _check(W.make_prefill(B, L, D, H, d_c, d, d, seed=41, d_r=64))
 
 
+def test_rope_prefill_score_range_forces_redo_pass():
+    """The redo path of the RoPE attention kernel (192-wide scores): the
+    content part as in the NoPE redo test (c = K = V = x with W_c, W_UK,
+    W_UV identities, each head's W_q a permutation, tokens from 64 on shifted
+    by 4 in every feature, so later scores lie hundreds of log2 units above
+    the first key tile's maximum) plus a small rotated RoPE part. The pass
+    at the first tile's reference overflows its bound and the workgroup must
+    redo it with the true maxima."""
+    say("[rope prefill redo]")
+    L, D, H, d_r = 300, 128, 2, 64
+    g = torch.Generator().manual_seed(29)
+    x = torch.randn(1, L, D, generator=g)
+    x[:, 64:] += 4.0
+    eye = torch.eye(D)
+    W_q = torch.cat([eye[torch.randperm(D, generator=g)] for _ in range(H)], 0)
+    bf = lambda t: t.to(torch.bfloat16).contiguous()
+    inp = W.PrefillInputs(B=1, L=L, d_model=D, H=H, d_c=D, d_k=D, d_v=D, sm_scale=1.0 / (D + d_r) ** 0.5,
+                          dtype=torch.bfloat16, x=bf(x), W_c=bf(eye), W_q=bf(W_q), W_uk=bf(eye.expand(H, D, D)),
+                          W_uv=bf(eye.expand(H, D, D)), W_g=bf(torch.zeros(H * D, D)), W_o=bf(torch.zeros(D, H * D)),
+                          name="rope redo", d_r=d_r, rope_base=10000.0,
+                          W_kr=bf(torch.randn(d_r, D, generator=g) * 0.05),
+                          W_qr=bf(torch.randn(H * d_r, D, generator=g) * 0.05))
+    _check(inp)
+
+
 def test_rope_prefill_with_low_rank_query():
     say("[rope prefill + low-rank q]")
     _check(W.make_prefill(2, 200, 256, 3, 128, 128, 128, seed=42, d_r=64, d_cq=192))
