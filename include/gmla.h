@@ -201,7 +201,10 @@ gmla_status_t gmla_decode_prepare(const void* x, const void* W_c, const void* W_
  * pre-multiplied into W_o because the gate between them is per channel).
  *   x [T, d_model], W_g [H*d_v, d_model], W_o [d_model, H*d_v], y [T, d_model]
  * BF16 needs d_model % 64 == 0, (H*d_v) % 64 == 0, d_c % 64 == 0 and
- * d_v % 4 == 0. The workspace holds gated (and o~ when W_uv is given) and,
+ * d_v % 4 == 0. At decode sizes (bf16, T <= 64, d_c == 512, an unsplit
+ * gate GEMM) the gate GEMM's workgroups form the o~ columns they gate from
+ * o_lat and W_uv themselves. The workspace holds gated (and o~ when W_uv is
+ * given, used when o~ is formed by a GEMM of its own) and,
  * for T <= 64 with bf16, the fp32 partial sums of GEMMs whose K is split
  * across workgroups; its size depends on every argument of the size query
  * (d_c is ignored without the value up-projection).
