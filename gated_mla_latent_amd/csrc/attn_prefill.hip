@@ -202,7 +202,7 @@ void prefill_attn_kernel(AttnArgs a) {
   float m = 0.f;               // reference max of this lane's query (scaled units)
   float m_true = -INFINITY;    // redo sweep: the largest score of this lane's keys
   float lsum = 0.f;
-  // NoPE: the S^T accumulators start at -m (the MFMA adds its C operand),
+  // the S^T accumulators start at -m (the MFMA adds its C operand),
   // so the weights are exp2 of the accumulator with no arithmetic per score
   floatx16 negm = floatx16{};
 
@@ -283,13 +283,8 @@ void prefill_attn_kernel(AttnArgs a) {
 
       // ---- S^T: 64 keys (2 blocks of 32) x 32 queries ----
       floatx16 s[2];
-      if constexpr (DR == 0) {
-        s[0] = negm;
-        s[1] = negm;
-      } else {
-        s[0] = floatx16{};
-        s[1] = floatx16{};
-      }
+      s[0] = negm;
+      s[1] = negm;
       auto readK = [&](int kk, int i) -> bf16x8 {
         const int row = 32 * i + krow;
         if (kk < C::KSC) {
@@ -351,14 +346,12 @@ void prefill_attn_kernel(AttnArgs a) {
         asm volatile("");
         const float mx = tile_max();
         m = fmaxf(mx, xor32(mx));
-        if constexpr (DR == 0) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) negm[r] = -m;
+        for (int r = 0; r < 16; ++r) negm[r] = -m;
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[i][r] -= m;
-        }
+          for (int r = 0; r < 16; ++r) s[i][r] -= m;
       }
       bf16x8 pb[4];
 #pragma unroll
@@ -366,7 +359,7 @@ void prefill_attn_kernel(AttnArgs a) {
         float p[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          p[r] = fast_exp2(DR == 0 ? s[i][r] : s[i][r] - m);
+          p[r] = fast_exp2(s[i][r]);
           lsum += p[r];
         }
 #pragma unroll
@@ -395,10 +388,8 @@ void prefill_attn_kernel(AttnArgs a) {
       negm = floatx16{};
     } else if (pass == 1) {
       m = fmaxf(m_true, xor32(m_true));
-      if constexpr (DR == 0) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) negm[r] = -m;
-      }
+      for (int r = 0; r < 16; ++r) negm[r] = -m;
     }
   }
 
