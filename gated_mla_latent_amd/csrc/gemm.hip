@@ -33,7 +33,8 @@
 //  * gemm_skinny_shared: 33..64 rows where 64-column workgroups would not
 //    fill the grid: a workgroup owns 128 columns and shares each activation
 //    chunk among its 4 waves (a quarter of the activation bytes per weight
-//    byte), 256-byte row pieces, K split across workgroups.
+//    byte), 256-byte row pieces, K split across workgroups (even shares of
+//    the column groups' chunks over the grid).
 #include "common.h"
 #include "kernels.h"
 
@@ -706,7 +707,8 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& g, int n0, int cw, i
 // per row, with one barrier per stage. Sharing the activation chunk cuts
 // the activation bytes per weight byte from M / 32 to M / 128, and the
 // 256-byte row pieces stream faster than 128-byte ones. K is split across
-// workgroups to fill the grid; fp32 partial sums go to the split-K reduce.
+// workgroups to fill the grid (one batch: the column groups' K chunks in
+// even shares over the grid); fp32 partial sums go to the split-K reduce.
 // Rows are 256 bytes; 16-byte piece p of row r sits at p ^ (r % 16).
 template <int MT>
 struct SharedCfg {
@@ -723,9 +725,24 @@ struct SharedCfg {
   static_assert((NST - 2) * IPS < 64, "vmcnt range");
 };
 
-// Columns n0 .. n0 + 127 of batch `batch`, K slice zi of nz.
+// Even shares of the T = groups x chunks (column group, K chunk) items over
+// W workgroups: workgroup w takes items [w T / W, (w + 1) T / W). The first
+// and the last workgroup whose share touches group grp (its items
+// grp C .. grp C + C - 1, C chunks per group): the largest w with
+// w T / W rounded down <= item, for its first and its last item.
+__host__ __device__ inline int sk_first(int grp, int chunks, long long tot, int wgs) {
+  return (int)((((long long)grp * chunks + 1) * wgs + tot - 1) / tot) - 1;
+}
+__host__ __device__ inline int sk_last(int grp, int chunks, long long tot, int wgs) {
+  return (int)((((long long)(grp + 1) * chunks) * wgs + tot - 1) / tot) - 1;
+}
+
+// Columns n0 .. n0 + 127 of batch `batch`, K chunks c_lo .. c_hi - 1 (of
+// 128); partial: fp32 partial sums into slice `slot` of the split-K space,
+// else the epilogue and the bf16 store.
 template <int MT, int EPI>
-__device__ __forceinline__ void shared_body(const GemmArgs& g, int n0, int batch, int zi, int nz) {
+__device__ __forceinline__ void shared_body(const GemmArgs& g, int n0, int batch, int c_lo, int c_hi, int slot,
+                                            bool partial) {
   using C = SharedCfg<MT>;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
@@ -736,10 +753,6 @@ __device__ __forceinline__ void shared_body(const GemmArgs& g, int n0, int batch
   const bf16* W = g.W + batch * g.sW;
   bf16* Cp = g.C + batch * g.sC;
   const bf16* Op = (EPI == EPI_GATE) ? g.O + batch * g.sO : nullptr;
-  const int all_chunks = g.K / C::KB;
-  const int per = (all_chunks + nz - 1) / nz;
-  const int c_lo = zi * per;
-  const int c_hi = (c_lo + per) < all_chunks ? (c_lo + per) : all_chunks;
   const int n = c_hi > c_lo ? c_hi - c_lo : 0;
 
   // DMA: instruction q of a wave moves 4 rows of 256 bytes; lane l writes
@@ -809,10 +822,10 @@ __device__ __forceinline__ void shared_body(const GemmArgs& g, int n0, int batch
     for (int r4 = 0; r4 < 4; ++r4) {
       const int col = n0 + 32 * wave + 8 * r4 + 4 * hk;
       const float v0 = acc[t][4 * r4], v1 = acc[t][4 * r4 + 1], v2 = acc[t][4 * r4 + 2], v3 = acc[t][4 * r4 + 3];
-      if (nz > 1) {
+      if (partial) {
         const int ldp = (g.N + 3) & ~3;
         if (m < g.M && col < g.N)
-          *(float4*)(g.part + (((int64_t)zi * g.batches + batch) * g.M + m) * ldp + col) = make_float4(v0, v1, v2, v3);
+          *(float4*)(g.part + (((int64_t)slot * g.batches + batch) * g.M + m) * ldp + col) = make_float4(v0, v1, v2, v3);
       } else {
         store4<EPI>(g, Cp, Op, m, col, v0, v1, v2, v3);
       }
@@ -822,7 +835,33 @@ __device__ __forceinline__ void shared_body(const GemmArgs& g, int n0, int batch
 
 template <int MT, int EPI>
 __global__ __launch_bounds__(256) void gemm_skinny_shared_kernel(GemmArgs g) {
-  shared_body<MT, EPI>(g, blockIdx.x * 128, blockIdx.y, blockIdx.z, gridDim.z);
+  const int chunks = g.K / SharedCfg<MT>::KB;
+  if (g.sk_wgs > 0) {
+    // even shares of the (column group, chunk) space: workgroup w takes
+    // chunks [w T / W, (w + 1) T / W) of the T = groups x chunks in order,
+    // which may end one group and start the next; each piece is a partial
+    // sum in the slot of its group given by sk_first
+    const int w = blockIdx.x;
+    const long long tot = (long long)((g.N + 127) / 128) * chunks;
+    int lo = (int)((long long)w * tot / g.sk_wgs);
+    const int hi = (int)((long long)(w + 1) * tot / g.sk_wgs);
+    bool first = true;
+    while (lo < hi) {
+      const int grp = lo / chunks;
+      const int end = hi < (grp + 1) * chunks ? hi : (grp + 1) * chunks;
+      if (!first) lds_barrier();  // every wave is done with the ring
+      shared_body<MT, EPI>(g, grp * 128, 0, lo - grp * chunks, end - grp * chunks,
+                           w - sk_first(grp, chunks, tot, g.sk_wgs), true);
+      lo = end;
+      first = false;
+    }
+    return;
+  }
+  const int nz = gridDim.z, zi = blockIdx.z;
+  const int per = (chunks + nz - 1) / nz;
+  const int c_lo = zi * per;
+  const int c_hi = (c_lo + per) < chunks ? (c_lo + per) : chunks;
+  shared_body<MT, EPI>(g, blockIdx.x * 128, blockIdx.y, c_lo, c_hi, zi, nz > 1);
 }
 
 // Several plain-store GEMMs that share A, M and K (one K slice each): segment
@@ -838,7 +877,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_shared_group_kernel(GemmGroup
   g.ldw = s == 0 ? gg.ldw[0] : s == 1 ? gg.ldw[1] : s == 2 ? gg.ldw[2] : gg.ldw[3];
   g.ldc = s == 0 ? gg.ldc[0] : s == 1 ? gg.ldc[1] : s == 2 ? gg.ldc[2] : gg.ldc[3];
   const int first = s == 0 ? 0 : s == 1 ? gg.first_wg[1] : s == 2 ? gg.first_wg[2] : gg.first_wg[3];
-  shared_body<MT, EPI_STORE>(g, (x - first) * 128, 0, 0, 1);
+  shared_body<MT, EPI_STORE>(g, (x - first) * 128, 0, 0, g.K / SharedCfg<MT>::KB, 0, false);
 }
 
 template <int MT, int NT, int EPI>
@@ -885,14 +924,22 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmArgs g) {
   const int64_t bm = i / q4;
   const int n = (int)(i % q4) * 4;
   float4 acc = {0.f, 0.f, 0.f, 0.f};
+  // slices of this column: all of them, or with even shares the workgroups
+  // whose shares touched its 128-column group
+  int ns = g.ksplit;
+  if (g.sk_wgs > 0) {
+    const int chunks = g.K / 128, grp = n / 128;
+    const long long tot = (long long)((g.N + 127) / 128) * chunks;
+    ns = sk_last(grp, chunks, tot, g.sk_wgs) - sk_first(grp, chunks, tot, g.sk_wgs) + 1;
+  }
   if (ok) {
     const float* p = g.part + bm * ldp + n;
-    for (int z0 = j; z0 < g.ksplit; z0 += 32) {
+    for (int z0 = j; z0 < ns; z0 += 32) {
       float4 v[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int z = z0 + 8 * u;
-        v[u] = z < g.ksplit ? *(const float4*)(p + z * slice) : float4{0.f, 0.f, 0.f, 0.f};
+        v[u] = z < ns ? *(const float4*)(p + z * slice) : float4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -934,6 +981,27 @@ static hipError_t launch_skinny(const GemmArgs& g, hipStream_t st) {
 
 
 // ----------------------------------------------------------------------------
+// One batch: the (column group, chunk) space in even shares over up to 256
+// workgroups of at least 8 chunks each, so the grid is full whatever the
+// group count (W_o at 64 rows: 56 groups of 128 columns would fill 224
+// workgroups with four equal K slices each); slots = the most workgroups
+// that share one group, the partial-sum slices the reduce reads.
+struct SharedPlan {
+  int wgs, slots;
+};
+static SharedPlan shared_even(int N, int K) {
+  const int G = (N + 127) / 128, C = K / 128;
+  const long long tot = (long long)G * C;
+  long long w = tot / 8;
+  w = w < 256 ? w : 256;
+  if (w <= G) return {0, 1};
+  int smax = 1;
+  for (int grp = 0; grp < G; ++grp) {
+    const int sl = sk_last(grp, C, tot, (int)w) - sk_first(grp, C, tot, (int)w) + 1;
+    smax = sl > smax ? sl : smax;
+  }
+  return {(int)w, smax};
+}
 template <int EPI>
 static hipError_t launch_shared(const GemmArgs& g, hipStream_t st) {
   using C = SharedCfg<2>;
@@ -944,10 +1012,19 @@ static hipError_t launch_shared(const GemmArgs& g, hipStream_t st) {
   }
   const int z = g.ksplit > 1 ? g.ksplit : 1;
   if (z > 1 && !g.part) return hipErrorInvalidValue;
-  hipError_t e = launch(kern, dim3((g.N + 127) / 128, g.batches, z), dim3(256), C::LDS_BYTES, st, g);
+  GemmArgs h = g;
+  h.sk_wgs = 0;
+  dim3 grid((g.N + 127) / 128, g.batches, z);
+  if (g.batches == 1 && z > 1) {
+    const SharedPlan pl = shared_even(g.N, g.K);
+    if (pl.wgs <= 0 || pl.slots != z) return hipErrorInvalidValue;  // not the plan the partial space is sized for
+    h.sk_wgs = pl.wgs;
+    grid = dim3(pl.wgs, 1, 1);
+  }
+  hipError_t e = launch(kern, grid, dim3(256), C::LDS_BYTES, st, h);
   if (e != hipSuccess || z == 1) return e;
   const int64_t n4 = (int64_t)g.batches * g.M * (((g.N + 3) & ~3) / 4);  // output quads, 8 threads each
-  return launch(gemm_splitk_reduce_kernel<EPI>, dim3((unsigned)((8 * n4 + 255) / 256)), dim3(256), 0, st, g);
+  return launch(gemm_splitk_reduce_kernel<EPI>, dim3((unsigned)((8 * n4 + 255) / 256)), dim3(256), 0, st, h);
 }
 
 template <int BN, int BM, int EPI>
@@ -1122,7 +1199,7 @@ static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
 // workgroup (one per wave).
 int gemm_ksplit(int M, int N, int K, int batches, int npad) {
   if (M <= 0 || N <= 0 || K <= 0 || batches <= 0 || !skinny_path(M, N, npad)) return 1;
-  if (shared_path(M, N, K, batches)) return shared_split(N, K, batches);
+  if (shared_path(M, N, K, batches)) return batches == 1 ? shared_even(N, K).slots : shared_split(N, K, batches);
   const long long wgs = (long long)((N + 31) / 32) * batches;
   if (wgs >= 64) return 1;
   const int want = (int)((256 + wgs - 1) / wgs);

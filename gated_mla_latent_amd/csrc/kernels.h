@@ -133,6 +133,8 @@ struct GemmArgs {
   float* part;              // split-K partial sums (gemm_ksplit(...) > 1): gemm_part_bytes(...) bytes
   int ksplit;               // K slices of the skinny kernel (<= 1: none)
   int cw;                   // skinny kernel: output columns per workgroup (set by the launcher)
+  int sk_wgs;               // shared-activation form: workgroups sharing the (column group, K chunk)
+                            // space evenly (0: K slices of equal length per group; set by the launcher)
   // EPI_GATE_VU: O[m, h d_v + j] = sum_c vo[m, h, c] vw[h, j, c] (bf16-rounded),
   // vo [M, H, d_c] with row stride ldvo, vw [H, d_v, d_c]
   const bf16* vo;

@@ -175,19 +175,43 @@ def test_decode_prepare_argument_checks(L):
     assert _prep(L, Wdq=A, d_cq=100) == UNSUPPORTED
 
 
+def _sk_first(grp, chunks, tot, wgs):
+    return -(-((grp * chunks + 1) * wgs) // tot) - 1
+
+
+def _sk_last(grp, chunks, tot, wgs):
+    return -(-((grp + 1) * chunks * wgs) // tot) - 1
+
+
+def _shared_even(N, K):
+    """Even shares of the (128-column group, 128-wide K chunk) space over up
+    to 256 workgroups of at least 8 chunks: (workgroups, slots), slots = the
+    most workgroups whose shares touch one group."""
+    G, C = -(-N // 128), K // 128
+    tot = G * C
+    w = min(tot // 8, 256)
+    if w <= G:
+        return 0, 1
+    return w, max(_sk_last(g, C, tot, w) - _sk_first(g, C, tot, w) + 1 for g in range(G))
+
+
 def _ksplit(M, N, K, batches):
     """The documented split-K rule of the skinny GEMM (M <= 64).
     33..64 rows with K a multiple of 128, K >= 2048, at least 32 workgroups
     of 128 columns and fewer than 256 of 64 columns take the
-    shared-activation form: workgroups of 128 columns, split towards 256
-    workgroups with at least eight 128-wide K chunks per slice. Otherwise:
-    split when the grid has fewer than 64 workgroups of 32 columns, towards
-    256 workgroups, keeping at least four 64-wide K chunks per workgroup.
-    Never an empty slice."""
+    shared-activation form: workgroups of 128 columns; one batch shares the
+    (column group, K chunk) space evenly over up to 256 workgroups (the
+    partial-sum slices are the most workgroups touching one group), several
+    batches split each group towards 256 workgroups with at least eight
+    128-wide K chunks per slice. Otherwise: split when the grid has fewer
+    than 64 workgroups of 32 columns, towards 256 workgroups, keeping at
+    least four 64-wide K chunks per workgroup. Never an empty slice."""
     if M > 64:
         return 1
     groups = -(-N // 128) * batches
     if 32 < M and K % 128 == 0 and K >= 2048 and groups >= 32 and -(-N // 64) * batches < 256:
+        if batches == 1:
+            return _shared_even(N, K)[1]
         z = min(256 // groups, K // 128 // 8)
         if z <= 1:
             return 1
@@ -212,12 +236,49 @@ def test_split_k_rule_examples():
     assert _ksplit(64, 512, 7168, 1) == 16      # narrow: 16 workgroups of 32 columns -> 256
     assert _ksplit(64, 128, 7168, 1) == 28      # 4 workgroups, capped at 4 chunks of 64 each
     assert _ksplit(64, 64, 7168, 1) == 28
-    assert _ksplit(64, 4096, 7168, 1) == 7      # shared form: 32 groups of 128 columns, 8 chunks of 128 each
+    assert _ksplit(64, 4096, 7168, 1) == 7      # shared form: 32 groups x 56 chunks over 224 workgroups of 8
     assert _ksplit(64, 16384, 7168, 1) == 1     # 256 workgroups of 64 columns already
-    assert _ksplit(64, 7168, 16384, 1) == 4     # W_o at 64 rows: 56 groups of 128 columns -> 224
+    assert _shared_even(7168, 16384) == (256, 6)  # W_o at 64 rows: 56 groups x 128 chunks, 28 per workgroup
+    assert _ksplit(64, 7168, 16384, 1) == 6
     assert _ksplit(32, 7168, 16384, 1) == 1     # 32 rows: 224 workgroups of 32 columns, not split
     assert _ksplit(64, 128, 512, 128) == 1      # batched value up-projection: short K, 512 workgroups
     assert _ksplit(65, 512, 7168, 1) == 1       # tile kernel, no split
+
+
+@pytest.mark.parametrize("N,K", [(7168, 16384), (4096, 7168), (4160, 7168), (7168, 8192), (5120, 2048),
+                                 (8064, 4096), (16256, 2048)])
+def test_shared_even_shares_cover_every_chunk_once(N, K):
+    """The even-share plan of the shared-activation GEMM, as the kernel walks
+    it: workgroup w takes items [w T / W, (w + 1) T / W) and writes each
+    piece to slot w - sk_first(group); the reduce reads slots 0 ..
+    sk_last - sk_first of the group. Every (group, chunk) item is covered
+    once, every slot the reduce reads is written exactly once, and no slot
+    reaches past the planned slice count."""
+    G, C = -(-N // 128), K // 128
+    tot = G * C
+    w, slots = _shared_even(N, K)
+    assert w > G and w <= 256 and tot // w >= 8
+    seen = [0] * tot
+    written = {}
+    for wg in range(w):
+        lo, hi = wg * tot // w, (wg + 1) * tot // w
+        assert hi > lo
+        while lo < hi:
+            grp = lo // C
+            end = min(hi, (grp + 1) * C)
+            slot = wg - _sk_first(grp, C, tot, w)
+            assert 0 <= slot < slots
+            assert (grp, slot) not in written
+            written[(grp, slot)] = wg
+            for it in range(lo, end):
+                seen[it] += 1
+            lo = end
+    assert all(c == 1 for c in seen)
+    for grp in range(G):
+        n = _sk_last(grp, C, tot, w) - _sk_first(grp, C, tot, w) + 1
+        assert n <= slots
+        assert all((grp, s) in written for s in range(n))
+        assert not any((grp, s) in written for s in range(n, slots))
 
 
 def test_decode_prepare_workspace_size_formula(L):
