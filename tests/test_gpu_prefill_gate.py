@@ -103,7 +103,11 @@ def test_prefill_fp32_tiny_config():
                                            (64, 7168, 32, 512, 128), (40, 4160, 40, 256, 64),
                                            # ... and batched: the value up-projection over d_c = 2048
                                            # (one 128-column group per head, K split in two)
-                                           (48, 512, 64, 2048, 128)])
+                                           (48, 512, 64, 2048, 128),
+                                           # even shares of W_o's 36 groups x 64 chunks over 256
+                                           # workgroups of 9 chunks: shares that end one group and
+                                           # start the next, up to 8 slots per group
+                                           (64, 4608, 64, 512, 128), (40, 4608, 64, 512, 128)])
 def test_gate_out_with_value_up_projection(T, D, H, d_c, d_v):
     say(f"[gate_out decode-side] T={T} D={D} H={H} d_c={d_c} d_v={d_v}")
     g = torch.Generator().manual_seed(5)
