@@ -17,7 +17,9 @@
 namespace gmla {
 
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args g) {
-  constexpr int T = 64, KT = 16;
+  // 64-wide k-steps: the workload's GEMMs are a few tiles each, so their
+  // time is the chain of load-then-multiply round trips (four per K = 256)
+  constexpr int T = 64, KT = 64;
   __shared__ float As[KT][T + 1];
   __shared__ float Ws[KT][T + 1];
   const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
