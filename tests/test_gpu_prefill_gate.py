@@ -266,3 +266,38 @@ def test_decode_output_side_full_size():
     e = rel_err(y.float(), ry)
     say(f"  rel err y {e:.2e}")
     assert e <= BF16_TOL
+
+
+def _sweep_shapes(n, seed):
+    """Seeded bf16 gate_out shapes over the decode-side paths: the skinny
+    per-wave form (with and without K split), the shared-activation form at
+    33..64 rows (even shares), the value up-projection batched or inside the
+    gate GEMM (d_c = 512), ragged row counts."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        T = int(rng.integers(1, 65))
+        H = int(rng.choice([4, 8, 16, 24, 32, 48, 64]))
+        d_v = int(rng.choice([32, 64, 128]))
+        d_c = int(rng.choice([64, 128, 256, 512, 512]))
+        D = int(rng.choice([256, 512, 1024, 2048, 3072, 4096, 4608]))
+        if (H * d_v) % 64 == 0 and H * d_v * D <= 6 * 2 ** 25:
+            out.append((T, D, H, d_c, d_v))
+    return out
+
+
+@pytest.mark.parametrize("T,D,H,d_c,d_v", _sweep_shapes(24, 7))
+def test_gate_out_shape_sweep(T, D, H, d_c, d_v):
+    say(f"[gate_out sweep] T={T} D={D} H={H} d_c={d_c} d_v={d_v}")
+    g = torch.Generator().manual_seed(T * 7919 + D + H * 31 + d_c + d_v)
+    o_lat = torch.randn(T, H, d_c, generator=g).to(torch.bfloat16)
+    x = torch.randn(T, D, generator=g).to(torch.bfloat16)
+    W_uv = (torch.randn(H, d_v, d_c, generator=g) / d_c ** 0.5).to(torch.bfloat16)
+    W_g = (torch.randn(H * d_v, D, generator=g) / D ** 0.5).to(torch.bfloat16)
+    W_o = (torch.randn(D, H * d_v, generator=g) / (H * d_v) ** 0.5).to(torch.bfloat16)
+    y = ops.gate_out(dev(x), dev(o_lat), dev(W_g), dev(W_o), W_uv=dev(W_uv))
+    torch.cuda.synchronize()
+    ry = O.gate_out_reference(_np(x), O.value_up_projection(_np(o_lat), _np(W_uv)), _np(W_g), _np(W_o))
+    e = rel_err(y.float(), ry)
+    say(f"  rel err y {e:.2e}")
+    assert e <= BF16_TOL
