@@ -165,3 +165,34 @@ def test_decode_full_size_workloads(cfg):
     inp = getattr(W, cfg)(with_output_side=False)
     o, lse = _run(inp)
     _check(inp, o, lse)
+
+
+def _decode_sweep(n, seed):
+    """Seeded decode batches: head counts that are and are not multiples of
+    the 64-head chunks, NoPE and RoPE, lengths from 0 (empty) to a few
+    thousand with ragged mixes, explicit and automatic slice counts."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        B = int(rng.integers(1, 40))
+        H = int(rng.choice([8, 16, 32, 64, 80, 128, 160]))
+        d_r = int(rng.choice([0, 64]))
+        lengths = [int(v) for v in rng.integers(0, 3000, size=B)]
+        if rng.random() < 0.3:
+            lengths[int(rng.integers(0, B))] = 0
+        splits = int(rng.choice([0, 0, 1, 7, 64]))
+        out.append((H, d_r, tuple(lengths), splits))
+    return out
+
+
+@pytest.mark.parametrize("H,d_r,lengths,splits", _decode_sweep(10, 19))
+def test_decode_shape_sweep(H, d_r, lengths, splits):
+    say(f"[decode sweep] B={len(lengths)} H={H} d_r={d_r} splits={splits} total={sum(lengths)}")
+    inp = W.make_decode(len(lengths), H, 512, d_r, 0, lengths=list(lengths), seed=len(lengths) * 31 + H,
+                        name="sweep")
+    o, lse = _run(inp, num_splits=splits)
+    empty = [b for b in range(len(lengths)) if lengths[b] == 0]
+    assert torch.all(o[empty] == 0) and torch.all(torch.isneginf(lse[empty]))
+    nonempty = [b for b in range(len(lengths)) if lengths[b] > 0]
+    if nonempty:
+        _check(inp, o, lse, batches=nonempty)

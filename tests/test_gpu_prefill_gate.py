@@ -301,3 +301,31 @@ def test_gate_out_shape_sweep(T, D, H, d_c, d_v):
     e = rel_err(y.float(), ry)
     say(f"  rel err y {e:.2e}")
     assert e <= BF16_TOL
+
+
+def _prefill_sweep(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        B = int(rng.integers(1, 4))
+        L = int(rng.integers(1, 420))
+        D = 64 * int(rng.integers(2, 17))
+        H = int(rng.integers(1, 9))
+        d_c = 64 * int(rng.integers(1, 9))
+        d = int(rng.choice([64, 128]))
+        out.append((B, L, D, H, d_c, d))
+    return out
+
+
+@pytest.mark.parametrize("B,L,D,H,d_c,d", _prefill_sweep(10, 13))
+def test_prefill_shape_sweep(B, L, D, H, d_c, d):
+    """Seeded prefill shapes: ragged L (query and key tiles cut anywhere,
+    L below one 256-query tile), several batches, both head widths."""
+    say(f"[prefill sweep] B={B} L={L} D={D} H={H} d_c={d_c} d={d}")
+    inp = W.make_prefill(B, L, D, H, d_c, d, d, seed=B * 1009 + L)
+    c, ot, y = _prefill(inp)
+    rc, rot, ry = O.gated_mla_layer(_np(inp.x), _np(inp.W_c), _np(inp.W_q), _np(inp.W_uk), _np(inp.W_uv),
+                                    _np(inp.W_g), _np(inp.W_o), inp.sm_scale)
+    e = (rel_err(c.float(), rc), rel_err(ot.float(), rot), rel_err(y.float(), ry))
+    say(f"  rel err c {e[0]:.2e}  o~ {e[1]:.2e}  y {e[2]:.2e}")
+    assert max(e) <= BF16_TOL

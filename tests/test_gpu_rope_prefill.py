@@ -143,3 +143,16 @@ def test_rope_prefill_full_size_sampled_rows():
     e_o = rel_err(ot[:, rows].float(), rot)
     say(f"  rel err cache rows {max(e_rows):.2e}  o~ {e_o:.2e} (per row {row_err(ot[:, rows].float(), rot):.2e})")
     assert max(e_rows) <= BF16_TOL and e_o <= BF16_TOL
+
+
+def _rope_sweep(n, seed):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, 4)), int(rng.integers(1, 420)), 64 * int(rng.integers(2, 17)),
+             int(rng.integers(1, 9)), 64 * int(rng.integers(1, 9)), int(rng.choice([64, 128]))) for _ in range(n)]
+
+
+@pytest.mark.parametrize("B,L,D,H,d_c,d", _rope_sweep(8, 17))
+def test_rope_prefill_shape_sweep(B, L, D, H, d_c, d):
+    """Seeded decoupled-RoPE prefill shapes (d_r = 64), ragged L."""
+    say(f"[rope prefill sweep] B={B} L={L} D={D} H={H} d_c={d_c} d={d} d_r=64")
+    _check(W.make_prefill(B, L, D, H, d_c, d, d, seed=B * 1013 + L, d_r=64))
