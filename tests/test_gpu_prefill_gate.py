@@ -126,7 +126,10 @@ def test_gate_out_with_value_up_projection(T, D, H, d_c, d_v):
 
 
 @pytest.mark.parametrize("T,H,d_v", [(1, 64, 128), (5, 64, 128), (32, 64, 128), (33, 24, 128), (37, 24, 128),
-                                     (64, 24, 128)])
+                                     (64, 24, 128),
+                                     # 17 heads: a grid that is not a multiple of the 8 XCDs keeps
+                                     # the plain workgroup order
+                                     (40, 17, 128), (64, 17, 128)])
 def test_gate_out_fused_value_up_gated_elementwise(T, H, d_v):
     """d_c = 512 with a wide enough gate GEMM computes o~ inside the gate
     GEMM's workgroups (no separate value up-projection launch). W_o = I
