@@ -9,13 +9,17 @@
 // second equation) when the output strides say so.
 //
 // Design (MI355X):
-//  * One workgroup = (b, h, 256 queries), 8 waves, two per SIMD: wave w owns
-//    32 queries. With O^T (D x 32) and the scores (64 keys x 32) per wave the
-//    registers fit two waves per SIMD, so one wave's softmax arithmetic runs
-//    while the other wave's MFMAs do.
-//  * K and V tiles of 64 keys stream through a 4-stage LDS ring with 1 KiB
-//    direct-to-LDS loads: one barrier per two tiles, after which the next
-//    two tiles are loaded into the stages of the previous two.
+//  * Without RoPE one workgroup = (b, h, 128 queries), 4 waves, one per
+//    SIMD, and two workgroups per compute unit (64 KiB of LDS each): wave w
+//    owns 32 queries. With O^T (D x 32) and the scores (64 keys x 32) per
+//    wave the registers fit two waves per SIMD, so one wave's softmax
+//    arithmetic runs while the other wave's MFMAs do; the two belong to
+//    different workgroups, so a barrier holds only one of them.
+//  * K and V tiles of 64 keys stream through a 2-stage LDS ring with 1 KiB
+//    direct-to-LDS loads: one barrier per tile, after which the next tile
+//    is loaded into the stage of the previous one.
+//  * With RoPE (a larger stage): one workgroup = (b, h, 256 queries), 8
+//    waves, two per SIMD, a 3-stage ring (below).
 //  * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16: each lane owns one query and
 //    16 keys per 32-key block, so the first-tile max needs one exchange with
 //    lane ^ 32. The K rows enter the MFMA in an order (bits 2 and 3 of the
@@ -61,11 +65,14 @@ namespace {
 // the order): one LDS latency then hides behind several MFMAs
 constexpr int kPFS = 4;  // k-steps of K fragments (two each) in flight in S^T
 constexpr int kPFV = 4;  // V^T fragments in flight in P.V
-constexpr int kSync = 2;  // key tiles per barrier; the ring holds 2 kSync tiles
+constexpr int kSync = 1;  // key tiles per barrier (NoPE); the ring holds 2 kSync tiles
 
 template <int D, int DR>
 struct FaCfg {
-  static constexpr int BQ = 256, BK = 64, NW = 8;
+  // NoPE: 128 queries and 4 waves, so that two workgroups share a compute
+  // unit (measured 1951 -> 1912 us against 256 queries, 8 waves and a
+  // 4-stage ring, same bits); RoPE: 256 queries, 8 waves
+  static constexpr int BQ = DR ? 256 : 128, BK = 64, NW = DR ? 8 : 4;
   static constexpr int CH = D / 8;             // 16-byte chunks per row
   static constexpr int ROWB = 2 * D;           // bytes per row
   static constexpr int TILE = BK * ROWB;       // one K tile (64 rows of D), or one V^T tile (D rows of 64)
@@ -99,7 +106,7 @@ __device__ __forceinline__ int swz_vt(int r) { return (r >> 1) & 7; }
 }  // namespace
 
 template <int D, int DR>
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * FaCfg<D, DR>::NW, 64 * FaCfg<D, DR>::NW), amdgpu_waves_per_eu(2, 2)))
 void prefill_attn_kernel(AttnArgs a) {
   using C = FaCfg<D, DR>;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
