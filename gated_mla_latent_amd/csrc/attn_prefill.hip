@@ -9,17 +9,16 @@
 // second equation) when the output strides say so.
 //
 // Design (MI355X):
-//  * Without RoPE one workgroup = (b, h, 128 queries), 4 waves, one per
-//    SIMD, and two workgroups per compute unit (64 KiB of LDS each): wave w
-//    owns 32 queries. With O^T (D x 32) and the scores (64 keys x 32) per
-//    wave the registers fit two waves per SIMD, so one wave's softmax
-//    arithmetic runs while the other wave's MFMAs do; the two belong to
-//    different workgroups, so a barrier holds only one of them.
+//  * One workgroup = (b, h, 128 queries), 4 waves, one per SIMD, and two
+//    workgroups per compute unit (at most 80 KiB of LDS each, no static
+//    LDS): wave w owns 32 queries. With O^T (D x 32) and the scores (64
+//    keys x 32) per wave the registers fit two waves per SIMD, so one
+//    wave's softmax arithmetic runs while the other wave's MFMAs do; the
+//    two belong to different workgroups, so a barrier holds only one of
+//    them.
 //  * K and V tiles of 64 keys stream through a 2-stage LDS ring with 1 KiB
 //    direct-to-LDS loads: one barrier per tile, after which the next tile
 //    is loaded into the stage of the previous one.
-//  * With RoPE (a larger stage): one workgroup = (b, h, 256 queries), 8
-//    waves, two per SIMD, a 3-stage ring (below).
 //  * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16: each lane owns one query and
 //    16 keys per 32-key block, so the first-tile max needs one exchange with
 //    lane ^ 32. The K rows enter the MFMA in an order (bits 2 and 3 of the
@@ -51,9 +50,8 @@
 //    score gains q^R . k^R over DR more features, the rotated RoPE query of
 //    the head and the RoPE key shared by all heads. They are DR / 16 more
 //    k-steps of S^T: the query fragments from their own rows, the key
-//    fragments from a third tile of the stage (64 keys x DR). The larger
-//    stage leaves room for three stages only: one barrier per tile, two
-//    tiles in flight behind the one being read.
+//    fragments from a third tile of the stage (64 keys x DR); two stages
+//    are then 80 KiB.
 #include "common.h"
 #include "kernels.h"
 
@@ -65,31 +63,29 @@ namespace {
 // the order): one LDS latency then hides behind several MFMAs
 constexpr int kPFS = 4;  // k-steps of K fragments (two each) in flight in S^T
 constexpr int kPFV = 4;  // V^T fragments in flight in P.V
-constexpr int kSync = 1;  // key tiles per barrier (NoPE); the ring holds 2 kSync tiles
+constexpr int kSync = 1;  // key tiles per barrier; the ring holds 2 kSync tiles
 
 template <int D, int DR>
 struct FaCfg {
-  // NoPE: 128 queries and 4 waves, so that two workgroups share a compute
-  // unit (measured 1951 -> 1912 us against 256 queries, 8 waves and a
-  // 4-stage ring, same bits); RoPE: 256 queries, 8 waves
-  static constexpr int BQ = DR ? 256 : 128, BK = 64, NW = DR ? 8 : 4;
+  // 128 queries and 4 waves, so that two workgroups share a compute unit
+  // (measured against 256 queries and 8 waves, same bits: NoPE with a
+  // 4-stage ring 1951 -> 1912 us, RoPE with a 3-stage ring 2437 -> 2354 us)
+  static constexpr int BQ = 128, BK = 64, NW = 4;
   static constexpr int CH = D / 8;             // 16-byte chunks per row
   static constexpr int ROWB = 2 * D;           // bytes per row
   static constexpr int TILE = BK * ROWB;       // one K tile (64 rows of D), or one V^T tile (D rows of 64)
   static constexpr int RTILE = BK * DR * 2;    // the RoPE key tile (64 rows of DR)
   static constexpr int STAGE = 2 * TILE + RTILE;
-  static constexpr int SYNC = DR ? 1 : kSync;  // key tiles per barrier
-  static constexpr int NST = DR ? 3 : 2 * kSync;  // ring stages
+  static constexpr int NST = 2 * kSync;  // ring stages
   static constexpr int LDS = NST * STAGE;
   static constexpr int KSC = D / 16;           // k-steps of S^T over the content features
   static constexpr int KS = (D + DR) / 16;     // all k-steps of S^T
   static constexpr int DB = D / 32;            // 32-row blocks of O^T
   static constexpr int RND = BK * CH / (64 * NW);  // 1 KiB loads per wave per K (or V) tile
   static constexpr int RNDR = BK * DR / 8 / (64 * NW);  // ... per RoPE key tile
-  static constexpr int LPT = 2 * RND + RNDR;   // loads per wave per tile
   static_assert(RND >= 1, "at least one load per wave");
-  static_assert(DR == 0 || (DR == 64 && RNDR == 1), "RoPE key tile: one load per wave");
-  static_assert(LDS <= 131072, "LDS budget");
+  static_assert(DR == 0 || (DR == 64 && RNDR >= 1 && RNDR * 64 * NW * 8 == BK * DR), "RoPE key tile: whole loads per wave");
+  static_assert(LDS <= 81920, "LDS budget: two workgroups per compute unit");
 };
 
 // Chunk swizzles (physical chunk = logical chunk ^ f(row)). The K and V^T
@@ -198,10 +194,14 @@ void prefill_attn_kernel(AttnArgs a) {
       // RoPE key rows 8 wave .. 8 wave + 7 (128-byte rows, the V^T swizzle)
       const unsigned rdst = kdst + 2 * C::TILE;
       const unsigned long long rbase = (unsigned long long)(uintptr_t)(krb + (int64_t)t0 * a.skrt);
-      const int row = 8 * wave + (lane >> 3);
-      int rr = t0 + row;
-      rr = (rr < a.L ? rr : a.L - 1) - t0;
-      g2lds16_s(rbase, (unsigned)((rr * a.skrt + ((lane & 7) ^ swz_vt(row)) * 8) * 2), rdst + wave * 1024);
+#pragma unroll
+      for (int r = 0; r < C::RNDR; ++r) {
+        const int blk = r * C::NW + wave;  // 8 rows per 1 KiB load
+        const int row = 8 * blk + (lane >> 3);
+        int rr = t0 + row;
+        rr = (rr < a.L ? rr : a.L - 1) - t0;
+        g2lds16_s(rbase, (unsigned)((rr * a.skrt + ((lane & 7) ^ swz_vt(row)) * 8) * 2), rdst + blk * 1024);
+      }
     }
   };
 
@@ -262,28 +262,19 @@ void prefill_attn_kernel(AttnArgs a) {
     for (int d = 0; d < C::DB; ++d) o[d] = floatx16{};
     lsum = 0.f;
     lds_barrier();
-    constexpr int PRE = DR ? 2 : kSync;  // tiles issued before the loop
+    constexpr int PRE = kSync;  // tiles issued before the loop
 #pragma unroll
     for (int j = 0; j < PRE; ++j)
       if (j < ntiles) load_tile(j, j);
     for (int it = 0; it < ntiles; ++it) {
-      if constexpr (DR == 0) {
-        if (it % kSync == 0) {
-          // tiles it .. it + kSync - 1 have landed; their successors go into
-          // the stages of the previous kSync tiles, which every wave is done with
-          wait_vmcnt<0>();
-          lds_barrier();
-#pragma unroll
-          for (int j = kSync; j < 2 * kSync; ++j)
-            if (it + j < ntiles) load_tile((it + j) % C::NST, it + j);
-        }
-      } else {
-        // tile it has landed (tile it + 1 may still be in flight); tile
-        // it + 2 goes into the stage of tile it - 1, which every wave is done with
-        if (it + 1 < ntiles) wait_vmcnt<C::LPT>();
-        else wait_vmcnt<0>();
+      if (it % kSync == 0) {
+        // tiles it .. it + kSync - 1 have landed; their successors go into
+        // the stages of the previous kSync tiles, which every wave is done with
+        wait_vmcnt<0>();
         lds_barrier();
-        if (it + 2 < ntiles) load_tile((it + 2) % C::NST, it + 2);
+#pragma unroll
+        for (int j = kSync; j < 2 * kSync; ++j)
+          if (it + j < ntiles) load_tile((it + j) % C::NST, it + j);
       }
       if (it >= my_tiles) continue;
       const LDS_AS char* kt_l = smem + (it % C::NST) * C::STAGE;
@@ -390,7 +381,16 @@ void prefill_attn_kernel(AttnArgs a) {
       // every weight is at most the sum: a sum within 2^32 (and not NaN)
       // bounds each weight by 2^32, the bound the pass was made for
       const float l = lsum + xor32(lsum);
-      if (!__syncthreads_or(!(l <= 0x1p32f))) break;
+      // workgroup OR through the idle ring (every tile is consumed and no
+      // load is in flight), which keeps the kernel free of static LDS
+      const bool wover = __builtin_amdgcn_ballot_w64(!(l <= 0x1p32f)) != 0;
+      lds_barrier();
+      if (lane == 0) ((LDS_AS int*)smem)[wave] = wover ? 1 : 0;
+      lds_barrier();
+      int any = 0;
+#pragma unroll
+      for (int w = 0; w < C::NW; ++w) any |= ((const LDS_AS int*)smem)[w];
+      if (!any) break;
       m = 0.f;
       negm = floatx16{};
     } else if (pass == 1) {
