@@ -34,7 +34,11 @@ def _check(inp, o, lse, tol=BF16_TOL, batches=None):
     say(f"  {inp.name or 'decode'} B={inp.B} H={inp.H} d_c={inp.d_c} d_r={inp.d_r}: o rel err {e_o:.2e} "
         f"(per row {e_r:.2e}), lse abs err {e_l:.2e}")
     assert e_o <= tol
-    assert e_l <= 2e-2  # natural-log units; scores are accumulated in fp32 from bf16 operands
+    # lse in absolute natural-log units. Scores are fp32 sums of exact bf16
+    # products; the one rounding the oracle does not share is the RoPE query,
+    # rotated in fp32 and rounded to bf16 before the MFMA (measured at most
+    # 4.8e-3 over these cases, 1e-6 without RoPE)
+    assert e_l <= 1e-2
     return e_o
 
 
