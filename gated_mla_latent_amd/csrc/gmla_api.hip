@@ -182,11 +182,11 @@ gmla_status_t gmla_prefill(const void* x, const void* W_c, const void* W_dq, con
   REQUIRE((long long)B * L * std::max({d_model, H * (d_k + d_r), H * d_v, d_cq}) < (1LL << 40), GMLA_ERR_UNSUPPORTED,
           "problem too large");
   // the token count B*L is a GEMM row count (int), and the bf16 attention
-  // grid holds one workgroup per (b, h, pair of 256-query tiles)
+  // grid holds one workgroup per (b, h, pair of 128-query tiles)
   REQUIRE((long long)B * L <= INT_MAX, GMLA_ERR_UNSUPPORTED, "B * L must not exceed INT_MAX");
   REQUIRE((long long)H * std::max(d_k, d_v) <= INT_MAX && (long long)H * (d_k + d_r) <= INT_MAX, GMLA_ERR_UNSUPPORTED,
           "H * d_k and H * d_v must not exceed INT_MAX");
-  REQUIRE(dtype != GMLA_BF16 || ((long long)L + 511) / 512 * B * H <= INT_MAX, GMLA_ERR_UNSUPPORTED,
+  REQUIRE(dtype != GMLA_BF16 || ((long long)L + 255) / 256 * B * H <= INT_MAX, GMLA_ERR_UNSUPPORTED,
           "prefill attention grid too large");
   REQUIRE(d_r == 0 || dtype == GMLA_BF16, GMLA_ERR_UNSUPPORTED, "decoupled RoPE in prefill is bf16 only");
   if (dtype == GMLA_BF16) {
