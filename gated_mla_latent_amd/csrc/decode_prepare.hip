@@ -21,11 +21,10 @@ namespace gmla {
 
 namespace {
 
-// One workgroup per new row: the latent copied in 16-byte pieces (4-byte ones
-// when d_c + d_r is not a multiple of 8), then the RoPE part rotated pair by
-// pair.
-__global__ __launch_bounds__(256) void decode_append_kernel(PrepareArgs a) {
-  const int b = blockIdx.x;
+// The new row of sequence b: the latent copied in 16-byte pieces (4-byte
+// ones when d_c + d_r is not a multiple of 8), then the RoPE part rotated
+// pair by pair, by the threads of one workgroup.
+__device__ void append_row(const PrepareArgs& a, int b) {
   const int W = a.d_c + a.d_r;
   const int pos = a.seq_len[b];
   const int64_t row = a.seq_start[b] + pos;
@@ -55,7 +54,9 @@ __global__ __launch_bounds__(256) void decode_append_kernel(PrepareArgs a) {
 // (column-major, so that the B operand is one 16-byte read per lane); the
 // queries of head h follow in blocks of 64 rows, zero past B. Wave w computes
 // the 32 x 32 tile (rows 32 (w >> 1), columns 32 (w & 1)) of each block. The
-// workgroup with c0 = 0 also copies the head's RoPE query into q_abs.
+// workgroup with c0 = 0 also copies the head's RoPE query into q_abs and
+// appends the cache rows of sequences h, h + H, h + 2H, ... (the append
+// rides on this launch instead of one of its own: 4 us less per step).
 constexpr int kAbsorbRows = 64;  // batch rows per block
 __device__ __forceinline__ int absorb_ld(int d_k) { return d_k + 8; }  // LDS row length (bf16), 16-byte rows
 __global__ __launch_bounds__(256) void decode_absorb_kernel(PrepareArgs a) {
@@ -100,6 +101,9 @@ __global__ __launch_bounds__(256) void decode_absorb_kernel(PrepareArgs a) {
       }
     }
   }
+  if (blockIdx.y == 0) {
+    for (int b = h; b < a.B; b += a.H) append_row(a, b);
+  }
   if (blockIdx.y == 0 && a.d_r > 0) {
     const int P = a.d_r / 2;
     for (int i = tid; i < a.B * P; i += 256) {
@@ -140,15 +144,10 @@ hipError_t launch_rope_rows(const RopeRowsArgs& a, hipStream_t st) {
   return launch(rope_rows_kernel, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, st, a);
 }
 
-hipError_t launch_decode_append(const PrepareArgs& a, hipStream_t st) {
-  if (a.B <= 0) return hipSuccess;
-  if (a.d_c % 8 != 0 || a.d_r % 2 != 0) return hipErrorInvalidValue;
-  return launch(decode_append_kernel, dim3(a.B), dim3(256), 0, st, a);
-}
-
 hipError_t launch_decode_absorb(const PrepareArgs& a, hipStream_t st) {
   if (a.B <= 0) return hipSuccess;
-  if (a.d_c % 64 != 0 || a.d_k <= 0 || a.d_k > 128 || a.d_k % 16 != 0 || a.d_r % 2 != 0) return hipErrorInvalidValue;
+  if (a.d_c % 64 != 0 || a.d_k <= 0 || a.d_k > 128 || a.d_k % 16 != 0 || a.d_r % 2 != 0 || a.H <= 0)
+    return hipErrorInvalidValue;
   const size_t lds = (size_t)(64 + kAbsorbRows) * (a.d_k + 8) * 2;  // <= 34 KiB
   return launch(decode_absorb_kernel, dim3(a.H, a.d_c / 64), dim3(256), lds, st, a);
 }

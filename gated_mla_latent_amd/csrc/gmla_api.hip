@@ -519,7 +519,6 @@ gmla_status_t gmla_decode_prepare(const void* x, const void* W_c, const void* W_
   a.seq_start = seq_start; a.seq_len = seq_len; a.q_abs = (bf16*)q_abs;
   a.B = B; a.H = H; a.d_c = d_c; a.d_k = d_k; a.d_r = d_r;
   a.rope_base = d_r > 0 ? rope_base : 0.f;
-  if ((s = run("decode_append", st, [&] { return launch_decode_append(a, st); }))) return s;
   if ((s = run("decode_absorb", st, [&] { return launch_decode_absorb(a, st); }))) return s;
   return ok();
 }

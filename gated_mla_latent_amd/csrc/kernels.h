@@ -80,7 +80,6 @@ struct PrepareArgs {
   int B, H, d_c, d_k, d_r;
   float rope_base;          // 0: no rotation
 };
-hipError_t launch_decode_append(const PrepareArgs& a, hipStream_t st);
 // in-place RoPE rotation of row-major rows (prefill): row r holds nvec
 // vectors of d_r elements at p + r ld + v d_r, position r % L; base 0: none
 struct RopeRowsArgs {
@@ -90,6 +89,7 @@ struct RopeRowsArgs {
   float base;
 };
 hipError_t launch_rope_rows(const RopeRowsArgs& a, hipStream_t st);
+// the query absorption, with the cache append of the new rows on the same launch
 hipError_t launch_decode_absorb(const PrepareArgs& a, hipStream_t st);
 
 // per-head scalar gate: gated[t, h d_v + j] = sigmoid(z[t, h] + bias[h]) o[t, h d_v + j]
