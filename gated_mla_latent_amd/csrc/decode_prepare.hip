@@ -54,9 +54,10 @@ __device__ void append_row(const PrepareArgs& a, int b) {
 // (column-major, so that the B operand is one 16-byte read per lane); the
 // queries of head h follow in blocks of 64 rows, zero past B. Wave w computes
 // the 32 x 32 tile (rows 32 (w >> 1), columns 32 (w & 1)) of each block. The
-// workgroup with c0 = 0 also copies the head's RoPE query into q_abs and
-// appends the cache rows of sequences h, h + H, h + 2H, ... (the append
-// rides on this launch instead of one of its own: 4 us less per step).
+// workgroup with c0 = 0 also copies the head's RoPE query into q_abs. The
+// workgroups also append the new cache rows, one sequence each in turn (the
+// append rides on this launch instead of one of its own: 4 us less per
+// step).
 constexpr int kAbsorbRows = 64;  // batch rows per block
 __device__ __forceinline__ int absorb_ld(int d_k) { return d_k + 8; }  // LDS row length (bf16), 16-byte rows
 __global__ __launch_bounds__(256) void decode_absorb_kernel(PrepareArgs a) {
@@ -101,9 +102,8 @@ __global__ __launch_bounds__(256) void decode_absorb_kernel(PrepareArgs a) {
       }
     }
   }
-  if (blockIdx.y == 0) {
-    for (int b = h; b < a.B; b += a.H) append_row(a, b);
-  }
+  // the cache appends, dealt round robin over all H x (d_c / 64) workgroups
+  for (int b = (int)blockIdx.y * a.H + h; b < a.B; b += a.H * (int)gridDim.y) append_row(a, b);
   if (blockIdx.y == 0 && a.d_r > 0) {
     const int P = a.d_r / 2;
     for (int i = tid; i < a.B * P; i += 256) {

@@ -68,6 +68,7 @@ def _check_prepare(dec, st, cache, q_abs):
     (5, 16, 256, 64, 256, 64),
     (1, 8, 128, 4, 192, 32),
     (70, 32, 64, 64, 128, 128),
+    (300, 8, 512, 64, 256, 128),    # B > 64 (tile GEMMs); several cache appends per absorb workgroup
 ])
 def test_prepare_matches_oracle(B, H, d_c, d_r, d_model, d_k):
     say(f"[decode_prepare] B={B} H={H} d_c={d_c} d_r={d_r} d_model={d_model} d_k={d_k}")
